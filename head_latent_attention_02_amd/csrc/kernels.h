@@ -1,0 +1,67 @@
+// Internal launch interface between the C-ABI layer (mla_api.hip) and the
+// kernel translation units.  Each launcher enqueues its kernel(s) on `stream`
+// and returns the launch status; shapes have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+struct ExplicitArgs {
+  int B, Sq, Skv, H, dkv, dn, dr, dv;
+  int64_t q_pos0, kv_pos0;
+  int causal;
+  float scale, rope_base;
+  mla_dtype in_dt, out_dt;
+  int s_vis;      // latent rows visible to at least one query
+  int s_pad;      // s_vis rounded up to the MFMA key tile
+  const void *q_nope, *q_pe, *c_kv, *k_pe, *w;
+  void* out;
+  float* lse;
+};
+
+struct DecodeArgs {
+  int B, H, dkv, dn, dr, dv;
+  int max_len;
+  int64_t cache_stride;
+  int n_splits;
+  float scale, rope_base;
+  mla_dtype in_dt, out_dt;
+  const void *q_nope, *q_pe, *cache, *w;
+  const int32_t* cache_len;
+  void* out;
+  float* lse;
+};
+
+// RoPE cos/sin table: table[p*(dr/2)+m] = (cos, sin)((pos0+p) * base^(-2m/dr)),
+// angles formed in fp64.
+hipError_t launch_rope_table(float2* table, int64_t pos0, int n, int dr, float base,
+                             hipStream_t stream);
+
+// ---- SIMT (fp32 arithmetic) explicit path --------------------------------
+// Workspace: Kn fp32 [B,H,s_vis,dn], V fp32 [B,H,s_vis,dv], krot fp32
+// [B,s_vis,dr], q table [Sq,dr/2], k table [s_vis,dr/2].
+hipError_t launch_simt_explicit(const ExplicitArgs& a, float* kn, float* v, float* krot,
+                                const float2* qtab, const float2* ktab, hipStream_t stream);
+
+// ---- MFMA explicit path ---------------------------------------------------
+// kn fp16 [B,H,s_pad,128], vt fp16 [B,H,128,s_pad], krot fp16 [B,s_pad,64].
+hipError_t launch_mfma_upproj(const ExplicitArgs& a, uint16_t* kn, uint16_t* vt,
+                              hipStream_t stream);
+hipError_t launch_krot_f16(const ExplicitArgs& a, const float2* ktab, uint16_t* krot,
+                           hipStream_t stream);
+hipError_t launch_mfma_attention(const ExplicitArgs& a, const uint16_t* kn, const uint16_t* vt,
+                                 const uint16_t* krot, const float2* qtab, hipStream_t stream);
+
+// ---- decode ---------------------------------------------------------------
+// q~ is fp32 [B,H,dkv+dr] (SIMT) or bf16 (MFMA); lse_part fp32 [B,ns,H];
+// o_part fp32 [B,ns,H,dkv].
+hipError_t launch_simt_absorb(const DecodeArgs& a, float* qt, hipStream_t stream);
+hipError_t launch_simt_splitkv(const DecodeArgs& a, const float* qt, float* lse_part,
+                               float* o_part, hipStream_t stream);
+hipError_t launch_absorb_bf16(const DecodeArgs& a, uint16_t* qt, hipStream_t stream);
+hipError_t launch_mfma_splitkv(const DecodeArgs& a, const uint16_t* qt, float* lse_part,
+                               float* o_part, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs& a, const float* lse_part, const float* o_part,
+                          hipStream_t stream);

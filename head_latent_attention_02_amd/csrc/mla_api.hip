@@ -1,0 +1,314 @@
+// C ABI of libmla: argument validation, workspace carving and the launch
+// sequence of each entry point.  Every check runs on the host before the first
+// launch, so an invalid call enqueues nothing.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kAlign = 256;
+constexpr int kUpTile = 256;        // latent-row tile of the MFMA up-projection
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(mla_dtype d) { return d == MLA_BF16 || d == MLA_FP32; }
+bool valid_algo(mla_algo a) { return a == MLA_ALGO_AUTO || a == MLA_ALGO_SIMT || a == MLA_ALGO_MFMA; }
+
+mla_status hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return MLA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- explicit --
+struct ExplicitPlan {
+  bool mfma = false;
+  int s_vis = 0, s_pad = 0;
+  size_t off_qtab = 0, off_ktab = 0, off_kn = 0, off_v = 0, off_krot = 0, total = 0;
+};
+
+bool explicit_shape_ok(const mla_explicit_desc* d) {
+  if (d == nullptr) return false;
+  if (d->batch < 1 || d->n_heads < 1 || d->s_q < 0 || d->s_kv < 0) return false;
+  if (d->d_kv < 1 || d->d_nope < 1 || d->d_v < 1 || d->d_rope < 2 || (d->d_rope & 1)) return false;
+  if (d->causal != 0 && d->causal != 1) return false;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype) || !valid_algo(d->algo)) return false;
+  if (!std::isfinite(d->softmax_scale) || !std::isfinite(d->rope_base) || !(d->rope_base > 0.f)) return false;
+  // element counts must stay addressable with 64-bit offsets and 32-bit grids
+  const int64_t B = d->batch, H = d->n_heads;
+  if (B * d->s_q * H > (int64_t)1 << 40 || B * d->s_kv > (int64_t)1 << 36) return false;
+  if (H * (int64_t)(d->d_nope + d->d_v) > (int64_t)1 << 24) return false;
+  return true;
+}
+
+bool explicit_mfma_eligible(const mla_explicit_desc* d) {
+  return d->in_dtype == MLA_BF16 && d->d_kv == 512 && d->d_nope == 128 && d->d_rope == 64 &&
+         d->d_v == 128;
+}
+
+bool explicit_simt_supported(const mla_explicit_desc* d) {
+  return d->d_nope + d->d_rope + d->d_v <= 448 && d->d_rope <= 256;
+}
+
+// Returns MLA_OK and fills `plan`, or the status that the call must return.
+mla_status make_explicit_plan(const mla_explicit_desc* d, ExplicitPlan* plan) {
+  if (!explicit_shape_ok(d)) return MLA_ERR_INVALID_ARGUMENT;
+  bool mfma;
+  if (d->algo == MLA_ALGO_MFMA) {
+    if (!explicit_mfma_eligible(d)) return MLA_ERR_UNSUPPORTED;
+    mfma = true;
+  } else if (d->algo == MLA_ALGO_SIMT) {
+    mfma = false;
+  } else {
+    mfma = explicit_mfma_eligible(d);
+  }
+  if (!mfma && !explicit_simt_supported(d)) return MLA_ERR_UNSUPPORTED;
+  ExplicitPlan p;
+  p.mfma = mfma;
+  if (d->s_q == 0) {
+    p.s_vis = 0;
+  } else if (d->causal) {
+    int64_t lim = d->q_pos0 + (int64_t)d->s_q - 1 - d->kv_pos0 + 1;
+    p.s_vis = (int)std::max<int64_t>(0, std::min<int64_t>(lim, d->s_kv));
+  } else {
+    p.s_vis = d->s_kv;
+  }
+  p.s_pad = (p.s_vis + kUpTile - 1) / kUpTile * kUpTile;
+  const size_t B = d->batch, H = d->n_heads, half = d->d_rope / 2;
+  size_t off = 0;
+  p.off_qtab = off; off = align_up(off + sizeof(float2) * (size_t)d->s_q * half);
+  p.off_ktab = off; off = align_up(off + sizeof(float2) * (size_t)p.s_vis * half);
+  if (mfma) {
+    p.off_kn = off;   off = align_up(off + 2 * B * H * (size_t)p.s_pad * 128);
+    p.off_v = off;    off = align_up(off + 2 * B * H * 128 * (size_t)p.s_pad);
+    p.off_krot = off; off = align_up(off + 2 * B * (size_t)p.s_pad * 64);
+  } else {
+    p.off_kn = off;   off = align_up(off + 4 * B * H * (size_t)p.s_vis * d->d_nope);
+    p.off_v = off;    off = align_up(off + 4 * B * H * (size_t)p.s_vis * d->d_v);
+    p.off_krot = off; off = align_up(off + 4 * B * (size_t)p.s_vis * d->d_rope);
+  }
+  p.total = off;
+  *plan = p;
+  return MLA_OK;
+}
+
+// ------------------------------------------------------------------ decode --
+struct DecodePlan {
+  bool mfma = false;
+  size_t off_qt = 0, off_lse = 0, off_opart = 0, qt_elem = 0, total = 0;
+};
+
+bool decode_shape_ok(const mla_decode_desc* d) {
+  if (d == nullptr) return false;
+  if (d->batch < 1 || d->n_heads < 1 || d->max_cache_len < 0 || d->n_splits < 1) return false;
+  if (d->d_kv < 1 || d->d_nope < 1 || d->d_v < 1 || d->d_rope < 2 || (d->d_rope & 1)) return false;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype) || !valid_algo(d->algo)) return false;
+  if (!std::isfinite(d->softmax_scale) || !std::isfinite(d->rope_base) || !(d->rope_base > 0.f)) return false;
+  const int64_t row = (int64_t)d->d_kv + d->d_rope;
+  if (d->cache_batch_stride < (int64_t)d->max_cache_len * row) return false;
+  if ((int64_t)d->batch * d->n_heads > (int64_t)1 << 30) return false;
+  return true;
+}
+
+bool decode_mfma_eligible(const mla_decode_desc* d) {
+  return d->in_dtype == MLA_BF16 && d->d_kv == 512 && d->d_nope == 128 && d->d_rope == 64 &&
+         d->d_v == 128 && d->n_heads % 16 == 0 && d->n_heads <= 128 && d->cache_batch_stride % 8 == 0;
+}
+
+bool decode_simt_supported(const mla_decode_desc* d) { return d->d_kv <= 1024 && d->d_rope <= 256; }
+
+mla_status make_decode_plan(const mla_decode_desc* d, DecodePlan* plan) {
+  if (!decode_shape_ok(d)) return MLA_ERR_INVALID_ARGUMENT;
+  if (d->n_splits > 64) return MLA_ERR_UNSUPPORTED;
+  if (d->d_kv > 1024) return MLA_ERR_UNSUPPORTED;   // combine keeps 8 merged rows in LDS
+  bool mfma;
+  if (d->algo == MLA_ALGO_MFMA) {
+    if (!decode_mfma_eligible(d)) return MLA_ERR_UNSUPPORTED;
+    mfma = true;
+  } else if (d->algo == MLA_ALGO_SIMT) {
+    mfma = false;
+  } else {
+    mfma = decode_mfma_eligible(d);
+  }
+  if (!mfma && !decode_simt_supported(d)) return MLA_ERR_UNSUPPORTED;
+  DecodePlan p;
+  p.mfma = mfma;
+  const size_t B = d->batch, H = d->n_heads, ns = d->n_splits, dlat = d->d_kv + d->d_rope;
+  p.qt_elem = mfma ? 2 : 4;
+  size_t off = 0;
+  p.off_qt = off;    off = align_up(off + p.qt_elem * B * H * dlat);
+  p.off_lse = off;   off = align_up(off + 4 * B * ns * H);
+  p.off_opart = off; off = align_up(off + 4 * B * ns * H * (size_t)d->d_kv);
+  p.total = off;
+  *plan = p;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_fwd_explicit_workspace_size(const mla_explicit_desc* desc) {
+  ExplicitPlan p;
+  if (make_explicit_plan(desc, &p) != MLA_OK) return 0;
+  return p.total;
+}
+
+mla_status mla_fwd_explicit_workspace_layout(const mla_explicit_desc* desc, size_t offsets[4]) {
+  if (offsets == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  ExplicitPlan p;
+  mla_status st = make_explicit_plan(desc, &p);
+  if (st != MLA_OK) return st;
+  if (!p.mfma) return MLA_ERR_UNSUPPORTED;
+  offsets[0] = p.off_kn;
+  offsets[1] = p.off_v;
+  offsets[2] = p.off_krot;
+  offsets[3] = (size_t)p.s_pad;
+  return MLA_OK;
+}
+
+mla_status mla_fwd_explicit(const mla_explicit_desc* desc, const void* q_nope, const void* q_pe,
+                            const void* c_kv, const void* k_pe, const void* w_kv_b, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  ExplicitPlan p;
+  mla_status st = make_explicit_plan(desc, &p);
+  if (st != MLA_OK) return st;
+  const bool has_q = desc->s_q > 0, has_kv = desc->s_kv > 0;
+  if (w_kv_b == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (has_q && (q_nope == nullptr || q_pe == nullptr || out == nullptr)) return MLA_ERR_INVALID_ARGUMENT;
+  if (has_kv && (c_kv == nullptr || k_pe == nullptr)) return MLA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (p.total > 0 && workspace == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (p.mfma) {
+    const void* ptrs[] = {q_nope, q_pe, c_kv, k_pe, w_kv_b, out, workspace};
+    for (const void* q : ptrs)
+      if (q != nullptr && !aligned16(q)) return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!has_q) return MLA_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  ExplicitArgs a;
+  a.B = desc->batch; a.Sq = desc->s_q; a.Skv = desc->s_kv; a.H = desc->n_heads;
+  a.dkv = desc->d_kv; a.dn = desc->d_nope; a.dr = desc->d_rope; a.dv = desc->d_v;
+  a.q_pos0 = desc->q_pos0; a.kv_pos0 = desc->kv_pos0; a.causal = desc->causal;
+  a.scale = desc->softmax_scale; a.rope_base = desc->rope_base;
+  a.in_dt = desc->in_dtype; a.out_dt = desc->out_dtype;
+  a.s_vis = p.s_vis; a.s_pad = p.s_pad;
+  a.q_nope = q_nope; a.q_pe = q_pe; a.c_kv = c_kv; a.k_pe = k_pe; a.w = w_kv_b;
+  a.out = out; a.lse = lse;
+
+  float2* qtab = reinterpret_cast<float2*>(ws + p.off_qtab);
+  float2* ktab = reinterpret_cast<float2*>(ws + p.off_ktab);
+  hipError_t e = launch_rope_table(qtab, a.q_pos0, a.Sq, a.dr, a.rope_base, s);
+  if (e != hipSuccess) return hip_fail(e, "rope table (queries)");
+  e = launch_rope_table(ktab, a.kv_pos0, a.s_vis, a.dr, a.rope_base, s);
+  if (e != hipSuccess) return hip_fail(e, "rope table (keys)");
+  if (p.mfma) {
+    uint16_t* kn = reinterpret_cast<uint16_t*>(ws + p.off_kn);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(ws + p.off_v);
+    uint16_t* kr = reinterpret_cast<uint16_t*>(ws + p.off_krot);
+    e = launch_mfma_upproj(a, kn, vt, s);
+    if (e != hipSuccess) return hip_fail(e, "mfma up-projection");
+    e = launch_krot_f16(a, ktab, kr, s);
+    if (e != hipSuccess) return hip_fail(e, "key rope band");
+    e = launch_mfma_attention(a, kn, vt, kr, qtab, s);
+    if (e != hipSuccess) return hip_fail(e, "mfma attention");
+  } else {
+    e = launch_simt_explicit(a, reinterpret_cast<float*>(ws + p.off_kn), reinterpret_cast<float*>(ws + p.off_v),
+                             reinterpret_cast<float*>(ws + p.off_krot), qtab, ktab, s);
+    if (e != hipSuccess) return hip_fail(e, "simt explicit forward");
+  }
+  return MLA_OK;
+}
+
+size_t mla_decode_absorbed_workspace_size(const mla_decode_desc* desc) {
+  DecodePlan p;
+  if (make_decode_plan(desc, &p) != MLA_OK) return 0;
+  return p.total;
+}
+
+mla_status mla_decode_absorbed_workspace_layout(const mla_decode_desc* desc, size_t offsets[4]) {
+  if (offsets == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  DecodePlan p;
+  mla_status st = make_decode_plan(desc, &p);
+  if (st != MLA_OK) return st;
+  offsets[0] = p.off_qt;
+  offsets[1] = p.off_lse;
+  offsets[2] = p.off_opart;
+  offsets[3] = p.qt_elem;
+  return MLA_OK;
+}
+
+mla_status mla_decode_absorbed(const mla_decode_desc* desc, const void* q_nope, const void* q_pe,
+                               const void* kv_cache, const int32_t* cache_len, const void* w_kv_b, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan p;
+  mla_status st = make_decode_plan(desc, &p);
+  if (st != MLA_OK) return st;
+  if (q_nope == nullptr || q_pe == nullptr || cache_len == nullptr || w_kv_b == nullptr || out == nullptr)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (desc->max_cache_len > 0 && kv_cache == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (p.mfma) {
+    const void* ptrs[] = {q_nope, q_pe, kv_cache, w_kv_b, out, workspace};
+    for (const void* q : ptrs)
+      if (q != nullptr && !aligned16(q)) return MLA_ERR_INVALID_ARGUMENT;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  DecodeArgs a;
+  a.B = desc->batch; a.H = desc->n_heads; a.dkv = desc->d_kv; a.dn = desc->d_nope;
+  a.dr = desc->d_rope; a.dv = desc->d_v; a.max_len = desc->max_cache_len;
+  a.cache_stride = desc->cache_batch_stride; a.n_splits = desc->n_splits;
+  a.scale = desc->softmax_scale; a.rope_base = desc->rope_base;
+  a.in_dt = desc->in_dtype; a.out_dt = desc->out_dtype;
+  a.q_nope = q_nope; a.q_pe = q_pe; a.cache = kv_cache; a.w = w_kv_b; a.cache_len = cache_len;
+  a.out = out; a.lse = lse;
+  float* lse_part = reinterpret_cast<float*>(ws + p.off_lse);
+  float* o_part = reinterpret_cast<float*>(ws + p.off_opart);
+  hipError_t e;
+  if (p.mfma) {
+    uint16_t* qt = reinterpret_cast<uint16_t*>(ws + p.off_qt);
+    e = launch_absorb_bf16(a, qt, s);
+    if (e != hipSuccess) return hip_fail(e, "query absorption");
+    e = launch_mfma_splitkv(a, qt, lse_part, o_part, s);
+    if (e != hipSuccess) return hip_fail(e, "mfma split-KV attention");
+  } else {
+    float* qt = reinterpret_cast<float*>(ws + p.off_qt);
+    e = launch_simt_absorb(a, qt, s);
+    if (e != hipSuccess) return hip_fail(e, "query absorption");
+    e = launch_simt_splitkv(a, qt, lse_part, o_part, s);
+    if (e != hipSuccess) return hip_fail(e, "simt split-KV attention");
+  }
+  e = launch_combine(a, lse_part, o_part, s);
+  if (e != hipSuccess) return hip_fail(e, "LSE combine");
+  return MLA_OK;
+}
+
+const char* mla_status_string(mla_status status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARGUMENT: return "MLA_ERR_INVALID_ARGUMENT";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+const char* mla_build_info(void) {
+  return "libmla: target gfx950; kernels: rope_table, simt (explicit, decode), mfma (up-projection, "
+         "attention, absorb, split-KV), lse combine";
+}
+
+}  // extern "C"

@@ -1,0 +1,263 @@
+"""Thin ctypes binding of libmla (include/mla.h).
+
+Argument marshalling only: every step of the MLA forward runs in the HIP
+kernels of libmla.so.  PyTorch supplies device memory and the current stream.
+If the library is missing the first call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE_TOO_SMALL = 3
+MLA_ERR_HIP = 4
+
+MLA_BF16 = 0
+MLA_FP32 = 1
+
+MLA_ALGO_AUTO = 0
+MLA_ALGO_SIMT = 1
+MLA_ALGO_MFMA = 2
+
+EXPORTED_SYMBOLS = (
+    "mla_fwd_explicit_workspace_size", "mla_fwd_explicit", "mla_fwd_explicit_workspace_layout",
+    "mla_decode_absorbed_workspace_size", "mla_decode_absorbed", "mla_decode_absorbed_workspace_layout",
+    "mla_status_string", "mla_last_error", "mla_build_info",
+)
+
+
+class MlaExplicitDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("s_q", ctypes.c_int32), ("s_kv", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32), ("d_kv", ctypes.c_int32), ("d_nope", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32), ("q_pos0", ctypes.c_int64),
+        ("kv_pos0", ctypes.c_int64), ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("rope_base", ctypes.c_float), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("algo", ctypes.c_int),
+    ]
+
+
+class MlaDecodeDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("d_kv", ctypes.c_int32),
+        ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("max_cache_len", ctypes.c_int32), ("cache_batch_stride", ctypes.c_int64),
+        ("n_splits", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float),
+        ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("algo", ctypes.c_int),
+    ]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _lib()
+        msg = lib.mla_status_string(status).decode()
+        detail = lib.mla_last_error().decode()
+        super().__init__(f"{where}: {msg}" + (f" ({detail})" if detail else ""))
+        self.status = status
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmla.so not built at {LIB_PATH}; run `python -m head_latent_attention_02_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.mla_fwd_explicit_workspace_size.argtypes = [ctypes.POINTER(MlaExplicitDesc)]
+        lib.mla_fwd_explicit_workspace_size.restype = sz
+        lib.mla_fwd_explicit.argtypes = [ctypes.POINTER(MlaExplicitDesc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.mla_fwd_explicit.restype = ctypes.c_int
+        lib.mla_fwd_explicit_workspace_layout.argtypes = [ctypes.POINTER(MlaExplicitDesc), ctypes.POINTER(sz)]
+        lib.mla_fwd_explicit_workspace_layout.restype = ctypes.c_int
+        lib.mla_decode_absorbed_workspace_size.argtypes = [ctypes.POINTER(MlaDecodeDesc)]
+        lib.mla_decode_absorbed_workspace_size.restype = sz
+        lib.mla_decode_absorbed.argtypes = [ctypes.POINTER(MlaDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.mla_decode_absorbed.restype = ctypes.c_int
+        lib.mla_decode_absorbed_workspace_layout.argtypes = [ctypes.POINTER(MlaDecodeDesc), ctypes.POINTER(sz)]
+        lib.mla_decode_absorbed_workspace_layout.restype = ctypes.c_int
+        lib.mla_status_string.argtypes = [ctypes.c_int]
+        lib.mla_status_string.restype = ctypes.c_char_p
+        lib.mla_last_error.argtypes = []
+        lib.mla_last_error.restype = ctypes.c_char_p
+        lib.mla_build_info.argtypes = []
+        lib.mla_build_info.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libmla handle (loads it on first use)."""
+    return _lib()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MLA_BF16
+    if t == torch.float32:
+        return MLA_FP32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == MLA_BF16 else torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != MLA_OK:
+        raise MlaError(status, where)
+
+
+# ----------------------------------------------------------------- explicit --
+def explicit_desc(*, batch, s_q, s_kv, n_heads, d_kv, d_nope, d_rope, d_v, q_pos0=0, kv_pos0=0,
+                  causal=True, softmax_scale=None, rope_base=10000.0, in_dtype=MLA_BF16,
+                  out_dtype=MLA_FP32, algo=MLA_ALGO_AUTO) -> MlaExplicitDesc:
+    if softmax_scale is None:
+        softmax_scale = (d_nope + d_rope) ** -0.5
+    return MlaExplicitDesc(batch, s_q, s_kv, n_heads, d_kv, d_nope, d_rope, d_v, q_pos0, kv_pos0,
+                           int(causal), softmax_scale, rope_base, in_dtype, out_dtype, algo)
+
+
+def mla_fwd_explicit_workspace_size(desc: MlaExplicitDesc) -> int:
+    return int(_lib().mla_fwd_explicit_workspace_size(ctypes.byref(desc)))
+
+
+def mla_fwd_explicit_workspace_layout(desc: MlaExplicitDesc) -> tuple:
+    off = (ctypes.c_size_t * 4)()
+    _check(_lib().mla_fwd_explicit_workspace_layout(ctypes.byref(desc), off), "mla_fwd_explicit_workspace_layout")
+    return tuple(int(x) for x in off)
+
+
+def mla_fwd_explicit(q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
+                     w_kv_b: torch.Tensor, *, q_pos0: int = 0, kv_pos0: int = 0, causal: bool = True,
+                     softmax_scale: Optional[float] = None, rope_base: float = 10000.0,
+                     out_dtype: torch.dtype = torch.float32, algo: int = MLA_ALGO_AUTO,
+                     return_lse: bool = True, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Explicit-form MLA forward; see mla_fwd_explicit in include/mla.h.
+
+    Shapes: q_nope [B,S_q,H,d_nope], q_pe [B,S_q,H,d_rope], c_kv [B,S_kv,d_kv],
+    k_pe [B,S_kv,d_rope], w_kv_b [H*(d_nope+d_v), d_kv].  Returns (out, lse,
+    workspace); lse is None when return_lse is False.
+    """
+    B, S_q, H, d_nope = q_nope.shape
+    S_kv, d_kv = c_kv.shape[1], c_kv.shape[2]
+    d_rope = q_pe.shape[-1]
+    d_v = w_kv_b.shape[0] // H - d_nope
+    dt = _dtype_code(q_nope.dtype)
+    for t in (q_pe, c_kv, k_pe, w_kv_b):
+        if t.dtype != q_nope.dtype or not t.is_contiguous() or t.device != q_nope.device:
+            raise ValueError("all inputs must share dtype and device and be contiguous")
+    if not q_nope.is_contiguous():
+        raise ValueError("q_nope must be contiguous")
+    desc = explicit_desc(batch=B, s_q=S_q, s_kv=S_kv, n_heads=H, d_kv=d_kv, d_nope=d_nope, d_rope=d_rope,
+                         d_v=d_v, q_pos0=q_pos0, kv_pos0=kv_pos0, causal=causal, softmax_scale=softmax_scale,
+                         rope_base=rope_base, in_dtype=dt, out_dtype=_dtype_code(out_dtype), algo=algo)
+    dev = q_nope.device
+    ws_bytes = mla_fwd_explicit_workspace_size(desc)
+    if ws_bytes == 0 and S_q > 0:
+        _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,
+               "mla_fwd_explicit_workspace_size")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((B, S_q, H, d_v), dtype=out_dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, S_q), dtype=torch.float32, device=dev)
+    st = _lib().mla_fwd_explicit(ctypes.byref(desc), _ptr(q_nope), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe),
+                                 _ptr(w_kv_b), _ptr(out), _ptr(lse) if return_lse else None,
+                                 workspace.data_ptr(), workspace.numel(), _stream(dev))
+    _check(st, "mla_fwd_explicit")
+    return out, (lse if return_lse else None), workspace
+
+
+# ------------------------------------------------------------------- decode --
+def decode_desc(*, batch, n_heads, d_kv, d_nope, d_rope, d_v, max_cache_len, cache_batch_stride=None,
+                n_splits=16, softmax_scale=None, rope_base=10000.0, in_dtype=MLA_BF16, out_dtype=MLA_FP32,
+                algo=MLA_ALGO_AUTO) -> MlaDecodeDesc:
+    if softmax_scale is None:
+        softmax_scale = (d_nope + d_rope) ** -0.5
+    if cache_batch_stride is None:
+        cache_batch_stride = max_cache_len * (d_kv + d_rope)
+    return MlaDecodeDesc(batch, n_heads, d_kv, d_nope, d_rope, d_v, max_cache_len, cache_batch_stride,
+                         n_splits, softmax_scale, rope_base, in_dtype, out_dtype, algo)
+
+
+def mla_decode_absorbed_workspace_size(desc: MlaDecodeDesc) -> int:
+    return int(_lib().mla_decode_absorbed_workspace_size(ctypes.byref(desc)))
+
+
+def mla_decode_absorbed_workspace_layout(desc: MlaDecodeDesc) -> tuple:
+    off = (ctypes.c_size_t * 4)()
+    _check(_lib().mla_decode_absorbed_workspace_layout(ctypes.byref(desc), off),
+           "mla_decode_absorbed_workspace_layout")
+    return tuple(int(x) for x in off)
+
+
+def mla_decode_absorbed(q_nope: torch.Tensor, q_pe: torch.Tensor, kv_cache: torch.Tensor,
+                        cache_len: torch.Tensor, w_kv_b: torch.Tensor, *, n_splits: int = 16,
+                        d_kv: Optional[int] = None, softmax_scale: Optional[float] = None,
+                        rope_base: float = 10000.0, out_dtype: torch.dtype = torch.float32,
+                        algo: int = MLA_ALGO_AUTO, return_lse: bool = True,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None):
+    """Absorbed split-KV decode step; see mla_decode_absorbed in include/mla.h.
+
+    q_nope [B,H,d_nope], q_pe [B,H,d_rope], kv_cache [B,L_max,d_kv+d_rope] (its
+    sequence stride may exceed L_max rows; rows must be contiguous),
+    cache_len [B] int32 on the device, w_kv_b [H*(d_nope+d_v), d_kv].
+    """
+    B, H, d_nope = q_nope.shape
+    d_rope = q_pe.shape[-1]
+    row = kv_cache.shape[-1]
+    if d_kv is None:
+        d_kv = row - d_rope
+    d_v = w_kv_b.shape[0] // H - d_nope
+    if kv_cache.stride(-1) != 1 or kv_cache.stride(-2) != row:
+        raise ValueError("kv_cache rows must be contiguous")
+    if cache_len.dtype != torch.int32:
+        raise ValueError("cache_len must be int32")
+    dt = _dtype_code(q_nope.dtype)
+    desc = decode_desc(batch=B, n_heads=H, d_kv=d_kv, d_nope=d_nope, d_rope=d_rope, d_v=d_v,
+                       max_cache_len=kv_cache.shape[1], cache_batch_stride=kv_cache.stride(0),
+                       n_splits=n_splits, softmax_scale=softmax_scale, rope_base=rope_base, in_dtype=dt,
+                       out_dtype=_dtype_code(out_dtype), algo=algo)
+    dev = q_nope.device
+    ws_bytes = mla_decode_absorbed_workspace_size(desc)
+    if ws_bytes == 0:
+        _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,
+               "mla_decode_absorbed_workspace_size")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=out_dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = _lib().mla_decode_absorbed(ctypes.byref(desc), _ptr(q_nope), _ptr(q_pe), _ptr(kv_cache),
+                                    _ptr(cache_len), _ptr(w_kv_b), _ptr(out), _ptr(lse) if return_lse else None,
+                                    workspace.data_ptr(), workspace.numel(), _stream(dev))
+    _check(st, "mla_decode_absorbed")
+    return out, (lse if return_lse else None), workspace
+
+
+def build_info() -> str:
+    return _lib().mla_build_info().decode()

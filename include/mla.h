@@ -1,0 +1,209 @@
+/*
+ * mla.h -- C ABI of libmla: the Multi-head Latent Attention (MLA) forward hot
+ * path on AMD MI355X (gfx950).
+ *
+ * Pages this interface follows (Pith review pages):
+ *   [LAGA]  "A Training-Memory Regression in MLA Sequence Parallelism: Why
+ *            Megatron-Core Forbids Absorption, and LAGA -- a
+ *            Communication-Efficient Fix"
+ *   [TPLA]  "TPLA: Tensor Parallel Latent Attention for Efficient
+ *            Disaggregated Prefill and Decode Inference"
+ *   [Helix] "Helix Parallelism: Rethinking Sharding Strategies for
+ *            Interactive Multi-Million-Token LLM Decoding"
+ *
+ * Two operations:
+ *   mla_fwd_explicit     the explicit (training / LAGA per-rank) form: the
+ *                        latent c_KV is up-projected through W_kv_b into
+ *                        per-head K_nope and V, the decoupled RoPE band is
+ *                        rotated, and causal softmax attention runs in head
+ *                        dimension ([LAGA] "What carries the argument" and the
+ *                        Fig. 2 caption, flows "Explicit (B1)" and "LAGA").
+ *   mla_decode_absorbed  the absorbed decode form: each query is absorbed into
+ *                        latent space, attends to the 576-wide latent cache
+ *                        rows directly, the KV sequence is split in chunks
+ *                        whose partial outputs are merged by log-sum-exp
+ *                        rescaling, and the merged latent output is
+ *                        up-projected to d_v ([LAGA] "What carries the
+ *                        argument" and Fig. 2 "Absorbed (B2)"; [TPLA] "If this
+ *                        is right" for the 576-wide cache row; [Helix] "What
+ *                        carries the argument" for the LSE merge).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers unless a comment says otherwise.
+ *     Tensors are dense row-major with the shapes given below, 16-byte
+ *     aligned.  The caller owns and allocates every buffer, including the
+ *     workspace; the library never allocates, frees or synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously; the call returns once the kernels are enqueued.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     validation failure the call returns a non-zero status and launches
+ *     nothing.  A failed kernel launch returns MLA_ERR_HIP.  No C++ exception
+ *     crosses this interface.
+ *   - Weight layout (reading of the pages, which give only the 512 x (128*256)
+ *     map): W_kv_b is the linear map from d_kv to H*(d_nope+d_v) stored one
+ *     row per output feature, i.e. [H*(d_nope+d_v), d_kv].  Rows
+ *     h*(d_nope+d_v) .. h*(d_nope+d_v)+d_nope-1 are head h's key part W_UK[h],
+ *     the next d_v rows its value part W_UV[h].
+ *   - RoPE: rotate-half pairs (m, m + d_rope/2), theta_m = base^(-2m/d_rope),
+ *     angle = absolute position * theta_m, angles formed in fp64.
+ *   - LSE outputs are natural logs of the sum of exp of the scaled logits;
+ *     a query that sees no key gets O = 0 and LSE = -inf.
+ *   - Calls are reentrant: the library keeps no state between calls.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad enum   */
+  MLA_ERR_UNSUPPORTED = 2,        /* valid request this build does not implement */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MLA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed  */
+} mla_status;
+
+typedef enum { MLA_BF16 = 0, MLA_FP32 = 1 } mla_dtype;
+
+typedef enum {
+  MLA_ALGO_AUTO = 0,     /* MFMA kernels when the shape allows, else SIMT      */
+  MLA_ALGO_SIMT = 1,     /* fp32 SIMT kernels, any supported shape or dtype     */
+  MLA_ALGO_MFMA = 2      /* MFMA kernels; MLA_ERR_UNSUPPORTED if not eligible   */
+} mla_algo;
+
+/* ------------------------------------------------------------------------ */
+/* Explicit form                                                             */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t batch;        /* B >= 1                                              */
+  int32_t s_q;          /* query rows per sequence, >= 0                       */
+  int32_t s_kv;         /* latent rows per sequence, >= 0                      */
+  int32_t n_heads;      /* H >= 1                                              */
+  int32_t d_kv;         /* latent width (512 at DeepSeek-V2/V3 dims)           */
+  int32_t d_nope;       /* per-head non-rotary q/k width (128)                 */
+  int32_t d_rope;       /* decoupled RoPE band width, even (64)                */
+  int32_t d_v;          /* per-head value width (128)                          */
+  int64_t q_pos0;       /* absolute position of query row 0                    */
+  int64_t kv_pos0;      /* absolute position of latent row 0                   */
+  int32_t causal;       /* 1: key j visible to query i iff kv_pos0+j <= q_pos0+i */
+  float softmax_scale;  /* multiplies the whole logit; usually 1/sqrt(d_nope+d_rope) */
+  float rope_base;      /* RoPE base, > 1 (10000)                              */
+  mla_dtype in_dtype;   /* dtype of q_nope, q_pe, c_kv, k_pe, w_kv_b            */
+  mla_dtype out_dtype;  /* dtype of out (lse is always fp32)                   */
+  mla_algo algo;        /* kernel family                                       */
+} mla_explicit_desc;
+
+/* Bytes of device workspace mla_fwd_explicit needs for `desc`; 0 if the
+ * descriptor is invalid or unsupported. */
+size_t mla_fwd_explicit_workspace_size(const mla_explicit_desc* desc);
+
+/* Explicit-form forward ([LAGA] "What carries the argument", Fig. 2 B1/LAGA):
+ *   K_nope[j,h] = W_UK[h] c_kv[j],  V[j,h] = W_UV[h] c_kv[j]
+ *   logit[h,i,j] = softmax_scale * ( q_nope[i,h].K_nope[j,h]
+ *                   + R(q_pe[i,h], q_pos0+i) . R(k_pe[j], kv_pos0+j) )
+ *   out[i,h] = sum_j softmax_j(logit)[h,i,j] V[j,h] over visible keys.
+ * k_pe is one band per latent row, shared by all heads.
+ *
+ *   q_nope [B, s_q, H, d_nope]     q_pe [B, s_q, H, d_rope]  (un-rotated)
+ *   c_kv   [B, s_kv, d_kv]         k_pe [B, s_kv, d_rope]    (un-rotated)
+ *   w_kv_b [H*(d_nope+d_v), d_kv]
+ *   out    [B, s_q, H, d_v]        (out_dtype)
+ *   lse    [B, H, s_q] fp32, or NULL when not wanted
+ *   workspace: device buffer of at least mla_fwd_explicit_workspace_size()
+ *   bytes; its contents on entry are ignored and on exit are unspecified
+ *   (see mla_fwd_explicit_workspace_layout for the MFMA path's intermediates).
+ * Latent rows no query can see (causal) are neither up-projected nor read. */
+mla_status mla_fwd_explicit(const mla_explicit_desc* desc,
+                            const void* q_nope, const void* q_pe,
+                            const void* c_kv, const void* k_pe,
+                            const void* w_kv_b,
+                            void* out, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Where the MFMA path leaves its intermediates inside the workspace, for
+ * testing the up-projection on its own.  Writes byte offsets (host memory,
+ * offsets[4]):
+ *   [0] K_nope  fp16 [B, H, s_kv_pad, d_nope]
+ *   [1] V^T     fp16 [B, H, d_v, s_kv_pad]   (key index fastest)
+ *   [2] R(k_pe) fp16 [B, s_kv_pad, d_rope]
+ *   [3] s_kv_pad (an element count, not an offset)
+ * Only rows below the last visible key are written.  Returns
+ * MLA_ERR_UNSUPPORTED when `desc` would not take the MFMA path. */
+mla_status mla_fwd_explicit_workspace_layout(const mla_explicit_desc* desc,
+                                             size_t offsets[4]);
+
+/* ------------------------------------------------------------------------ */
+/* Absorbed split-KV decode                                                  */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t batch;             /* B >= 1                                         */
+  int32_t n_heads;           /* H >= 1                                         */
+  int32_t d_kv, d_nope, d_rope, d_v;
+  int32_t max_cache_len;     /* host-side upper bound of cache_len[b] (grid sizing) */
+  int64_t cache_batch_stride;/* elements between sequences in kv_cache,
+                                >= max_cache_len * (d_kv + d_rope)             */
+  int32_t n_splits;          /* chunks per sequence, >= 1                       */
+  float softmax_scale;
+  float rope_base;
+  mla_dtype in_dtype;        /* dtype of q_nope, q_pe, kv_cache, w_kv_b         */
+  mla_dtype out_dtype;
+  mla_algo algo;
+} mla_decode_desc;
+
+size_t mla_decode_absorbed_workspace_size(const mla_decode_desc* desc);
+
+/* One decode step in absorbed form ([LAGA] Fig. 2 B2; [Helix] "What carries
+ * the argument"):
+ *   p = cache_len[b] - 1 (the new token's position; its row is in the cache)
+ *   q~[b,h] = [ W_UK[h]^T q_nope[b,h] ; R(q_pe[b,h], p) ]      (d_kv+d_rope)
+ *   logit_t = softmax_scale * q~[b,h] . kv_cache[b,t]        for t < cache_len[b]
+ *   chunk size c = ceil(cache_len[b] / n_splits), chunk k = [k c, min(L,(k+1)c));
+ *   per chunk a partial latent output normalised within the chunk plus its
+ *   LSE; the partials are merged by LSE rescaling into o_lat[b,h] (d_kv);
+ *   out[b,h] = W_UV[h] o_lat[b,h].
+ *
+ *   q_nope   [B, H, d_nope]             q_pe [B, H, d_rope] (un-rotated)
+ *   kv_cache [B, *, d_kv + d_rope] with row stride d_kv+d_rope and sequence
+ *            stride cache_batch_stride; each row is the latent c_kv then the
+ *            already-rotated k_pe band
+ *   cache_len [B] int32, device: rows attended per sequence, 0..max_cache_len
+ *   w_kv_b   [H*(d_nope+d_v), d_kv]
+ *   out      [B, H, d_v] (out_dtype)    lse [B, H] fp32 or NULL
+ * cache_len values outside [0, max_cache_len] are clamped to that range on
+ * the device.  A sequence with cache_len 0 gets out = 0 and lse = -inf. */
+mla_status mla_decode_absorbed(const mla_decode_desc* desc,
+                               const void* q_nope, const void* q_pe,
+                               const void* kv_cache, const int32_t* cache_len,
+                               const void* w_kv_b,
+                               void* out, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Offsets of the decode intermediates inside the workspace (host memory,
+ * offsets[4]):
+ *   [0] q~        [B, H, d_kv+d_rope]  (bf16 on the MFMA path, fp32 on SIMT)
+ *   [1] lse_part  fp32 [B, n_splits, H]
+ *   [2] o_part    fp32 [B, n_splits, H, d_kv]   (normalised within the chunk)
+ *   [3] bytes per q~ element (2 or 4) */
+mla_status mla_decode_absorbed_workspace_layout(const mla_decode_desc* desc,
+                                                size_t offsets[4]);
+
+/* Static description of a status code. */
+const char* mla_status_string(mla_status status);
+
+/* Text of the last HIP error seen by this thread (empty if none). */
+const char* mla_last_error(void);
+
+/* Build information: offload target and kernel families compiled in. */
+const char* mla_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H */

@@ -1,0 +1,198 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mla.h declares, sizes workspaces, and rejects invalid calls on the host
+before anything is enqueued (so fake device pointers are never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from head_latent_attention_02_amd import mla
+from head_latent_attention_02_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mla.LIB_PATH),
+                                reason="libmla.so not built (run __graft_entry__.build())")
+
+FAKE = 0x10000          # never dereferenced: every call below fails validation first
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = mla.library()
+    declared = _header_functions()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(mla.EXPORTED_SYMBOLS)
+
+
+def test_status_strings_and_info():
+    lib = mla.library()
+    for code, name in [(0, "MLA_OK"), (1, "MLA_ERR_INVALID_ARGUMENT"), (2, "MLA_ERR_UNSUPPORTED"),
+                       (3, "MLA_ERR_WORKSPACE_TOO_SMALL"), (4, "MLA_ERR_HIP")]:
+        assert lib.mla_status_string(code).decode() == name
+    assert "gfx950" in mla.build_info()
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """ctypes field offsets equal what a C compiler makes of include/mla.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void) {"]
+    for cname, py in [("mla_explicit_desc", mla.MlaExplicitDesc), ("mla_decode_desc", mla.MlaDecodeDesc)]:
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in [("mla_explicit_desc", mla.MlaExplicitDesc), ("mla_decode_desc", mla.MlaDecodeDesc)]:
+        assert got[(cname, "size")] == ctypes.sizeof(py)
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def _v3_desc(**kw):
+    base = dict(batch=1, s_q=4096, s_kv=4096, n_heads=128, d_kv=512, d_nope=128, d_rope=64, d_v=128)
+    base.update(kw)
+    return mla.explicit_desc(**base)
+
+
+def test_explicit_workspace_sizes():
+    d = _v3_desc()
+    ws = mla.mla_fwd_explicit_workspace_size(d)
+    # K_nope + V^T fp16 for 4096 padded rows x 128 heads x 256, plus small tables
+    assert ws >= 2 * 128 * 4096 * 256
+    assert ws < 2 * 128 * 4096 * 256 + (8 << 20)
+    kn, vt, kr, s_pad = mla.mla_fwd_explicit_workspace_layout(d)
+    assert s_pad == 4096 and kn < vt < kr < ws
+    # one SP rank: only the 8192 visible latent rows are projected
+    d2 = _v3_desc(s_q=2048, s_kv=16384, q_pos0=6144)
+    assert mla.mla_fwd_explicit_workspace_layout(d2)[3] == 8192
+    # fp32 inputs take the SIMT path, which has no MFMA layout
+    d3 = _v3_desc(in_dtype=mla.MLA_FP32)
+    assert mla.mla_fwd_explicit_workspace_size(d3) > 0
+    with pytest.raises(mla.MlaError):
+        mla.mla_fwd_explicit_workspace_layout(d3)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("batch", 0), ("n_heads", 0), ("s_q", -1), ("d_rope", 63), ("d_rope", 0), ("d_kv", 0),
+    ("causal", 2), ("in_dtype", 7), ("algo", 9), ("rope_base", -1.0), ("softmax_scale", float("nan")),
+])
+def test_explicit_rejects_bad_descriptor(field, value):
+    d = _v3_desc()
+    setattr(d, field, value)
+    assert mla.mla_fwd_explicit_workspace_size(d) == 0
+    st = mla.library().mla_fwd_explicit(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                        1 << 40, None)
+    assert st == mla.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_explicit_null_pointers_and_workspace():
+    lib = mla.library()
+    d = _v3_desc()
+    ws = mla.mla_fwd_explicit_workspace_size(d)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None]
+    for i in range(6):
+        a = list(args)
+        a[i] = None
+        assert lib.mla_fwd_explicit(ctypes.byref(d), *a) == mla.MLA_ERR_INVALID_ARGUMENT
+    a = list(args)
+    a[8] = ws - 1
+    assert lib.mla_fwd_explicit(ctypes.byref(d), *a) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args)
+    a[7] = None
+    assert lib.mla_fwd_explicit(ctypes.byref(d), *a) == mla.MLA_ERR_INVALID_ARGUMENT
+    # misaligned operand on the MFMA path
+    a = list(args)
+    a[0] = FAKE + 2
+    assert lib.mla_fwd_explicit(ctypes.byref(d), *a) == mla.MLA_ERR_INVALID_ARGUMENT
+    # empty query set: valid and a no-op that touches nothing
+    d0 = _v3_desc(s_q=0)
+    assert lib.mla_fwd_explicit(ctypes.byref(d0), None, None, FAKE, FAKE, FAKE, None, None, FAKE,
+                                mla.mla_fwd_explicit_workspace_size(d0), None) == mla.MLA_OK
+
+
+def test_explicit_unsupported():
+    lib = mla.library()
+    d = _v3_desc(d_nope=96, algo=mla.MLA_ALGO_MFMA)
+    assert mla.mla_fwd_explicit_workspace_size(d) == 0
+    assert lib.mla_fwd_explicit(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                None) == mla.MLA_ERR_UNSUPPORTED
+    # SIMT path limit on head widths
+    d = _v3_desc(d_nope=256, d_rope=64, d_v=256, algo=mla.MLA_ALGO_SIMT)
+    assert lib.mla_fwd_explicit(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                None) == mla.MLA_ERR_UNSUPPORTED
+
+
+def _dec_desc(**kw):
+    base = dict(batch=64, n_heads=128, d_kv=512, d_nope=128, d_rope=64, d_v=128, max_cache_len=32768,
+                n_splits=16)
+    base.update(kw)
+    return mla.decode_desc(**base)
+
+
+def test_decode_workspace_and_layout():
+    d = _dec_desc()
+    ws = mla.mla_decode_absorbed_workspace_size(d)
+    q, l, o, esz = mla.mla_decode_absorbed_workspace_layout(d)
+    assert esz == 2 and q < l < o < ws
+    assert ws - o >= 64 * 16 * 128 * 512 * 4
+    d2 = _dec_desc(in_dtype=mla.MLA_FP32)
+    assert mla.mla_decode_absorbed_workspace_layout(d2)[3] == 4
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, mla.MLA_ERR_INVALID_ARGUMENT), ("n_splits", 0, mla.MLA_ERR_INVALID_ARGUMENT),
+    ("max_cache_len", -1, mla.MLA_ERR_INVALID_ARGUMENT), ("cache_batch_stride", 100, mla.MLA_ERR_INVALID_ARGUMENT),
+    ("d_rope", 3, mla.MLA_ERR_INVALID_ARGUMENT), ("n_splits", 65, mla.MLA_ERR_UNSUPPORTED),
+    ("out_dtype", 5, mla.MLA_ERR_INVALID_ARGUMENT),
+])
+def test_decode_rejects(field, value, status):
+    d = _dec_desc()
+    setattr(d, field, value)
+    st = mla.library().mla_decode_absorbed(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                           1 << 40, None)
+    assert st == status
+
+
+def test_decode_mfma_eligibility():
+    lib = mla.library()
+    for kw in [dict(n_heads=24), dict(n_heads=256), dict(cache_batch_stride=32768 * 576 + 4)]:
+        d = _dec_desc(algo=mla.MLA_ALGO_MFMA, **kw)
+        st = lib.mla_decode_absorbed(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                     None)
+        assert st == mla.MLA_ERR_UNSUPPORTED, kw
+    d = _dec_desc()
+    ws = mla.mla_decode_absorbed_workspace_size(d)
+    assert lib.mla_decode_absorbed(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws - 1,
+                                   None) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.mla_decode_absorbed(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, ws,
+                                   None) == mla.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_flop_and_byte_accounting():
+    v3 = I.EXPLICIT_CONFIGS["v3_bf16"].flops()
+    assert v3["up_proj"] == 2 * 4096 * 512 * 128 * 256
+    assert v3["attention"] == 2 * 128 * (4096 * 4097 // 2) * 320
+    sp = I.EXPLICIT_CONFIGS["v3_sp8_rank3"]
+    assert sp.visible_keys() == 8192
+    assert sp.visible_pairs() == sum(6144 + i + 1 for i in range(2048))
+    dec = I.DECODE_CONFIGS["v3_decode_b64_32k"].algorithmic_bytes()
+    assert dec["cache"] == 64 * 32768 * 576 * 2

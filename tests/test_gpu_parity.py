@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Bars: bf16 configurations max|d| <= 1e-2 and rel-L2 <= 5e-3 on the output;
+the fp32 configuration max|d| <= 1e-5.  LSE is checked to the same absolute
+bar where finite, and -inf exactly where the oracle has -inf.  Large
+configurations compare sampled heads / rows / sequences that the oracle
+computes one by one.  Workspaces are filled with NaN bytes before each call so
+that a kernel reading memory it did not write shows up.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from head_latent_attention_02_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS, BF16_REL_L2, FP32_MAX_ABS = 1e-2, 5e-3, 1e-5
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from head_latent_attention_02_amd import mla as m
+    m.library()
+    return m
+
+
+def _dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dtype).cuda()
+
+
+def _poisoned(nbytes):
+    return torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+def _compare(got, ref, bf16, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    denom = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref) / denom) if denom > 0 else float(np.linalg.norm(got))
+    _say(f"{what}: max|d|={max_abs:.3e} rel-L2={rel:.3e}")
+    if bf16:
+        assert max_abs <= BF16_MAX_ABS, f"{what}: max|d| {max_abs}"
+        assert rel <= BF16_REL_L2, f"{what}: rel-L2 {rel}"
+    else:
+        assert max_abs <= FP32_MAX_ABS, f"{what}: max|d| {max_abs}"
+
+
+def _compare_lse(got, ref, bf16, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(got), ~fin), f"{what}: -inf pattern differs"
+    if fin.any():
+        err = float(np.abs(got[fin] - ref[fin]).max())
+        _say(f"{what}: lse max|d|={err:.3e}")
+        assert err <= (BF16_MAX_ABS if bf16 else FP32_MAX_ABS), f"{what}: lse max|d| {err}"
+
+
+def _run_explicit(mla, cfg, x, *, algo=0, out_dtype=torch.float32, poison=True):
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    t = {k: _dev(v, tdt) for k, v in x.items()}
+    desc = mla.explicit_desc(batch=cfg.batch, s_q=cfg.s_q, s_kv=cfg.s_kv, n_heads=cfg.n_heads, d_kv=cfg.d_kv,
+                             d_nope=cfg.d_nope, d_rope=cfg.d_rope, d_v=cfg.d_v, q_pos0=cfg.q_pos0,
+                             kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale,
+                             in_dtype=mla.MLA_BF16 if cfg.dtype == "bf16" else mla.MLA_FP32, algo=algo)
+    ws = _poisoned(mla.mla_fwd_explicit_workspace_size(desc)) if poison else None
+    _say(f"explicit {cfg.name}: B={cfg.batch} Sq={cfg.s_q} Skv={cfg.s_kv} H={cfg.n_heads} q_pos0={cfg.q_pos0} "
+         f"kv_pos0={cfg.kv_pos0} causal={cfg.causal} algo={algo} out={out_dtype}")
+    out, lse, ws = mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"],
+                                        q_pos0=cfg.q_pos0, kv_pos0=cfg.kv_pos0, causal=cfg.causal,
+                                        softmax_scale=cfg.softmax_scale, out_dtype=out_dtype, algo=algo,
+                                        workspace=ws)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy(), ws, desc
+
+
+def _oracle_explicit(cfg, x, heads=None, rows=None):
+    return O.explicit_fwd(x["q_nope"], x["q_pe"], x["c_kv"], x["k_pe"], x["w_kv_b"], q_pos0=cfg.q_pos0,
+                          kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale,
+                          rope_base=cfg.rope_base, heads=heads, rows=rows)
+
+
+# ------------------------------------------------------------ explicit ----
+def test_tiny_fp32(mla):
+    cfg = I.EXPLICIT_CONFIGS["tiny_fp32"]
+    x = I.make_explicit_inputs(cfg)
+    o, l, _, _ = _run_explicit(mla, cfg, x)
+    ro, rl = _oracle_explicit(cfg, x)
+    _compare(o, ro, False, "tiny_fp32 out")
+    _compare_lse(l, rl, False, "tiny_fp32")
+
+
+EDGE = [
+    I.small_explicit("ragged", batch=2, s_q=300, s_kv=300, n_heads=3, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     dtype="bf16", seed=101),
+    I.small_explicit("offset_q", s_q=100, s_kv=612, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=512, dtype="bf16", seed=102),
+    I.small_explicit("masked_rows", s_q=96, s_kv=96, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=0, kv_pos0=40, dtype="bf16", seed=103),
+    I.small_explicit("noncausal", s_q=77, s_kv=131, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     causal=False, dtype="bf16", seed=104),
+    I.small_explicit("one_key", s_q=1, s_kv=1, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     dtype="bf16", seed=105),
+    I.small_explicit("skv17", s_q=40, s_kv=17, n_heads=1, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=0, causal=False, dtype="bf16", seed=106),
+    I.small_explicit("multi_tile", s_q=700, s_kv=700, n_heads=1, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     dtype="bf16", seed=107),
+    I.small_explicit("far_pos", s_q=64, s_kv=320, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=30000, kv_pos0=29744, dtype="bf16", seed=108),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=lambda c: c.name)
+def test_mfma_explicit_edges(mla, cfg):
+    x = I.make_explicit_inputs(cfg)
+    o, l, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA)
+    ro, rl = _oracle_explicit(cfg, x)
+    _compare(o, ro, True, f"{cfg.name} out")
+    _compare_lse(l, rl, True, cfg.name)
+
+
+@pytest.mark.parametrize("cfg", EDGE[:4], ids=lambda c: c.name)
+def test_simt_explicit_bf16(mla, cfg):
+    x = I.make_explicit_inputs(cfg)
+    o, l, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_SIMT)
+    ro, rl = _oracle_explicit(cfg, x)
+    # fp32 arithmetic on bf16 inputs: far inside the bf16 bar
+    _compare(o, ro, False if np.abs(ro).max() < 8 else True, f"simt {cfg.name} out")
+
+
+def test_bf16_output(mla):
+    cfg = EDGE[0]
+    x = I.make_explicit_inputs(cfg)
+    o, l, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA, out_dtype=torch.bfloat16)
+    ro, rl = _oracle_explicit(cfg, x)
+    # bf16 output rounding is at most half an ulp of |O| <= 4 here
+    assert np.abs(o - ro).max() <= 2.0 ** -8 * max(1.0, np.abs(ro).max()) + 2e-3
+    _compare_lse(l, rl, True, "bf16-out")
+
+
+def test_upproj_intermediates(mla):
+    cfg = I.small_explicit("upproj", batch=2, s_q=300, s_kv=300, n_heads=2, d_kv=512, d_nope=128, d_rope=64,
+                           d_v=128, dtype="bf16", seed=111)
+    x = I.make_explicit_inputs(cfg)
+    _, _, ws, desc = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA)
+    off_kn, off_vt, off_kr, s_pad = mla.mla_fwd_explicit_workspace_layout(desc)
+    B, H, S = cfg.batch, cfg.n_heads, cfg.s_kv
+    kn = ws[off_kn:off_kn + 2 * B * H * s_pad * 128].view(torch.float16).view(B, H, s_pad, 128)
+    vt = ws[off_vt:off_vt + 2 * B * H * 128 * s_pad].view(torch.float16).view(B, H, 128, s_pad)
+    kr = ws[off_kr:off_kr + 2 * B * s_pad * 64].view(torch.float16).view(B, s_pad, 64)
+    w_uk, w_uv = O.weight_slices(x["w_kv_b"], H, 128, 128)
+    c = x["c_kv"].astype(np.float64)
+    for b in range(B):
+        for h in range(H):
+            rk = c[b] @ w_uk[h].T
+            rv = c[b] @ w_uv[h].T
+            gk = kn[b, h, :S].float().cpu().numpy()
+            gv = vt[b, h, :, :S].float().cpu().numpy().T
+            assert np.abs(gk - rk).max() <= 2e-3 * max(1, np.abs(rk).max())
+            assert np.abs(gv - rv).max() <= 2e-3 * max(1, np.abs(rv).max())
+        rr = O.rope_rotate(x["k_pe"][b], np.arange(S), 10000.0)
+        assert np.abs(kr[b, :S].float().cpu().numpy() - rr).max() <= 2e-3 * max(1, np.abs(rr).max())
+
+
+def test_v2lite_full(mla):
+    cfg = I.EXPLICIT_CONFIGS["v2lite_bf16"]
+    x = I.make_explicit_inputs(cfg)
+    o, l, _, _ = _run_explicit(mla, cfg, x)
+    ro, rl = _oracle_explicit(cfg, x)
+    _compare(o, ro, True, "v2lite out")
+    _compare_lse(l, rl, True, "v2lite")
+
+
+def _sample_rows(n, rng, k=96):
+    rows = set(range(min(32, n))) | set(range(max(0, n - 32), n))
+    rows |= set(rng.choice(n, size=min(k, n), replace=False).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["v3_bf16", "v3_sp8_rank3"])
+def test_v3_sampled(mla, name):
+    cfg = I.EXPLICIT_CONFIGS[name]
+    x = I.make_explicit_inputs(cfg)
+    o, l, _, _ = _run_explicit(mla, cfg, x)
+    rng = np.random.default_rng(7)
+    heads = [0, 1, 63, 64, 126, 127]
+    rows = _sample_rows(cfg.s_q, rng)
+    ro, rl = _oracle_explicit(cfg, x, heads=heads, rows=rows)
+    _compare(o[:, rows][:, :, heads], ro, True, f"{name} sampled out")
+    _compare_lse(l[:, heads][:, :, rows], rl, True, name)
+    # whole-tensor properties: finite, and rel-L2 of the sample representative
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+def test_explicit_repeatable(mla):
+    cfg = EDGE[0]
+    x = I.make_explicit_inputs(cfg)
+    o1, l1, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA)
+    o2, l2, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# -------------------------------------------------------------- decode ----
+def _run_decode(mla, cfg, x, *, algo=0, stride_rows=None, poison=True):
+    B, L = cfg.batch, cfg.cache_len
+    dlat = cfg.d_kv + cfg.d_rope
+    rows = L if stride_rows is None else stride_rows
+    bits = x["cache_bits"]
+    if rows != L:
+        pad = np.zeros((B, rows, dlat), dtype=np.uint16)
+        pad[:, :L] = bits
+        bits = pad
+    cache = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)[:, :L]
+    qn = _dev(x["q_nope"], torch.bfloat16)
+    qp = _dev(x["q_pe"], torch.bfloat16)
+    w = _dev(x["w_kv_b"], torch.bfloat16)
+    cl = torch.from_numpy(x["cache_len"]).cuda()
+    desc = mla.decode_desc(batch=B, n_heads=cfg.n_heads, d_kv=cfg.d_kv, d_nope=cfg.d_nope, d_rope=cfg.d_rope,
+                           d_v=cfg.d_v, max_cache_len=L, cache_batch_stride=cache.stride(0),
+                           n_splits=cfg.n_splits, softmax_scale=cfg.softmax_scale, algo=algo)
+    ws = _poisoned(mla.mla_decode_absorbed_workspace_size(desc)) if poison else None
+    _say(f"decode {cfg.name}: B={B} L={L} H={cfg.n_heads} splits={cfg.n_splits} lens={x['cache_len'][:8]} "
+         f"stride_rows={rows} algo={algo}")
+    out, lse, ws = mla.mla_decode_absorbed(qn, qp, cache, cl, w, n_splits=cfg.n_splits, d_kv=cfg.d_kv,
+                                           softmax_scale=cfg.softmax_scale, algo=algo, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), ws, desc
+
+
+def _oracle_decode(cfg, x, batches=None):
+    bits = x["cache_bits"]
+    return O.decode_absorbed(x["q_nope"], x["q_pe"], lambda b: I.bf16_bits_to_f32(bits[b]), x["cache_len"],
+                             x["w_kv_b"], n_splits=cfg.n_splits, d_kv=cfg.d_kv, softmax_scale=cfg.softmax_scale,
+                             rope_base=cfg.rope_base, batches=batches)
+
+
+DEC_EDGE = [
+    (I.small_decode("lens", batch=5, cache_len=700, n_heads=16, n_splits=16, seed=201), [700, 1, 0, 17, 333], None),
+    (I.small_decode("stride", batch=3, cache_len=515, n_heads=32, n_splits=3, seed=202), [515, 514, 100], 530),
+    (I.small_decode("one_split", batch=2, cache_len=300, n_heads=128, n_splits=1, seed=203), [300, 299], None),
+    (I.small_decode("many_splits", batch=2, cache_len=100, n_heads=16, n_splits=64, seed=204), [100, 63], None),
+]
+
+
+@pytest.mark.parametrize("case", DEC_EDGE, ids=lambda c: c[0].name)
+@pytest.mark.parametrize("algo", [2, 1], ids=["mfma", "simt"])
+def test_decode_edges(mla, case, algo):
+    cfg, lens, stride_rows = case
+    x = I.make_decode_inputs(cfg, cache_len=np.array(lens, dtype=np.int32))
+    o, l, ws, desc = _run_decode(mla, cfg, x, algo=algo, stride_rows=stride_rows)
+    r = _oracle_decode(cfg, x)
+    _compare(o, r["out"], True, f"decode {cfg.name} out")
+    _compare_lse(l, r["lse"], True, f"decode {cfg.name}")
+    # per-chunk partials left in the workspace
+    off_q, off_l, off_o, esz = mla.mla_decode_absorbed_workspace_layout(desc)
+    B, ns, H = cfg.batch, cfg.n_splits, cfg.n_heads
+    lp = ws[off_l:off_l + 4 * B * ns * H].view(torch.float32).view(B, ns, H).cpu().numpy()
+    op = ws[off_o:off_o + 4 * B * ns * H * cfg.d_kv].view(torch.float32).view(B, ns, H, cfg.d_kv).cpu().numpy()
+    _compare_lse(lp, r["lse_part"], True, f"decode {cfg.name} lse_part")
+    fin = np.isfinite(r["lse_part"])
+    assert np.all(op[~fin] == 0)
+    _compare(op[fin], r["o_part"][fin], True, f"decode {cfg.name} o_part")
+
+
+def test_decode_full_config_sampled(mla):
+    cfg = I.DECODE_CONFIGS["v3_decode_b64_32k"]
+    _say("generating the 2.4 GB latent cache on the host")
+    x = I.make_decode_inputs(cfg)
+    o, l, _, _ = _run_decode(mla, cfg, x)
+    batches = [0, 31, 63]
+    r = _oracle_decode(cfg, x, batches=batches)
+    _compare(o[batches], r["out"], True, "decode v3 sampled out")
+    _compare_lse(l[batches], r["lse"], True, "decode v3 sampled")
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+def test_decode_repeatable(mla):
+    cfg, lens, _ = DEC_EDGE[0]
+    x = I.make_decode_inputs(cfg, cache_len=np.array(lens, dtype=np.int32))
+    o1, l1, _, _ = _run_decode(mla, cfg, x, algo=2)
+    o2, l2, _, _ = _run_decode(mla, cfg, x, algo=2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2, equal_nan=True)
