@@ -1,0 +1,270 @@
+"""Benchmark of the MLA forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * explicit (LAGA-local) forward at DeepSeek-V3 dims: B=1, S=4096, n_h=128,
+    d_kv=512, d_nope=128, d_rope=64, d_v=128, causal (latent up-projection,
+    RoPE, causal attention);
+  * absorbed split-KV decode: B=64 sequences of 32768 cached tokens, n_h=128,
+    16 KV chunks merged by log-sum-exp, up-projected to d_v=128.
+
+Prints ONE JSON line.  `value` is the explicit forward's algorithmic TFLOP/s
+(causally visible pairs plus the up-projection of the visible latent rows,
+divided by the time of the explicit part of each step); the decode part is
+reported as tokens/s and algorithmic HBM GB/s.  Per-kernel durations come from
+HIP events the library records around each of its launches on the stream the
+kernels run on (mla_timing_*), inside the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 / fp16
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "MLA attn fwd TFLOP/s (+% MFMA peak) at V3 dims; absorbed decode tok/s (+% HBM)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--explicit-config", default="v3_bf16")
+    p.add_argument("--decode-config", default="v3_decode_b64_32k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=15.0,
+                   help="approximate CPU seconds for the oracle baseline sample")
+    return p.parse_args()
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(ecfg, x_host, out_gpu, dcfg, dx_host, dout_gpu, budget_s):
+    """Time the fp64 oracle on a bounded sample of the same workload and, on
+    the same sample, compare the GPU outputs with it."""
+    from oracle import mla_oracle as O
+
+    # explicit: the first k heads, all query rows
+    t0 = time.perf_counter()
+    ro, _ = O.explicit_fwd(x_host["q_nope"], x_host["q_pe"], x_host["c_kv"], x_host["k_pe"], x_host["w_kv_b"],
+                           q_pos0=ecfg.q_pos0, kv_pos0=ecfg.kv_pos0, causal=ecfg.causal,
+                           softmax_scale=ecfg.softmax_scale, heads=[0])
+    t_one = time.perf_counter() - t0
+    k = int(max(1, min(ecfg.n_heads, (0.7 * budget_s) // max(t_one, 1e-3))))
+    heads = list(range(k))
+    t0 = time.perf_counter()
+    ro, _ = O.explicit_fwd(x_host["q_nope"], x_host["q_pe"], x_host["c_kv"], x_host["k_pe"], x_host["w_kv_b"],
+                           q_pos0=ecfg.q_pos0, kv_pos0=ecfg.kv_pos0, causal=ecfg.causal,
+                           softmax_scale=ecfg.softmax_scale, heads=heads)
+    t_exp = time.perf_counter() - t0
+    fl = ecfg.flops()
+    flops_sample = fl["total"] * k / ecfg.n_heads
+    got = out_gpu[:, :, :k]
+    err = np.abs(got - ro)
+    parity_exp = {"max_abs": float(err.max()), "rel_l2": float(np.linalg.norm(got - ro) / np.linalg.norm(ro)),
+                  "sample": f"heads 0..{k - 1} of {ecfg.n_heads}, all {ecfg.s_q} query rows"}
+
+    # decode: one sequence, all heads
+    bits = dx_host["cache_bits"]
+    from head_latent_attention_02_amd import inputs as I
+    t0 = time.perf_counter()
+    r = O.decode_absorbed(dx_host["q_nope"], dx_host["q_pe"], lambda b: I.bf16_bits_to_f32(bits[b]),
+                          dx_host["cache_len"], dx_host["w_kv_b"], n_splits=dcfg.n_splits, d_kv=dcfg.d_kv,
+                          softmax_scale=dcfg.softmax_scale, batches=[0])
+    t_dec = time.perf_counter() - t0
+    dg = dout_gpu[:1]
+    derr = np.abs(dg - r["out"])
+    parity_dec = {"max_abs": float(derr.max()),
+                  "rel_l2": float(np.linalg.norm(dg - r["out"]) / np.linalg.norm(r["out"])),
+                  "sample": f"sequence 0 of {dcfg.batch}, all {dcfg.n_heads} heads"}
+    cores = blas_threads()
+    return ({"value": flops_sample / t_exp / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+             "sample": f"explicit fwd at {ecfg.name} dims, heads 0..{k - 1} of {ecfg.n_heads} (all rows), "
+                       f"{t_exp:.1f} s; fp64 numpy"},
+            {"value": 1.0 / t_dec, "unit": "tok/s", "cores": cores, "kind": "oracle",
+             "sample": f"absorbed decode, 1 of {dcfg.batch} sequences (L={dcfg.cache_len}, all heads), "
+                       f"{t_dec:.1f} s; fp64 numpy"},
+            {"explicit": parity_exp, "decode": parity_dec})
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs the MLA hot path on one GPU; multi-GPU runs are not "
+                                   "part of this build (--gpus must be 1)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from head_latent_attention_02_amd import inputs as I
+    from head_latent_attention_02_amd import mla
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mla.library()
+
+    ecfg = I.EXPLICIT_CONFIGS[args.explicit_config]
+    dcfg = I.DECODE_CONFIGS[args.decode_config]
+    log(f"generating inputs: {ecfg.name}, {dcfg.name}")
+    x = I.make_explicit_inputs(ecfg)
+    dx = I.make_decode_inputs(dcfg)
+    t = {k: torch.from_numpy(v).to(torch.bfloat16).to(dev) for k, v in x.items()}
+    cache = torch.from_numpy(dx["cache_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    dq_nope = torch.from_numpy(dx["q_nope"]).to(torch.bfloat16).to(dev)
+    dq_pe = torch.from_numpy(dx["q_pe"]).to(torch.bfloat16).to(dev)
+    dw = torch.from_numpy(dx["w_kv_b"]).to(torch.bfloat16).to(dev)
+    dlen = torch.from_numpy(dx["cache_len"]).to(dev)
+
+    out = torch.empty((ecfg.batch, ecfg.s_q, ecfg.n_heads, ecfg.d_v), dtype=torch.float32, device=dev)
+    lse = torch.empty((ecfg.batch, ecfg.n_heads, ecfg.s_q), dtype=torch.float32, device=dev)
+    dout = torch.empty((dcfg.batch, dcfg.n_heads, dcfg.d_v), dtype=torch.float32, device=dev)
+    dlse = torch.empty((dcfg.batch, dcfg.n_heads), dtype=torch.float32, device=dev)
+    ws = dws = None
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    exp_ms, dec_ms = [], []
+
+    def step(record):
+        nonlocal ws, dws
+        if record:
+            ev[0].record()
+        _, _, ws = mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"],
+                                        q_pos0=ecfg.q_pos0, kv_pos0=ecfg.kv_pos0, causal=ecfg.causal,
+                                        softmax_scale=ecfg.softmax_scale, out=out, lse=lse, workspace=ws)
+        if record:
+            ev[1].record()
+        _, _, dws = mla.mla_decode_absorbed(dq_nope, dq_pe, cache, dlen, dw, n_splits=dcfg.n_splits,
+                                            softmax_scale=dcfg.softmax_scale, out=dout, lse=dlse, workspace=dws)
+        if record:
+            ev[2].record()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    mla.mla_timing_reset()
+    mla.mla_timing_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        exp_ms.append(ev[0].elapsed_time(ev[1]))
+        dec_ms.append(ev[1].elapsed_time(ev[2]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mla.mla_timing_end()
+    kt = mla.mla_timing_get()
+    log("timed region done")
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    e_ms = float(np.mean(exp_ms))
+    d_ms = float(np.mean(dec_ms))
+    fl = ecfg.flops()
+    dflops = dcfg.flops()
+    dbytes = dcfg.algorithmic_bytes()
+    explicit_tflops = fl["total"] / (e_ms * 1e-3) / 1e12
+    decode_tok_s = dcfg.batch / (d_ms * 1e-3)
+    decode_gbs = dbytes["total"] / (d_ms * 1e-3) / 1e9
+
+    # per-kernel averages and their algorithmic rates
+    B, H, L = dcfg.batch, dcfg.n_heads, dcfg.cache_len
+    per_kernel_work = {
+        "mfma_attention": ("TFLOP/s", fl["attention"]),
+        "mfma_up_projection": ("TFLOP/s", fl["up_proj"]),
+        "mfma_split_kv": ("GB/s", dbytes["cache"]),
+        "lse_combine": ("GB/s", B * dcfg.n_splits * H * (dcfg.d_kv + 1) * 4 + H * dcfg.d_v * dcfg.d_kv * 2),
+        "absorb": ("GB/s", H * dcfg.d_nope * dcfg.d_kv * 2 + B * H * (dcfg.d_kv + dcfg.d_rope) * 2),
+    }
+    kernels = {}
+    for name, (ms_tot, n) in kt.items():
+        avg = ms_tot / max(n, 1)
+        ent = {"avg_ms": avg, "launches_per_step": n / args.steps}
+        if name in per_kernel_work:
+            unit, work = per_kernel_work[name]
+            ent["achieved"] = work / (avg * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+            ent["unit"] = unit
+        kernels[name] = ent
+
+    def roof(name, bound, unit, work, peak):
+        if name not in kt:
+            return None
+        avg = kt[name][0] / max(kt[name][1], 1)
+        ach = work / (avg * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak, "traffic": None,
+                "kernel": name, "avg_ms": avg,
+                "work_per_launch": work}
+
+    roofline = roof("mfma_attention", "mfma", "TFLOP/s", fl["attention"], PEAK_MFMA_TFLOPS)
+    roofline_decode = roof("mfma_split_kv", "hbm", "GB/s", dbytes["cache"], PEAK_HBM_GBS)
+
+    res = {
+        "metric": METRIC,
+        "value": explicit_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{ecfg.name} explicit fwd (B={ecfg.batch}, S={ecfg.s_q}, n_h={ecfg.n_heads}, causal) + "
+                        f"{dcfg.name} absorbed decode (B={dcfg.batch}, L={dcfg.cache_len}, n_h={dcfg.n_heads}, "
+                        f"{dcfg.n_splits} splits)",
+            "explicit": {"batch": ecfg.batch, "seq_len": ecfg.s_q, "n_heads": ecfg.n_heads, "d_kv": ecfg.d_kv,
+                         "d_nope": ecfg.d_nope, "d_rope": ecfg.d_rope, "d_v": ecfg.d_v,
+                         "algorithmic_flop": fl["total"]},
+            "decode": {"batch": dcfg.batch, "cache_len": dcfg.cache_len, "n_heads": dcfg.n_heads,
+                       "n_splits": dcfg.n_splits, "algorithmic_bytes": dbytes["total"],
+                       "algorithmic_flop": dflops["total"]},
+            "arithmetic": "bf16 inputs; up-projection bf16 MFMA; attention QK^T/PV fp16 MFMA; decode bf16 MFMA; "
+                          "fp32 accumulate and fp32 outputs",
+        },
+        "explicit": {"ms": e_ms, "tflops": explicit_tflops, "frac_mfma_peak": explicit_tflops / PEAK_MFMA_TFLOPS},
+        "decode": {"ms": d_ms, "tok_per_s": decode_tok_s, "algorithmic_gbs": decode_gbs,
+                   "frac_hbm_peak": decode_gbs / PEAK_HBM_GBS},
+        "roofline": roofline,
+        "roofline_decode": roofline_decode,
+        "kernels": kernels,
+    }
+
+    if not args.no_cpu_baseline:
+        log("oracle CPU baseline on a bounded sample")
+        cb_e, cb_d, parity = cpu_baseline(ecfg, x, out.cpu().numpy(), dcfg, dx, dout.cpu().numpy(),
+                                          args.cpu_budget_s)
+        res["cpu_baseline"] = cb_e
+        res["cpu_baseline_decode"] = cb_d
+        res["parity_sample"] = parity
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

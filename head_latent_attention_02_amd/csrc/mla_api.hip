@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -25,6 +26,57 @@ mla_status hip_fail(hipError_t e, const char* where) {
   g_last_error = std::string(where) + ": " + hipGetErrorString(e);
   return MLA_ERR_HIP;
 }
+
+// ---------------------------------------------------------------- timing --
+struct TimingTotal {
+  const char* name;
+  double ms;
+  int64_t launches;
+};
+struct PendingLaunch {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct TimingState {
+  bool active = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<PendingLaunch> pending;
+  std::vector<TimingTotal> totals;
+};
+thread_local TimingState g_timing;
+
+hipEvent_t timing_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t e = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launcher call with events when timing is active.
+class TimedLaunch {
+ public:
+  TimedLaunch(const char* name, hipStream_t s) : name_(name), stream_(s) {
+    if (!g_timing.active) return;
+    start_ = timing_event();
+    if (start_ != nullptr) (void)hipEventRecord(start_, stream_);
+  }
+  ~TimedLaunch() {
+    if (!g_timing.active || start_ == nullptr) return;
+    hipEvent_t stop = timing_event();
+    if (stop == nullptr) return;
+    (void)hipEventRecord(stop, stream_);
+    g_timing.pending.push_back({name_, start_, stop});
+  }
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr;
+};
 
 // ---------------------------------------------------------------- explicit --
 struct ExplicitPlan {
@@ -206,21 +258,34 @@ mla_status mla_fwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
 
   float2* qtab = reinterpret_cast<float2*>(ws + p.off_qtab);
   float2* ktab = reinterpret_cast<float2*>(ws + p.off_ktab);
-  hipError_t e = launch_rope_table(qtab, a.q_pos0, a.Sq, a.dr, a.rope_base, s);
-  if (e != hipSuccess) return hip_fail(e, "rope table (queries)");
-  e = launch_rope_table(ktab, a.kv_pos0, a.s_vis, a.dr, a.rope_base, s);
-  if (e != hipSuccess) return hip_fail(e, "rope table (keys)");
+  hipError_t e;
+  {
+    TimedLaunch t("rope_tables", s);
+    e = launch_rope_table(qtab, a.q_pos0, a.Sq, a.dr, a.rope_base, s);
+    if (e == hipSuccess) e = launch_rope_table(ktab, a.kv_pos0, a.s_vis, a.dr, a.rope_base, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "rope tables");
   if (p.mfma) {
     uint16_t* kn = reinterpret_cast<uint16_t*>(ws + p.off_kn);
     uint16_t* vt = reinterpret_cast<uint16_t*>(ws + p.off_v);
     uint16_t* kr = reinterpret_cast<uint16_t*>(ws + p.off_krot);
-    e = launch_mfma_upproj(a, kn, vt, s);
+    {
+      TimedLaunch t("mfma_up_projection", s);
+      e = launch_mfma_upproj(a, kn, vt, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "mfma up-projection");
-    e = launch_krot_f16(a, ktab, kr, s);
+    {
+      TimedLaunch t("key_rope_band", s);
+      e = launch_krot_f16(a, ktab, kr, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "key rope band");
-    e = launch_mfma_attention(a, kn, vt, kr, qtab, s);
+    {
+      TimedLaunch t("mfma_attention", s);
+      e = launch_mfma_attention(a, kn, vt, kr, qtab, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "mfma attention");
   } else {
+    TimedLaunch t("simt_explicit", s);
     e = launch_simt_explicit(a, reinterpret_cast<float*>(ws + p.off_kn), reinterpret_cast<float*>(ws + p.off_v),
                              reinterpret_cast<float*>(ws + p.off_krot), qtab, ktab, s);
     if (e != hipSuccess) return hip_fail(e, "simt explicit forward");
@@ -277,19 +342,83 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc, const void* q_nope, 
   hipError_t e;
   if (p.mfma) {
     uint16_t* qt = reinterpret_cast<uint16_t*>(ws + p.off_qt);
-    e = launch_absorb_bf16(a, qt, s);
+    {
+      TimedLaunch t("absorb", s);
+      e = launch_absorb_bf16(a, qt, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "query absorption");
-    e = launch_mfma_splitkv(a, qt, lse_part, o_part, s);
+    {
+      TimedLaunch t("mfma_split_kv", s);
+      e = launch_mfma_splitkv(a, qt, lse_part, o_part, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "mfma split-KV attention");
   } else {
     float* qt = reinterpret_cast<float*>(ws + p.off_qt);
-    e = launch_simt_absorb(a, qt, s);
+    {
+      TimedLaunch t("simt_absorb", s);
+      e = launch_simt_absorb(a, qt, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "query absorption");
-    e = launch_simt_splitkv(a, qt, lse_part, o_part, s);
+    {
+      TimedLaunch t("simt_split_kv", s);
+      e = launch_simt_splitkv(a, qt, lse_part, o_part, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "simt split-KV attention");
   }
-  e = launch_combine(a, lse_part, o_part, s);
+  {
+    TimedLaunch t("lse_combine", s);
+    e = launch_combine(a, lse_part, o_part, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "LSE combine");
+  return MLA_OK;
+}
+
+mla_status mla_timing_begin(void) {
+  g_timing.active = true;
+  return MLA_OK;
+}
+
+mla_status mla_timing_end(void) {
+  g_timing.active = false;
+  mla_status st = MLA_OK;
+  for (const PendingLaunch& p : g_timing.pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(p.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.start, p.stop);
+    if (e != hipSuccess) {
+      st = hip_fail(e, "timing");
+    } else {
+      bool found = false;
+      for (TimingTotal& t : g_timing.totals)
+        if (std::strcmp(t.name, p.name) == 0) {
+          t.ms += ms;
+          t.launches += 1;
+          found = true;
+        }
+      if (!found) g_timing.totals.push_back({p.name, (double)ms, 1});
+    }
+    g_timing.pool.push_back(p.start);
+    g_timing.pool.push_back(p.stop);
+  }
+  g_timing.pending.clear();
+  return st;
+}
+
+mla_status mla_timing_reset(void) {
+  g_timing.totals.clear();
+  return MLA_OK;
+}
+
+int32_t mla_timing_count(void) { return (int32_t)g_timing.totals.size(); }
+
+mla_status mla_timing_get(int32_t index, const char** name, double* total_ms, int64_t* launches) {
+  if (index < 0 || index >= (int32_t)g_timing.totals.size() || name == nullptr || total_ms == nullptr ||
+      launches == nullptr)
+    return MLA_ERR_INVALID_ARGUMENT;
+  const TimingTotal& t = g_timing.totals[index];
+  *name = t.name;
+  *total_ms = t.ms;
+  *launches = t.launches;
   return MLA_OK;
 }
 

@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "mla_fwd_explicit_workspace_size", "mla_fwd_explicit", "mla_fwd_explicit_workspace_layout",
     "mla_decode_absorbed_workspace_size", "mla_decode_absorbed", "mla_decode_absorbed_workspace_layout",
     "mla_status_string", "mla_last_error", "mla_build_info",
+    "mla_timing_begin", "mla_timing_end", "mla_timing_reset", "mla_timing_count", "mla_timing_get",
 )
 
 
@@ -93,6 +94,14 @@ def _lib() -> ctypes.CDLL:
         lib.mla_last_error.restype = ctypes.c_char_p
         lib.mla_build_info.argtypes = []
         lib.mla_build_info.restype = ctypes.c_char_p
+        for f in ("mla_timing_begin", "mla_timing_end", "mla_timing_reset"):
+            getattr(lib, f).argtypes = []
+            getattr(lib, f).restype = ctypes.c_int
+        lib.mla_timing_count.argtypes = []
+        lib.mla_timing_count.restype = ctypes.c_int32
+        lib.mla_timing_get.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
+                                       ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        lib.mla_timing_get.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -257,6 +266,29 @@ def mla_decode_absorbed(q_nope: torch.Tensor, q_pe: torch.Tensor, kv_cache: torc
                                     workspace.data_ptr(), workspace.numel(), _stream(dev))
     _check(st, "mla_decode_absorbed")
     return out, (lse if return_lse else None), workspace
+
+
+def mla_timing_begin():
+    _check(_lib().mla_timing_begin(), "mla_timing_begin")
+
+
+def mla_timing_end():
+    _check(_lib().mla_timing_end(), "mla_timing_end")
+
+
+def mla_timing_reset():
+    _check(_lib().mla_timing_reset(), "mla_timing_reset")
+
+
+def mla_timing_get() -> dict:
+    """{kernel name: (total ms, launches)} accumulated since the last reset."""
+    lib = _lib()
+    res = {}
+    for i in range(lib.mla_timing_count()):
+        name, ms, n = ctypes.c_char_p(), ctypes.c_double(), ctypes.c_int64()
+        _check(lib.mla_timing_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)), "mla_timing_get")
+        res[name.value.decode()] = (ms.value, n.value)
+    return res
 
 
 def build_info() -> str:

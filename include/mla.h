@@ -48,7 +48,8 @@
  *     angle = absolute position * theta_m, angles formed in fp64.
  *   - LSE outputs are natural logs of the sum of exp of the scaled logits;
  *     a query that sees no key gets O = 0 and LSE = -inf.
- *   - Calls are reentrant: the library keeps no state between calls.
+ *   - Calls are reentrant.  Apart from the optional per-thread timing records
+ *     (mla_timing_*), the library keeps no state between calls.
  */
 #ifndef MLA_H
 #define MLA_H
@@ -193,6 +194,26 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc,
  *   [3] bytes per q~ element (2 or 4) */
 mla_status mla_decode_absorbed_workspace_layout(const mla_decode_desc* desc,
                                                 size_t offsets[4]);
+
+/* ------------------------------------------------------------------------ */
+/* Per-kernel timing (profiling aid; not needed for computing)               */
+/* ------------------------------------------------------------------------ */
+/* Between mla_timing_begin() and mla_timing_end() on the calling thread, each
+ * kernel (or fixed group of kernels) the entry points above enqueue is
+ * bracketed by two HIP events recorded on the call's stream.  The launches
+ * themselves are unchanged.  mla_timing_end() waits for the recorded events
+ * and adds each launch's elapsed time to a per-name total, which
+ * mla_timing_get() reports until mla_timing_reset().  Events are created by
+ * the library the first time they are needed and reused afterwards.
+ * Errors: MLA_ERR_HIP if an event call fails; MLA_ERR_INVALID_ARGUMENT for an
+ * index out of range or a NULL output pointer. */
+mla_status mla_timing_begin(void);
+mla_status mla_timing_end(void);
+mla_status mla_timing_reset(void);
+int32_t mla_timing_count(void);
+/* name: static string owned by the library; total_ms: summed duration;
+ * launches: number of bracketed launches (host memory outputs). */
+mla_status mla_timing_get(int32_t index, const char** name, double* total_ms, int64_t* launches);
 
 /* Static description of a status code. */
 const char* mla_status_string(mla_status status);

@@ -275,7 +275,14 @@ def test_decode_edges(mla, case, algo):
     _compare_lse(lp, r["lse_part"], True, f"decode {cfg.name} lse_part")
     fin = np.isfinite(r["lse_part"])
     assert np.all(op[~fin] == 0)
-    _compare(op[fin], r["o_part"][fin], True, f"decode {cfg.name} o_part")
+    # o_part is an intermediate in latent space: a convex combination of cache
+    # rows whose weights the MFMA path rounds to bf16 (relative 2^-9 each), so
+    # its bar is relative to the rows' size: 1% of max|ref| and rel-L2 5e-3.
+    got, ref = op[fin], r["o_part"][fin]
+    err = float(np.abs(got - ref).max())
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    _say(f"decode {cfg.name} o_part: max|d|={err:.3e} (max|ref| {np.abs(ref).max():.2f}) rel-L2={rel:.3e}")
+    assert err <= 1e-2 * max(1.0, float(np.abs(ref).max())) and rel <= BF16_REL_L2
 
 
 def test_decode_full_config_sampled(mla):
