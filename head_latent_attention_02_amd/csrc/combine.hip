@@ -6,64 +6,114 @@
 // value part of W_kv_b ("A Training-Memory Regression in MLA Sequence
 // Parallelism ... LAGA" (Pith review), Fig. 2 "Absorbed (B2)", un-absorb).
 //
-// One block per (head, group of CB sequences): the head's W_UV rows are read
-// once per group while the group's merged accumulators sit in LDS.
+// One block per (head, group of CB sequences), 256 threads.
+//   1. chunk weights w_k = exp(lse_k - lse) per sequence (one wave each);
+//   2. merge: each thread owns float4 columns of the group's latent rows and
+//      issues the loads of all chunks of a column before combining them, so
+//      a whole chunk row is in flight at once (the step is bandwidth-bound);
+//   3. un-absorb: thread (v, half) computes out[b, h, v] for half of the
+//      group's sequences from W_UV[h] row v (read once per block, 16 bytes at
+//      a time) and the merged rows in LDS.
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int CB = 8;         // sequences per block
+constexpr int CB = 8;          // sequences per block
 constexpr int CTHREADS = 256;
+constexpr int MAXNS = 64;      // chunk limit (checked on the host)
+constexpr int KBATCH = 16;     // chunk loads in flight per column
+
+template <mla_dtype WT>
+__device__ __forceinline__ void load8(const void* w, int64_t idx, float (&f)[8]) {
+  if constexpr (WT == MLA_BF16) {
+    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(w) + idx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_bits_to_float((uint16_t)(raw[e] & 0xffff));
+      f[2 * e + 1] = bf16_bits_to_float((uint16_t)(raw[e] >> 16));
+    }
+  } else {
+    const f32x4_t* p = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(w) + idx);
+    f32x4_t a = p[0], b = p[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = a[e];
+      f[4 + e] = b[e];
+    }
+  }
+}
 
 template <mla_dtype WT, mla_dtype OT>
 __global__ void __launch_bounds__(CTHREADS)
 combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const float* __restrict__ o_part) {
-  extern __shared__ float olat[];            // [CB][dkv]
-  __shared__ float wk[CB][64];               // chunk weights (n_splits <= 64)
+  extern __shared__ __attribute__((aligned(16))) float olat[];   // [CB][dkv]
+  __shared__ float wk[CB][MAXNS];
   __shared__ float lse_s[CB];
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * CB;
   const int nb = min(CB, a.B - b0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ns = a.n_splits;
+  const int ns = a.n_splits, dkv = a.dkv;
 
-  // chunk weights: one wave per sequence
+  // 1. chunk weights
   for (int bi = wave; bi < nb; bi += CTHREADS / 64) {
-    int b = b0 + bi;
-    float l = (lane < ns) ? lse_part[((int64_t)b * ns + lane) * a.H + h] : -INFINITY;
-    float m = wave_max(l);
-    float e = (l == -INFINITY) ? 0.f : expf(l - m);
-    float tot = wave_sum(e);
+    const int b = b0 + bi;
+    const float l = (lane < ns) ? lse_part[((int64_t)b * ns + lane) * a.H + h] : -INFINITY;
+    const float m = wave_max(l);
+    const float e = (l == -INFINITY) ? 0.f : expf(l - m);
+    const float tot = wave_sum(e);
     if (lane < ns) wk[bi][lane] = (tot > 0.f) ? e / tot : 0.f;
     if (lane == 0) lse_s[bi] = (tot > 0.f) ? m + logf(tot) : -INFINITY;
   }
   __syncthreads();
-  for (int e = tid; e < nb * a.dkv; e += CTHREADS) {
-    int bi = e / a.dkv, c = e % a.dkv, b = b0 + bi;
-    float acc = 0.f;
-    for (int k = 0; k < ns; ++k) {
-      float wgt = wk[bi][k];
-      if (wgt != 0.f) acc += wgt * o_part[(((int64_t)b * ns + k) * a.H + h) * a.dkv + c];
+
+  // 2. merge (float4 columns; dkv is a multiple of 4 on this path)
+  const int c4n = dkv / 4;
+  const int64_t kstride = (int64_t)a.H * dkv;             // floats between chunks
+  for (int it = tid; it < nb * c4n; it += CTHREADS) {
+    const int bi = it / c4n, c4 = it - bi * c4n, b = b0 + bi;
+    const float* src = o_part + ((int64_t)b * ns * a.H + h) * dkv + 4 * c4;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < ns; k0 += KBATCH) {
+      f32x4_t v[KBATCH];
+#pragma unroll
+      for (int j = 0; j < KBATCH; ++j)
+        v[j] = (k0 + j < ns) ? *reinterpret_cast<const f32x4_t*>(src + (k0 + j) * kstride)
+                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KBATCH; ++j)
+        if (k0 + j < ns) acc += v[j] * wk[bi][k0 + j];
     }
-    olat[bi * a.dkv + c] = acc;
+    *reinterpret_cast<f32x4_t*>(&olat[bi * dkv + 4 * c4]) = acc;
   }
   __syncthreads();
-  // out[b,h,v] = W_UV[h][v] . o_lat[b]: one wave per row v, lanes over c
+
+  // 3. un-absorb: out[b, h, v] = W_UV[h][v] . o_lat[b]
+  constexpr int HALF = CB / 2;
   const int64_t wrow0 = (int64_t)h * (a.dn + a.dv) + a.dn;
-  for (int v = wave; v < a.dv; v += CTHREADS / 64) {
-    float acc[CB];
+  for (int it = tid; it < a.dv * 2; it += CTHREADS) {
+    const int v = it % a.dv, half = it / a.dv;
+    float acc[HALF];
 #pragma unroll
-    for (int bi = 0; bi < CB; ++bi) acc[bi] = 0.f;
-    for (int c = lane; c < a.dkv; c += 64) {
-      float wv = load_elem<WT>(a.w, (wrow0 + v) * a.dkv + c);
+    for (int j = 0; j < HALF; ++j) acc[j] = 0.f;
+    const int64_t wbase = (wrow0 + v) * dkv;
+    for (int c = 0; c < dkv; c += 8) {
+      float w[8];
+      load8<WT>(a.w, wbase + c, w);
 #pragma unroll
-      for (int bi = 0; bi < CB; ++bi) acc[bi] += wv * olat[(bi < nb ? bi : 0) * a.dkv + c];
+      for (int j = 0; j < HALF; ++j) {
+        const int bi = half * HALF + j;
+        const f32x4_t* o = reinterpret_cast<const f32x4_t*>(&olat[(bi < nb ? bi : 0) * dkv + c]);
+        const f32x4_t o0 = o[0], o1 = o[1];
+        acc[j] += w[0] * o0[0] + w[1] * o0[1] + w[2] * o0[2] + w[3] * o0[3] +
+                  w[4] * o1[0] + w[5] * o1[1] + w[6] * o1[2] + w[7] * o1[3];
+      }
     }
 #pragma unroll
-    for (int bi = 0; bi < CB; ++bi) {
-      float r = wave_sum(acc[bi]);
-      if (lane == 0 && bi < nb) store_elem<OT>(a.out, ((int64_t)(b0 + bi) * a.H + h) * a.dv + v, r);
+    for (int j = 0; j < HALF; ++j) {
+      const int bi = half * HALF + j;
+      if (bi < nb) store_elem<OT>(a.out, ((int64_t)(b0 + bi) * a.H + h) * a.dv + v, acc[j]);
     }
   }
   if (a.lse != nullptr && tid < nb) a.lse[(int64_t)(b0 + tid) * a.H + h] = lse_s[tid];

@@ -31,8 +31,10 @@ constexpr int QT = QW * NW;       // query rows per workgroup
 constexpr int KT = 64;            // keys per tile
 constexpr int DN = 128, DR = 64, DQK = 192, DV = 128;
 constexpr int KP = DQK + 8;       // K tile pitch (fp16)
-constexpr int VP = KT + 8;        // V^T tile pitch (fp16)
+constexpr int VP = KT + 12;       // V^T tile pitch (fp16): 8-byte aligned rows, measured
+                                  // free of bank conflicts for the 8-byte reads below
 constexpr int NTHREADS = NW * 64;
+constexpr float RESCALE_TAU = 8.f;   // log2 units
 
 template <mla_dtype OT>
 __global__ void __launch_bounds__(NTHREADS)
@@ -144,7 +146,9 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
     for (int u = 0; u < 2; ++u) {
       int q = tid + NTHREADS * u;
       int row = q >> 3, c = q & 7;
-      *reinterpret_cast<u32x4_t*>(&Vs[buf][row * VP + c * 8]) = pre[3 + u];
+      u32x2_t* dst = reinterpret_cast<u32x2_t*>(&Vs[buf][row * VP + c * 8]);
+      dst[0] = u32x2_t{pre[3 + u][0], pre[3 + u][1]};
+      dst[1] = u32x2_t{pre[3 + u][2], pre[3 + u][3]};
     }
   };
 
@@ -195,9 +199,22 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
           mx = fmaxf(mx, x);
         }
       mx = half_pair_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+      // The reference max only moves when the tile exceeds it by more than
+      // RESCALE_TAU (log2 units); P then stays below 2^RESCALE_TAU and the O^T
+      // rescale is skipped on almost every tile.  A row that has seen no
+      // visible key keeps m_run = -inf and uses 0 as its reference.
+      const bool move = mx > m_run + RESCALE_TAU;
+      if (__ballot(move) != 0ull) {
+        const float alpha = move ? fast_exp2(m_run - mx) : 1.f;   // 0 when m_run was -inf
+        const float m_new = move ? mx : m_run;
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int v = 0; v < DV / 32; ++v)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[v][e] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -207,14 +224,7 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
           sacc[kt][e] = pv;
           rs += pv;
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__ballot(alpha != 1.f) != 0ull) {
-#pragma unroll
-        for (int v = 0; v < DV / 32; ++v)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[v][e] *= alpha;
-      }
+      l_run += rs;
       // O^T += V^T P^T
 #pragma unroll
       for (int ps = 0; ps < KT / 16; ++ps) {

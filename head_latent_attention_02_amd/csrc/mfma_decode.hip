@@ -69,77 +69,111 @@ absorb_bf16_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV partial attention.  One workgroup per (chunk, sequence), 8 waves;
-// wave w owns heads 16w .. 16w+15 (heads beyond H idle).  Per 32-token tile:
-//   S^T[t][h] = C[t][:576] . q~[h]      (16x16x32 MFMAs, q~ held in registers)
-//   online softmax per head (each lane owns one head of its 16)
-//   O^T[d][h] += C^T[d][t] P^T[t][h]    (16x16x32 MFMAs, P from registers)
-// The tile is staged twice in LDS: row-major C for the first product and
-// transposed C^T (built by a 4x8 register transpose on the way in) for the
-// second, both double-buffered with a register prefetch of the next tile.
-constexpr int TT = 32;               // tokens per tile
-constexpr int CP = DLAT + 8;         // C tile pitch (bf16)
-constexpr int CTP = TT + 8;          // C^T tile pitch (bf16)
+// Split-KV partial attention.
+//
+// One workgroup per (chunk, sequence); 8 waves, wave w owns heads 16w ..
+// 16w+15 (heads past H idle).  The chunk's cache rows stream through a ring of
+// 4 LDS tile buffers of 32 tokens x 576 latent columns (direct buffer->LDS
+// loads by 4 loader waves, 3 tiles in flight).  Per tile each wave computes
+//   S^T[t][h] = C[t][:576] . q~[h]          (16x16x32 bf16 MFMA, q~ in VGPRs)
+//   online softmax in the log2 domain       (each lane owns one head)
+//   O^T[d][h] += C^T[d][t] P^T[t][h]        (16x16x32 bf16 MFMA, P in VGPRs)
+// so P never leaves registers: the first product's result layout (token rows
+// 4q4 + r of each 16-token half) is the k-slot layout the second product needs
+// once C^T is read with the LDS transpose read (ds_read_b64_tr_b16).
+// The reference max of a head only moves when a tile exceeds it by more than
+// 8 (log2 units), which skips the accumulator rescale on most tiles; the
+// result is exact either way because l and O share the same reference.
+// Inside a tile row the 16-byte chunks are XOR-swizzled by row&7, measured
+// free of LDS bank conflicts for both the row reads and the transposed reads.
+constexpr int TT = 32;                   // tokens per tile
+constexpr int NBUF = 4;                  // tile ring depth
+constexpr int CHUNKS = DLAT / 8;         // 16-byte chunks per row (72)
 constexpr int NTHREADS = 512;
+constexpr int LOADERS = 4;               // waves that issue the tile loads
+constexpr int LOADS = TT * CHUNKS / (LOADERS * 64);   // loads per loader wave per tile (9)
+constexpr float RESCALE_TAU = 8.f;       // log2 units
+
+typedef short lds_v4s __attribute__((__vector_size__(4 * sizeof(short))));
+#define LDS_AS __attribute__((address_space(3)))
+
+// 16-byte chunk swizzle of a tile row (measured free of LDS bank conflicts for
+// both the row reads and the transposed reads below)
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer load of `size` bytes per lane straight into LDS at lds + 16 * lane
+// (LLVM intrinsic llvm.amdgcn.raw.buffer.load.lds).  Offsets at or past the
+// resource's byte range read as zero.
+extern "C" __device__ void mla_raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void* lds,
+                                                   int size, int voffset, int soffset, int offset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer resource for `bytes` bytes at `base` (gfx9 data-format word).
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r = {(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)bytes, 0x00020000};
+  return r;
+}
+
+// s_waitcnt vmcnt(n), leaving the other counters unconstrained
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ bf16x8_t cat_bf16(lds_v4s lo, lds_v4s hi) {
+  u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
+  u32x4_t r = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8_t, r);
+}
 
 __global__ void __launch_bounds__(NTHREADS)
 mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __restrict__ lse_part,
                     float* __restrict__ o_part) {
-  __shared__ __attribute__((aligned(16))) uint16_t Cs[2][TT * CP];
-  __shared__ __attribute__((aligned(16))) uint16_t Cts[2][DC * CTP];
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[NBUF][TT * DLAT];
 
   const int k = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int h = wave * 16 + l16;
-  const bool wave_active = wave * 16 < a.H;
+  const bool wave_active = wave * 16 < a.H;     // H is a multiple of 16
 
   const int L = min(max(a.cache_len[b], 0), a.max_len);
   const int csz = (L + a.n_splits - 1) / a.n_splits;
   const int t0 = min(L, k * csz), t1 = min(L, (k + 1) * csz);
   const int ntile = (t1 - t0 + TT - 1) / TT;
 
-  // q~ operand in registers: lane holds q~[h][32ks + 8q4 .. +8]
+  // q~ as the B operand: lane holds q~[h][32ks + 8q4 .. +8]
   bf16x8_t qf[DLAT / 32];
-  if (wave_active) {
-    const uint16_t* qrow = qt + ((int64_t)b * a.H + h) * DLAT;
+  {
+    const uint16_t* qrow = qt + ((int64_t)b * a.H + (wave_active ? h : 0)) * DLAT;
 #pragma unroll
     for (int ks = 0; ks < DLAT / 32; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 32 + q4 * 8);
   }
 
+  // Tile loads: loader wave w, instruction i fills tile slots (w*LOADS+i)*64 +
+  // lane, i.e. row slot/72 and swizzled chunk slot%72.  The buffer range ends
+  // at the chunk's last row, so rows past it read as zero.
   const uint16_t* cbase = static_cast<const uint16_t*>(a.cache) + (int64_t)b * a.cache_stride;
-  // load roles: c-part 4 rows x 8 columns per thread; rope part one 16 B chunk
-  const int tq = tid >> 6, db = tid & 63;
-  const int rtok = (tid & 255) >> 3, rc = tid & 7;
-  u32x4_t pre[5];
-  auto gload = [&](int tt) {
+  const i32x4_t rsrc = make_rsrc(cbase, (uint32_t)t1 * (DLAT * 2));
+  int voff[LOADS];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int tok = tt + 4 * tq + r;
-      pre[r] = (tok < t1) ? *reinterpret_cast<const u32x4_t*>(cbase + (int64_t)tok * DLAT + 8 * db)
-                          : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    int tok = tt + rtok;
-    pre[4] = (tid < 256 && tok < t1)
-                 ? *reinterpret_cast<const u32x4_t*>(cbase + (int64_t)tok * DLAT + DC + 8 * rc)
-                 : u32x4_t{0u, 0u, 0u, 0u};
-  };
-  auto lstore = [&](int buf) {
+  for (int i = 0; i < LOADS; ++i) {
+    const int slot = ((wave & (LOADERS - 1)) * LOADS + i) * 64 + lane;
+    const int r = slot / CHUNKS, pc = slot - r * CHUNKS;
+    voff[i] = r * (DLAT * 2) + swz(r, pc) * 16;
+  }
+  auto issue_tile = [&](int tile) {
+    if (wave >= LOADERS) return;
+    const int tbyte = (t0 + tile * TT) * (DLAT * 2);
+    uint16_t* dst = &Cs[tile & (NBUF - 1)][0];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<u32x4_t*>(&Cs[buf][(4 * tq + r) * CP + 8 * db]) = pre[r];
-    if (tid < 256) *reinterpret_cast<u32x4_t*>(&Cs[buf][rtok * CP + DC + 8 * rc]) = pre[4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) ? 16 : 0;
-      uint32_t x0 = (pre[0][e >> 1] >> sh) & 0xffffu, x1 = (pre[1][e >> 1] >> sh) & 0xffffu;
-      uint32_t x2 = (pre[2][e >> 1] >> sh) & 0xffffu, x3 = (pre[3][e >> 1] >> sh) & 0xffffu;
-      u32x2_t v2;
-      v2[0] = x0 | (x1 << 16);
-      v2[1] = x2 | (x3 << 16);
-      *reinterpret_cast<u32x2_t*>(&Cts[buf][(8 * db + e) * CTP + 4 * tq]) = v2;
-    }
+    for (int i = 0; i < LOADS; ++i)
+      mla_raw_buffer_load_lds(rsrc, (LDS_AS void*)(dst + (wave * LOADS + i) * 512), 16, voff[i] + tbyte, 0, 0, 0);
   };
 
   const float c_log2 = a.scale * MLA_LOG2E;
@@ -148,77 +182,108 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
 #pragma unroll
   for (int d = 0; d < DC / 16; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (ntile > 0) {
-    gload(t0);
-    lstore(0);
-  }
-  __syncthreads();
+  for (int i = 0; i < NBUF - 1 && i < ntile; ++i) issue_tile(i);
 
   for (int t = 0; t < ntile; ++t) {
-    const int tt = t0 + t * TT;
-    const int buf = t & 1;
-    if (t + 1 < ntile) gload(tt + TT);
+    const int ahead = min(NBUF - 2, ntile - 1 - t);       // tiles issued after tile t
+    if (ahead >= 2) wait_vmcnt<2 * LOADS>();
+    else if (ahead == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    // own loads of tile t have landed; the barrier makes that true for all
+    // waves and also fences the reuse of the buffer read in iteration t-1
+    __builtin_amdgcn_s_barrier();
+    if (t + NBUF - 1 < ntile) issue_tile(t + NBUF - 1);
+    if (!wave_active) continue;
 
-    if (wave_active) {
-      f32x4_t sacc[2];
+    const uint16_t* C = &Cs[t & (NBUF - 1)][0];
+    const int tt = t0 + t * TT;
+
+    // S^T = C q~^T: sacc[st][r] is head h, token 16st + 4q4 + r.  The row read
+    // for k-step ks is chunk (4ks + q4) ^ sw(row); since q4 < 4 this is
+    // 4*(ks ^ sw/4) + (q4 ^ sw%4), so even and odd k-steps each walk a fixed
+    // base in steps of 8 chunks.
+    f32x4_t sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const uint16_t* pe[2];
+    const uint16_t* po[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int row = st * 16 + l16;
+      const int rsw = row & 7;
+      const uint16_t* rp = C + row * DLAT + 8 * (q4 ^ (rsw & 3));
+      pe[st] = rp + 32 * (rsw >> 2);          // chunk group of even k-steps
+      po[st] = rp + 32 * (1 - (rsw >> 2));    // and of odd ones
+    }
+    // the two 16-token halves are independent accumulation chains; interleave them
+#pragma unroll
+    for (int ks = 0; ks < DLAT / 32; ++ks)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        sacc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DLAT / 32; ++ks) {
-          bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&Cs[buf][(st * 16 + l16) * CP + ks * 32 + q4 * 8]);
-          sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[ks], sacc[st], 0, 0, 0);
-        }
+        const uint16_t* ap = ((ks & 1) ? po[st] : pe[st]) + 64 * (ks >> 1);
+        bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(ap);
+        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[ks], sacc[st], 0, 0, 0);
       }
-      // sacc[st][r]: token tt + 16st + 4q4 + r, head h
-      const bool tail = (tt + TT > t1);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = sacc[st][r] * c_log2;
-          if (tail && (tt + 16 * st + 4 * q4 + r >= t1)) x = -INFINITY;
-          sacc[st][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
-      bf16x8_t pf;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float pv = fast_exp2(sacc[st][r] - m_use);
-          rs += pv;
-          pf[4 * st + r] = __builtin_bit_cast(__bf16, float_to_bf16_bits(pv));
-        }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__ballot(alpha != 1.f) != 0ull) {
-#pragma unroll
-        for (int d = 0; d < DC / 16; ++d) oacc[d] *= alpha;
-      }
-#pragma unroll
-      for (int d = 0; d < DC / 16; ++d) {
-        const uint16_t* crow = &Cts[buf][(d * 16 + l16) * CTP + 4 * q4];
-        u32x2_t lo = *reinterpret_cast<const u32x2_t*>(crow);
-        u32x2_t hi = *reinterpret_cast<const u32x2_t*>(crow + 16);
-        u32x4_t raw = {lo[0], lo[1], hi[0], hi[1]};
-        bf16x8_t af = __builtin_bit_cast(bf16x8_t, raw);
-        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, oacc[d], 0, 0, 0);
-      }
-    }
 
-    if (t + 1 < ntile) lstore(buf ^ 1);
-    __syncthreads();
+    // online softmax (log2 domain) with a lazily moved reference max
+    const bool tail = (tt + TT > t1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = sacc[st][r] * c_log2;
+        if (tail && (tt + 16 * st + 4 * q4 + r >= t1)) x = -INFINITY;
+        sacc[st][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool move = mx > m_run + RESCALE_TAU;         // always true on the first tile
+    if (__ballot(move) != 0ull) {
+      const float alpha = move ? fast_exp2(m_run - mx) : 1.f;   // 0 on the first tile
+      const float m_new = move ? mx : m_run;
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < DC / 16; ++d) oacc[d] *= alpha;
+    }
+    bf16x8_t pf;
+    float rs = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float pv = fast_exp2(sacc[st][r] - m_run);
+        rs += pv;
+        pf[4 * st + r] = __builtin_bit_cast(__bf16, float_to_bf16_bits(pv));
+      }
+    l_run += rs;
+
+    // O^T += C^T P^T.  Lane (row d = 16dt + l16, k-slots 8q4 + u) holds
+    // C[token][d] for tokens 4q4 + u (u < 4) and 16 + 4q4 + u - 4 (u >= 4):
+    // two transposed reads of 4 rows x 16 columns per 16-lane group.
+    // Element e0 = 16dt + 4(l16&3) sits in chunk 2dt + x, x = (l16&3)>>1, which
+    // the row swizzle s maps to 2(dt ^ s/2) + (x ^ s%2): within each group of 4
+    // d-tiles the order is permuted, so 4 bases per row walk in steps of 8 chunks.
+    const int ra = 4 * q4 + (l16 >> 2), rb = ra + 16;
+    const int sa = ra & 7, sb = rb & 7;
+    const int x = (l16 & 3) >> 1, w = 4 * (l16 & 1);
+    const uint16_t* pa[4];
+    const uint16_t* pb[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      pa[m] = C + ra * DLAT + 8 * (2 * (m ^ (sa >> 1)) + (x ^ (sa & 1))) + w;
+      pb[m] = C + rb * DLAT + 8 * (2 * (m ^ (sb >> 1)) + (x ^ (sb & 1))) + w;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DC / 16; ++dt) {
+      const int m = dt & 3, j = dt >> 2;
+      lds_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(pa[m] + 64 * j));
+      lds_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(pb[m] + 64 * j));
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat_bf16(lo, hi), pf, oacc[dt], 0, 0, 0);
+    }
   }
 
-  if (!wave_active || h >= a.H) return;
+  if (!wave_active) return;
   float l = l_run + __shfl_xor(l_run, 16, 64);
   l += __shfl_xor(l, 32, 64);
   const float inv = (l > 0.f) ? 1.f / l : 0.f;

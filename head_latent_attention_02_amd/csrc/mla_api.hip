@@ -169,8 +169,10 @@ bool decode_shape_ok(const mla_decode_desc* d) {
 }
 
 bool decode_mfma_eligible(const mla_decode_desc* d) {
+  // tile loads use 32-bit byte offsets within one sequence's rows
   return d->in_dtype == MLA_BF16 && d->d_kv == 512 && d->d_nope == 128 && d->d_rope == 64 &&
-         d->d_v == 128 && d->n_heads % 16 == 0 && d->n_heads <= 128 && d->cache_batch_stride % 8 == 0;
+         d->d_v == 128 && d->n_heads % 16 == 0 && d->n_heads <= 128 && d->cache_batch_stride % 8 == 0 &&
+         (int64_t)d->max_cache_len * (d->d_kv + d->d_rope) * 2 < ((int64_t)1 << 31);
 }
 
 bool decode_simt_supported(const mla_decode_desc* d) { return d->d_kv <= 1024 && d->d_rope <= 256; }
@@ -178,7 +180,8 @@ bool decode_simt_supported(const mla_decode_desc* d) { return d->d_kv <= 1024 &&
 mla_status make_decode_plan(const mla_decode_desc* d, DecodePlan* plan) {
   if (!decode_shape_ok(d)) return MLA_ERR_INVALID_ARGUMENT;
   if (d->n_splits > 64) return MLA_ERR_UNSUPPORTED;
-  if (d->d_kv > 1024) return MLA_ERR_UNSUPPORTED;   // combine keeps 8 merged rows in LDS
+  // the combine keeps 8 merged rows in LDS and reads rows 8 elements at a time
+  if (d->d_kv > 1024 || d->d_kv % 8 != 0) return MLA_ERR_UNSUPPORTED;
   bool mfma;
   if (d->algo == MLA_ALGO_MFMA) {
     if (!decode_mfma_eligible(d)) return MLA_ERR_UNSUPPORTED;
@@ -322,8 +325,9 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc, const void* q_nope, 
   if (desc->max_cache_len > 0 && kv_cache == nullptr) return MLA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (workspace == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(w_kv_b) || !aligned16(workspace)) return MLA_ERR_INVALID_ARGUMENT;
   if (p.mfma) {
-    const void* ptrs[] = {q_nope, q_pe, kv_cache, w_kv_b, out, workspace};
+    const void* ptrs[] = {q_nope, q_pe, kv_cache, out};
     for (const void* q : ptrs)
       if (q != nullptr && !aligned16(q)) return MLA_ERR_INVALID_ARGUMENT;
   }

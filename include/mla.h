@@ -177,7 +177,9 @@ size_t mla_decode_absorbed_workspace_size(const mla_decode_desc* desc);
  *   w_kv_b   [H*(d_nope+d_v), d_kv]
  *   out      [B, H, d_v] (out_dtype)    lse [B, H] fp32 or NULL
  * cache_len values outside [0, max_cache_len] are clamped to that range on
- * the device.  A sequence with cache_len 0 gets out = 0 and lse = -inf. */
+ * the device.  A sequence with cache_len 0 gets out = 0 and lse = -inf.
+ * Limits: d_kv a multiple of 8 and at most 1024, n_splits at most 64
+ * (MLA_ERR_UNSUPPORTED otherwise); w_kv_b and workspace 16-byte aligned. */
 mla_status mla_decode_absorbed(const mla_decode_desc* desc,
                                const void* q_nope, const void* q_pe,
                                const void* kv_cache, const int32_t* cache_len,

@@ -61,15 +61,20 @@ def _compare(got, ref, bf16, what):
         assert max_abs <= FP32_MAX_ABS, f"{what}: max|d| {max_abs}"
 
 
-def _compare_lse(got, ref, bf16, what):
+def _compare_lse(got, ref, bf16, what, magnitude_scaled=False):
+    """LSE check.  With magnitude_scaled the bar grows by 2^-9 |LSE|: logits
+    formed from bf16 / fp16 operands carry an absolute error proportional to
+    their size, which only matters for the deliberately huge logits of the
+    jump tests."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     fin = np.isfinite(ref)
     assert np.array_equal(np.isneginf(got), ~fin), f"{what}: -inf pattern differs"
     if fin.any():
-        err = float(np.abs(got[fin] - ref[fin]).max())
-        _say(f"{what}: lse max|d|={err:.3e}")
-        assert err <= (BF16_MAX_ABS if bf16 else FP32_MAX_ABS), f"{what}: lse max|d| {err}"
+        err = np.abs(got[fin] - ref[fin])
+        bar = (BF16_MAX_ABS if bf16 else FP32_MAX_ABS) + (2.0 ** -9 * np.abs(ref[fin]) if magnitude_scaled else 0)
+        _say(f"{what}: lse max|d|={float(err.max()):.3e} (max |lse| {float(np.abs(ref[fin]).max()):.1f})")
+        assert np.all(err <= bar), f"{what}: lse max|d| {float(err.max())}"
 
 
 def _run_explicit(mla, cfg, x, *, algo=0, out_dtype=torch.float32, poison=True):
@@ -303,3 +308,51 @@ def test_decode_repeatable(mla):
     o1, l1, _, _ = _run_decode(mla, cfg, x, algo=2)
     o2, l2, _, _ = _run_decode(mla, cfg, x, algo=2)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2, equal_nan=True)
+
+
+# ------------------------------------------------ large logit jumps ----
+def _unit_rotated(pos, d_rope=64, base=10000.0):
+    """R(e_0, -pos): the band that the kernel's rotation at `pos` maps to e_0."""
+    v = np.zeros((len(pos), d_rope))
+    ang = -np.asarray(pos, dtype=np.float64)        # theta_0 = 1
+    v[:, 0] = np.cos(ang)
+    v[:, d_rope // 2] = np.sin(ang)
+    return v
+
+
+@pytest.mark.parametrize("algo", [2, 1], ids=["mfma", "simt"])
+def test_decode_logit_jumps(mla, algo):
+    """Scores rise by ~5.5 nats (8 in log2 units) from one 32-token tile to the
+    next and fall again, so the online softmax must move its reference max
+    mid-chunk.  q_nope = 0 makes the score lambda_t * sigma exactly through the
+    RoPE band: q_pe = R(e_0, -(L-1)), cache band = lambda_t e_0."""
+    cfg = I.small_decode("jumps", batch=2, cache_len=400, n_heads=32, n_splits=2, seed=301)
+    x = I.make_decode_inputs(cfg, cache_len=np.array([400, 333], dtype=np.int32))
+    x["q_nope"][:] = 0
+    for b, L in enumerate(x["cache_len"]):
+        x["q_pe"][b] = I.bf16_bits_to_f32(I.round_to_bf16_bits(_unit_rotated([L - 1]).repeat(cfg.n_heads, 0)))
+    t = np.arange(cfg.cache_len)
+    lam = 76.0 * np.minimum(t // 32, 6) - 60.0 * np.maximum(t // 32 - 8, 0)
+    band = np.zeros((cfg.cache_len, 64))
+    band[:, 0] = lam
+    x["cache_bits"][:, :, 512:] = I.round_to_bf16_bits(band)[None]
+    o, l, _, _ = _run_decode(mla, cfg, x, algo=algo)
+    r = _oracle_decode(cfg, x)
+    _compare(o, r["out"], True, f"decode jumps out ({algo})")
+    _compare_lse(l, r["lse"], True, f"decode jumps ({algo})", magnitude_scaled=True)
+
+
+def test_explicit_logit_jumps(mla):
+    cfg = I.small_explicit("xjumps", s_q=300, s_kv=300, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                           dtype="bf16", seed=302)
+    x = I.make_explicit_inputs(cfg)
+    x["q_nope"][:] = 0
+    S = cfg.s_q
+    qb = I.bf16_bits_to_f32(I.round_to_bf16_bits(_unit_rotated(np.arange(S))))
+    x["q_pe"][0] = np.repeat(qb[:, None, :], cfg.n_heads, axis=1)
+    lam = 76.0 * np.minimum(np.arange(S) // 64, 4) - 50.0 * np.maximum(np.arange(S) // 64 - 4, 0)
+    x["k_pe"][0] = I.bf16_bits_to_f32(I.round_to_bf16_bits(_unit_rotated(np.arange(S)) * lam[:, None]))
+    o, l, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA)
+    ro, rl = _oracle_explicit(cfg, x)
+    _compare(o, ro, True, "explicit jumps out")
+    _compare_lse(l, rl, True, "explicit jumps", magnitude_scaled=True)
