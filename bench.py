@@ -15,10 +15,19 @@ HIP events the library records around each of its launches on the stream the
 kernels run on (mla_timing_*), inside the timed region.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--copy-calibration]
+
+HBM traffic (`roofline.traffic`) comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
+passes over this same command, each divided by the factor the same counter
+reads for a plain device copy of known size (`--copy-calibration` runs that
+copy before the warm-up).  The figures sit in HBM_COUNTERS below together with
+a digest of the kernel's sources; once those sources change, traffic is
+reported as null until the counters are taken again.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +41,47 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 / fp16
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "MLA attn fwd TFLOP/s (+% MFMA peak) at V3 dims; absorbed decode tok/s (+% HBM)"
+COPY_CALIBRATION_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
+
+CSRC = os.path.join(ROOT, "head_latent_attention_02_amd", "csrc")
+# Kernel -> the sources its code comes from.
+KERNEL_SOURCES = {
+    "mfma_attention": ["mfma_attn.hip", "common.h", "kernels.h"],
+    "mfma_up_projection": ["mfma_upproj.hip", "common.h", "kernels.h"],
+    "mfma_split_kv": ["mfma_decode.hip", "common.h", "kernels.h"],
+    "lse_combine": ["combine.hip", "common.h", "kernels.h"],
+}
+# rocprofv3 counter readings per launch at the default workloads, KiB as the
+# counter reports them, and the copy-calibration factors (counter KiB * 1024
+# per byte actually moved by the calibration copy).  "digest" is
+# source_digest() of the kernel's sources when the counters were taken.
+HBM_COUNTERS: dict = {
+    # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
+    "mfma_attention": {"digest": "140b9edea956bc9d", "fetch_kib": 356707.8, "write_kib": 264578.6,
+                       "fetch_factor": 0.50003, "write_factor": 1.0},
+    "mfma_up_projection": {"digest": "804c127f2b8434a7", "fetch_kib": 207065.8, "write_kib": 339206.0,
+                           "fetch_factor": 0.50003, "write_factor": 1.0},
+    "mfma_split_kv": {"digest": "121416f8a70d5077", "fetch_kib": 1217212.8, "write_kib": 271347.2,
+                      "fetch_factor": 0.50003, "write_factor": 1.0},
+    "lse_combine": {"digest": "5752885ed86c67f4", "fetch_kib": 149567.9, "write_kib": 4356.3,
+                    "fetch_factor": 0.50003, "write_factor": 1.0},
+}
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def hbm_traffic(kernel: str):
+    """HBM bytes per launch from the recorded counters, or None if stale."""
+    c = HBM_COUNTERS.get(kernel)
+    if c is None or kernel not in KERNEL_SOURCES or source_digest(kernel) != c["digest"]:
+        return None
+    return c["fetch_kib"] * 1024 / c["fetch_factor"] + c["write_kib"] * 1024 / c["write_factor"]
 
 
 def log(msg):
@@ -48,6 +98,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle baseline sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run a plain 1 GiB device copy (3 times) before the warm-up, as the "
+                        "reference reading for HBM byte counters")
     return p.parse_args()
 
 
@@ -160,6 +213,16 @@ def main():
         if record:
             ev[2].record()
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: 3 x {COPY_CALIBRATION_BYTES} bytes")
+        del src, dst
+
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step(False)
@@ -208,6 +271,8 @@ def main():
             unit, work = per_kernel_work[name]
             ent["achieved"] = work / (avg * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
             ent["unit"] = unit
+        if name in KERNEL_SOURCES:
+            ent["traffic"] = hbm_traffic(name)
         kernels[name] = ent
 
     def roof(name, bound, unit, work, peak):
@@ -215,9 +280,10 @@ def main():
             return None
         avg = kt[name][0] / max(kt[name][1], 1)
         ach = work / (avg * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
-        return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak, "traffic": None,
-                "kernel": name, "avg_ms": avg,
-                "work_per_launch": work}
+        return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+                "traffic": hbm_traffic(name), "traffic_unit": "bytes per launch",
+                "kernel": name, "avg_ms": avg, "work_per_launch": work,
+                "source_digest": source_digest(name)}
 
     roofline = roof("mfma_attention", "mfma", "TFLOP/s", fl["attention"], PEAK_MFMA_TFLOPS)
     roofline_decode = roof("mfma_split_kv", "hbm", "GB/s", dbytes["cache"], PEAK_HBM_GBS)
