@@ -84,3 +84,29 @@ __device__ __forceinline__ float half_pair_sum(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+// ---- direct global->LDS copies and wait counters (gfx950) ------------------
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// Buffer load of `size` bytes per lane straight into LDS at lds + size * lane
+// (LLVM intrinsic llvm.amdgcn.raw.buffer.load.lds).  The byte address is
+// voffset + soffset + offset from the resource base; addresses at or past the
+// resource's byte range read as zero.
+extern "C" __device__ void mla_raw_buffer_load_lds(i32x4_t rsrc, LDS_AS void* lds, int size, int voffset,
+                                                   int soffset, int offset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer resource for `bytes` bytes at `base` (gfx9 data-format word).
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r = {(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)bytes, 0x00020000};
+  return r;
+}
+
+// s_waitcnt vmcnt(n), leaving the other counters unconstrained
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}

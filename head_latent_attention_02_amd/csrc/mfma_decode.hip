@@ -95,34 +95,10 @@ constexpr int LOADS = TT * CHUNKS / (LOADERS * 64);   // loads per loader wave p
 constexpr float RESCALE_TAU = 8.f;       // log2 units
 
 typedef short lds_v4s __attribute__((__vector_size__(4 * sizeof(short))));
-#define LDS_AS __attribute__((address_space(3)))
 
 // 16-byte chunk swizzle of a tile row (measured free of LDS bank conflicts for
 // both the row reads and the transposed reads below)
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
-
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// Buffer load of `size` bytes per lane straight into LDS at lds + 16 * lane
-// (LLVM intrinsic llvm.amdgcn.raw.buffer.load.lds).  Offsets at or past the
-// resource's byte range read as zero.
-extern "C" __device__ void mla_raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void* lds,
-                                                   int size, int voffset, int soffset, int offset,
-                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-
-// Buffer resource for `bytes` bytes at `base` (gfx9 data-format word).
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
-  uint64_t p = reinterpret_cast<uint64_t>(base);
-  i32x4_t r = {(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)bytes, 0x00020000};
-  return r;
-}
-
-// s_waitcnt vmcnt(n), leaving the other counters unconstrained
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 __device__ __forceinline__ bf16x8_t cat_bf16(lds_v4s lo, lds_v4s hi) {
   u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);

@@ -99,6 +99,8 @@ bool explicit_shape_ok(const mla_explicit_desc* d) {
   return true;
 }
 
+constexpr int kMaxMfmaKeys = 1 << 22;    // visible keys (rounded up) on the MFMA path
+
 bool explicit_mfma_eligible(const mla_explicit_desc* d) {
   return d->in_dtype == MLA_BF16 && d->d_kv == 512 && d->d_nope == 128 && d->d_rope == 64 &&
          d->d_v == 128;
@@ -111,18 +113,7 @@ bool explicit_simt_supported(const mla_explicit_desc* d) {
 // Returns MLA_OK and fills `plan`, or the status that the call must return.
 mla_status make_explicit_plan(const mla_explicit_desc* d, ExplicitPlan* plan) {
   if (!explicit_shape_ok(d)) return MLA_ERR_INVALID_ARGUMENT;
-  bool mfma;
-  if (d->algo == MLA_ALGO_MFMA) {
-    if (!explicit_mfma_eligible(d)) return MLA_ERR_UNSUPPORTED;
-    mfma = true;
-  } else if (d->algo == MLA_ALGO_SIMT) {
-    mfma = false;
-  } else {
-    mfma = explicit_mfma_eligible(d);
-  }
-  if (!mfma && !explicit_simt_supported(d)) return MLA_ERR_UNSUPPORTED;
   ExplicitPlan p;
-  p.mfma = mfma;
   if (d->s_q == 0) {
     p.s_vis = 0;
   } else if (d->causal) {
@@ -132,6 +123,20 @@ mla_status make_explicit_plan(const mla_explicit_desc* d, ExplicitPlan* plan) {
     p.s_vis = d->s_kv;
   }
   p.s_pad = (p.s_vis + kUpTile - 1) / kUpTile * kUpTile;
+  // the MFMA attention addresses one head's K_nope / V^T rows with 32-bit
+  // byte offsets: s_pad * 256 bytes must stay below 2^31
+  const bool mfma_ok = explicit_mfma_eligible(d) && p.s_pad <= kMaxMfmaKeys;
+  bool mfma;
+  if (d->algo == MLA_ALGO_MFMA) {
+    if (!mfma_ok) return MLA_ERR_UNSUPPORTED;
+    mfma = true;
+  } else if (d->algo == MLA_ALGO_SIMT) {
+    mfma = false;
+  } else {
+    mfma = mfma_ok;
+  }
+  if (!mfma && !explicit_simt_supported(d)) return MLA_ERR_UNSUPPORTED;
+  p.mfma = mfma;
   const size_t B = d->batch, H = d->n_heads, half = d->d_rope / 2;
   size_t off = 0;
   p.off_qtab = off; off = align_up(off + sizeof(float2) * (size_t)d->s_q * half);

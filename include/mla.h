@@ -96,7 +96,9 @@ typedef struct {
   float rope_base;      /* RoPE base, > 1 (10000)                              */
   mla_dtype in_dtype;   /* dtype of q_nope, q_pe, c_kv, k_pe, w_kv_b            */
   mla_dtype out_dtype;  /* dtype of out (lse is always fp32)                   */
-  mla_algo algo;        /* kernel family                                       */
+  mla_algo algo;        /* kernel family.  MFMA needs bf16 inputs, d_kv 512,
+                           d_nope 128, d_rope 64, d_v 128, and at most 2^22
+                           visible latent rows per sequence                  */
 } mla_explicit_desc;
 
 /* Bytes of device workspace mla_fwd_explicit needs for `desc`; 0 if the
