@@ -26,13 +26,18 @@
 //
 // Tiles.  K (64 x 192, as a K_nope part and a rope part) and V^T (128 x 64)
 // tiles are copied from global memory straight into LDS (buffer loads to LDS,
-// 16 bytes per lane, 5 per wave per tile) through a ring of 3 stages, two
-// tiles ahead of the one being consumed.  In every tile row the 16-byte chunks
-// are XOR-swizzled with row & 7, so the 16-byte operand reads of a lane group
-// fall in distinct banks.
+// 16 bytes per lane, 5 per wave per tile) through a ring of 4 stages, two
+// tiles ahead of the one whose S is computed.  In every tile row the 16-byte
+// chunks are XOR-swizzled by row so that the 16-byte operand reads of 16
+// consecutive lanes fall in distinct banks.
 //
-// Only the diagonal tiles run the masked variant of the tile code; tiles past
-// a wave's last visible key are skipped.  The reference max of a row only
+// Schedule.  The waves form two groups with one wave of each on every SIMD;
+// the groups run half an iteration apart, so that on each SIMD one wave issues
+// MFMAs (the PV of the previous tile and the S of the current one) while the
+// other computes a softmax on the vector ALU.
+//
+// Only the diagonal tiles are masked; tiles past a wave's last visible key are
+// skipped.  The reference max of a row only
 // moves when a tile exceeds it by more than 8 (log2 units), which skips the
 // O^T rescale on almost every tile (P stays below 2^8, inside fp16's range).
 // The row sum is taken on the fp16 P the MFMA consumes (v_dot2 with ones).
@@ -63,12 +68,20 @@ constexpr int V_SLOTS = DV * (KT / 8);    // 1024
 constexpr int R0 = N_SLOTS * 8, V0 = (N_SLOTS + R_SLOTS) * 8;    // fp16 offsets of the parts
 constexpr int LPW = (N_SLOTS + R_SLOTS + V_SLOTS) / (64 * NW);  // copies per wave per tile (5)
 constexpr int STAGE = (N_SLOTS + R_SLOTS + V_SLOTS) * 8;        // fp16 elements per ring stage
-constexpr int NSTAGE = 3;
+constexpr int NSTAGE = 4;
 constexpr float RESCALE_TAU = 8.f;   // log2 units
+constexpr int MPF = 4;               // MFMA operand fragments read ahead
 static_assert(LPW * 64 * NW == N_SLOTS + R_SLOTS + V_SLOTS, "tile chunks must split evenly over the waves");
 static_assert(N_SLOTS % 64 == 0 && R_SLOTS % 64 == 0, "a copy must not straddle two parts");
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+// Chunk swizzles (stored chunk = logical chunk ^ swizzle(row)), measured free of
+// LDS bank conflicts for the 16-byte reads below, where 16 consecutive lanes
+// read 16 consecutive rows: 256-byte rows need 16 distinct chunks over those
+// rows, 128-byte rows (two per bank sweep) 8 distinct chunks per row parity.
+__device__ __forceinline__ int sw_n(int row) { return row & 15; }
+__device__ __forceinline__ int sw_8(int row) { return (row >> 1) & 7; }
 
 // key offset (inside its 32-key block) carried by LDS row rho of that block
 __device__ __forceinline__ int key_of_row(int rho) {
@@ -95,7 +108,6 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hb = lane >> 5;
-  const int sw = l32 & 7;                  // row swizzle of every row this lane reads
   const int iw0 = i0 + wave * QW;
   const int i = iw0 + l32;                 // this lane's query row
   const bool row_ok = i < a.Sq;
@@ -160,13 +172,13 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
   for (int u = 0; u < LPW; ++u) {
     const int s = (wave * LPW + u) * 64 + lane;
     if (s < N_SLOTS) {
-      const int rho = s >> 4, c = (s & 15) ^ (rho & 7);
+      const int rho = s >> 4, c = (s & 15) ^ sw_n(rho);
       goff[u] = (32 * (rho >> 5) + key_of_row(rho & 31)) * (DN * 2) + 16 * c;
     } else if (s < N_SLOTS + R_SLOTS) {
-      const int sr = s - N_SLOTS, rho = sr >> 3, c = (sr & 7) ^ (rho & 7);
+      const int sr = s - N_SLOTS, rho = sr >> 3, c = (sr & 7) ^ sw_8(rho);
       goff[u] = (32 * (rho >> 5) + key_of_row(rho & 31)) * (DR * 2) + 16 * c;
     } else {
-      const int sv = s - N_SLOTS - R_SLOTS, d = sv >> 3, c = (sv & 7) ^ (d & 7);
+      const int sv = s - N_SLOTS - R_SLOTS, d = sv >> 3, c = (sv & 7) ^ sw_8(d);
       goff[u] = d * (a.s_pad * 2) + 16 * c;
     }
   }
@@ -190,22 +202,32 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
     ++issue_tile;
   };
 
-  // ---- per-lane LDS read offsets (fp16 elements within a stage) --------------
-  // A lane reads rows kt*32 + l32 (K parts) or v*32 + l32 (V^T), all with row
-  // swizzle sw, at logical chunk 2q + hb of an 8-chunk group q:
-  //   K_nope, k-step ks < 8:  row pitch 16 chunks, group ks/4, q = ks%4
-  //   rope,   k-step ks >= 8: row pitch 8 chunks, q = ks-8
-  //   V^T,    key step ps:    row pitch 8 chunks, q = ps (keys 16ps + 8hb .. +7)
-  // The pointers address the stage of the tile being consumed and advance with it.
-  LDS_AS const uint16_t* np[4];
-  LDS_AS const uint16_t* rp[4];             // V^T: rp[q] + (V0 - R0), since l32*KT = l32*DR
+  // ---- per-lane LDS read pointers ----------------------------------------------
+  // A lane reads rows kt*32 + l32 (K parts) or v*32 + l32 (V^T) at logical
+  // chunk 2q + hb:
+  //   K_nope, k-step ks < 8:  16-chunk rows, q = ks      (kp[ks])
+  //   rope,   k-step ks >= 8: 8-chunk rows,  q = ks - 8  (rp[q])
+  //   V^T,    key step ps:    8-chunk rows,  q = ps      (vp[q])
+  // The row swizzles depend only on l32's low bits, shared by all those rows.
+  // kp/rp address the stage of the next tile whose S is computed, vp the stage
+  // of the next tile whose PV is computed; each advances with its tile.
+  LDS_AS const uint16_t* kp[DN / 16];
+  LDS_AS const uint16_t* rp[4];
+  LDS_AS const uint16_t* vp[4];
+#pragma unroll
+  for (int q = 0; q < DN / 16; ++q) kp[q] = (LDS_AS const uint16_t*)Ls + l32 * DN + 8 * ((2 * q + hb) ^ sw_n(l32));
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int x = 8 * ((2 * q + hb) ^ sw);
-    np[q] = (LDS_AS const uint16_t*)Ls + l32 * DN + x;
+    const int x = 8 * ((2 * q + hb) ^ sw_8(l32));
     rp[q] = (LDS_AS const uint16_t*)Ls + R0 + l32 * DR + x;
+    vp[q] = (LDS_AS const uint16_t*)Ls + V0 + l32 * KT + x;
   }
-  static_assert(KT == DR, "V^T and rope rows share the per-lane offsets");
+  int kstage = 0, vstage = 0;
+  auto ring_step = [](int& st) {
+    const int step = (st == NSTAGE - 1) ? -(NSTAGE - 1) * STAGE : STAGE;
+    st = (st == NSTAGE - 1) ? 0 : st + 1;
+    return step;
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t oacc[DV / 32];
@@ -213,53 +235,95 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
   for (int v = 0; v < DV / 32; ++v)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[v][e] = 0.f;
+  f32x16_t sacc[2];             // S^T of the tile between its MFMA phase and its softmax
+  f16x8_t pk[KT / 16];          // P of the tile between its softmax and its PV
+#pragma unroll
+  for (int ps = 0; ps < KT / 16; ++ps)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pk[ps][e] = (_Float16)0.f;
   const h2_t ones = {(_Float16)1.f, (_Float16)1.f};
 
-  auto tile = [&](int j0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    // S^T = K Q^T: the two 32-key blocks are independent accumulation chains,
-    // interleaved; K fragments are read KPF k-steps ahead of their MFMAs (the
-    // scheduling fence keeps the compiler from hoisting all 24 reads, which
-    // would need 96 more registers)
-    constexpr int KPF = 1;
-    auto kread = [&](int ks, int kt) {
-      LDS_AS const uint16_t* src = (ks < DN / 16) ? np[ks & 3] + kt * 32 * DN + 64 * (ks >> 2)
-                                                  : rp[ks - DN / 16] + kt * 32 * DR;
+  const int t_full = min(kfull_w / KT, ntile);                 // tiles with every key visible
+  const int t_end = min((kend_w + KT - 1) / KT, ntile);        // tiles with any key visible
+
+  // MFMA phase of tile T: O^T += V^T P^T for tile T-1 (16 MFMAs), then
+  // S^T = K Q^T for tile T (24 MFMAs, the two 32-key blocks interleaved as two
+  // accumulation chains).  The 40 operand fragments come from LDS; each is
+  // read MPF MFMAs ahead of its use, a software pipeline that hides the LDS
+  // latency inside the wave (the other wave of the SIMD is busy with its
+  // softmax meanwhile).  The scheduling fences keep the compiler from hoisting
+  // more reads than that, which would cost registers.
+  auto mfma_phase = [&](int T) {
+    // op k: k < 16 -> PV step ps = k/4, d-block v = k%4;  k >= 16 -> S k-step (k-16)/2, block (k-16)%2
+    auto frag = [&](int k) -> f16x8_t {
+      if (k < 16) return *(LDS_AS const f16x8_t*)(vp[k >> 2] + (k & 3) * 32 * KT);
+      const int ks = (k - 16) >> 1, kt = (k - 16) & 1;
+      LDS_AS const uint16_t* src = (ks < DN / 16) ? kp[ks] + kt * 32 * DN : rp[ks - DN / 16] + kt * 32 * DR;
       return *(LDS_AS const f16x8_t*)src;
     };
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
-    f16x8_t kfr[KPF + 1][2];
-#pragma unroll
-    for (int ks = 0; ks < KPF; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) kfr[ks][kt] = kread(ks, kt);
-#pragma unroll
-    for (int ks = 0; ks < DQK / 16; ++ks) {
-      if (ks + KPF < DQK / 16) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) kfr[(ks + KPF) % (KPF + 1)][kt] = kread(ks + KPF, kt);
-      }
+    // One straight-line variant serves every tile up to the wave's last: the PV
+    // of T = 0 multiplies tile 0's V^T (loaded, finite) by P = 0, and the S
+    // computed at T = t_end (possibly from a stage holding no tile) is never
+    // used.  Past that the wave only copies.  Without any tile nothing runs, so
+    // no LDS data that was never written can reach O.
+    if (T <= t_end && ntile > 0) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfr[ks % (KPF + 1)][kt], qf[ks], sacc[kt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
+      constexpr int NOPS = 16 + 2 * (DQK / 16);
+      f16x8_t fr[MPF + 1];
+#pragma unroll
+      for (int k = 0; k < MPF; ++k) fr[k] = frag(k);
+#pragma unroll
+      for (int k = 0; k < NOPS; ++k) {
+        if (k + MPF < NOPS) fr[(k + MPF) % (MPF + 1)] = frag(k + MPF);
+        if (k < 16) {
+          oacc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[k % (MPF + 1)], pk[k >> 2], oacc[k & 3], 0, 0, 0);
+        } else {
+          const int ks = (k - 16) >> 1, kt = (k - 16) & 1;
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[k % (MPF + 1)], qf[ks], sacc[kt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    float mx = -INFINITY;
+    if (T >= 1) {
+      const int st = ring_step(vstage);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int q = 0; q < 4; ++q) vp[q] += st;
+    }
+    if (T < ntile) {
+      const int st = ring_step(kstage);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        if constexpr (MASKED) {
+      for (int q = 0; q < DN / 16; ++q) kp[q] += st;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rp[q] += st;
+    }
+  };
+
+  // Softmax phase of tile T: mask (diagonal tiles), lazy reference max, P in fp16.
+  auto softmax_phase = [&](int T) {
+    if (T < 0 || T >= t_end) return;
+    if (T >= t_full) {
+      const int j0 = T * KT;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
           const int g = e >> 2, r = e & 3;
           const int j = j0 + kt * 32 + 16 * (g >> 1) + 8 * hb + 4 * (g & 1) + r;
           if (j >= lim_i) sacc[kt][e] = -INFINITY;
         }
-        mx = fmaxf(mx, sacc[kt][e]);
-      }
+    }
+    // Short dependency chains throughout: this runs on a SIMD whose other wave
+    // keeps the matrix unit busy, so its latency is what counts.
+    float m8[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int kt = c >> 2, e = 4 * (c & 3);
+      m8[c] = fmaxf(fmaxf(sacc[kt][e], sacc[kt][e + 1]), fmaxf(sacc[kt][e + 2], sacc[kt][e + 3]));
+    }
+    float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
     mx = half_pair_max(mx);
     const bool move = mx > m_run + RESCALE_TAU;
     if (__ballot(move) != 0ull) {
@@ -274,68 +338,62 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
     }
     // A row that has seen no visible key keeps m_run = -inf and uses 0.
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    // O^T += V^T P^T, 16 keys per step: elements 8u..8u+7 of block kt
+    float pv[32];
 #pragma unroll
-    for (int ps = 0; ps < KT / 16; ++ps) {
-      const int kt = ps >> 1, u = ps & 1;
-      f16x8_t pf;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = (_Float16)fast_exp2(sacc[kt][8 * u + e] - m_use);
+      for (int e = 0; e < 16; ++e) pv[16 * kt + e] = fast_exp2(sacc[kt][e] - m_use);
+    // P elements 8u..8u+7 of block kt feed PV step ps = 2kt + u
+#pragma unroll
+    for (int ps = 0; ps < KT / 16; ++ps)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[ps][e] = (_Float16)pv[8 * ps + e];
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ps = 0; ps < KT / 16; ++ps)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const h2_t pr = {pf[2 * e], pf[2 * e + 1]};
-        l_run = __builtin_amdgcn_fdot2(pr, ones, l_run, false);
+        const h2_t pr = {pk[ps][2 * e], pk[ps][2 * e + 1]};
+        ls[e] = __builtin_amdgcn_fdot2(pr, ones, ls[e], false);
       }
-      f16x8_t vf[DV / 32];
-#pragma unroll
-      for (int v = 0; v < DV / 32; ++v) vf[v] = *(LDS_AS const f16x8_t*)(rp[ps] + (V0 - R0) + v * 32 * KT);
-#pragma unroll
-      for (int v = 0; v < DV / 32; ++v)
-        oacc[v] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[v], pf, oacc[v], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
-  // ---- main loop: ring of NSTAGE tiles, two in flight ------------------------
+  // ---- main loop -----------------------------------------------------------------
+  // Two wave groups, one wave of each per SIMD, run half an iteration apart:
+  // while one group issues the MFMAs of a tile the other computes a softmax, so
+  // each SIMD keeps its matrix unit and its vector ALU busy at the same time.
+  //   group 0, iteration T:  MFMA(T)       | barrier | softmax(T)
+  //   group 1, iteration T:  softmax(T-1)  | barrier | MFMA(T)
+  // Every wave passes the same 2*(ntile+1) barriers.  At the top of iteration T
+  // the copies of tile T have landed for every wave, and the last reads of tile
+  // T-2 (its PV, in MFMA(T-1)) are done, so the copy of tile T+2 can take its
+  // stage: a ring of 4 stages with two tiles in flight.
+  auto top = [&](int T) {
+    if (T < ntile) {
+      if (T + 1 < ntile) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (T + 2 < ntile) issue();
+  };
   if (ntile > 0) issue();
   if (ntile > 1) issue();
-  // Every wave passes the same ntile barriers; its own tiles split into the
-  // unmasked ones, the diagonal ones (masked) and those past its last key
-  // (copies only), each in a loop of its own so that the accumulators keep
-  // their registers across iterations.
-  int stage = 0;
-  auto next_tile = [&](int t) {
-    // this wave's copies of tile t have landed (tile t+1's may still run); the
-    // barrier extends that to every wave and also retires all reads of tile t-1,
-    // whose stage the copy of tile t+2 overwrites
-    if (t + 1 < ntile) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (t + 2 < ntile) issue();
-  };
-  auto advance = [&]() {
-    const int step = (stage == NSTAGE - 1) ? -(NSTAGE - 1) * STAGE : STAGE;
-    stage = (stage == NSTAGE - 1) ? 0 : stage + 1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      np[q] += step;
-      rp[q] += step;
+  if (wave < NW / 2) {
+    for (int T = 0; T <= ntile; ++T) {
+      top(T);
+      mfma_phase(T);
+      __builtin_amdgcn_s_barrier();
+      softmax_phase(T);
     }
-  };
-  const int t_full = min(kfull_w / KT, ntile);                 // tiles with every key visible
-  const int t_end = min((kend_w + KT - 1) / KT, ntile);        // tiles with any key visible
-  int t = 0;
-  for (; t < t_full; ++t) {
-    next_tile(t);
-    tile(t * KT, std::false_type{});
-    advance();
+  } else {
+    for (int T = 0; T <= ntile; ++T) {
+      top(T);
+      softmax_phase(T - 1);
+      __builtin_amdgcn_s_barrier();
+      mfma_phase(T);
+    }
   }
-  for (; t < t_end; ++t) {
-    next_tile(t);
-    tile(t * KT, std::true_type{});
-    advance();
-  }
-  for (; t < ntile; ++t) next_tile(t);
 
   // ---- epilogue ---------------------------------------------------------------
   const float l = half_pair_sum(l_run);
