@@ -29,9 +29,18 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file compiler options.  The split-KV decode kernel keeps its value
+# accumulators in AGPRs through inline assembly; selecting the VGPR form for
+# the compiler's own MFMAs keeps the score accumulators (read by the softmax)
+# out of the AGPR file that those accumulators fill.
+FILE_FLAGS = {
+    "mfma_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str, resource_usage: bool) -> tuple[str, str]:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if resource_usage:
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -97,6 +97,27 @@ extern "C" __device__ void mla_raw_buffer_load_lds(i32x4_t rsrc, LDS_AS void* ld
                                                    int soffset, int offset,
                                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
+// The same 16-byte buffer->LDS copy issued as inline assembly: M0 holds the
+// LDS address of lane 0's destination (lane l writes at M0 + 16 l); the byte
+// address is voffset (per lane) + soffset (uniform) from the resource base.  The
+// compiler does not see these as LDS writes, so it adds no waits of its own
+// before later LDS reads (it would otherwise wait for every copy in flight
+// before reading any LDS array it cannot prove disjoint); the caller orders
+// them with s_waitcnt vmcnt and a workgroup barrier.  Copies past the
+// resource's byte range read as zero.
+__device__ __forceinline__ void lds_dma_b128(i32x4_t rsrc, uint32_t lds_addr, int voffset, int soffset = 0) {
+  int saved;    // M0 is restored, so the compiler's own uses of it are unaffected
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
+
 // Buffer resource for `bytes` bytes at `base` (gfx9 data-format word).
 __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
   uint64_t p = reinterpret_cast<uint64_t>(base);

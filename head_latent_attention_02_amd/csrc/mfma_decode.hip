@@ -71,16 +71,33 @@ absorb_bf16_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
 // ---------------------------------------------------------------------------
 // Split-KV partial attention.
 //
-// One workgroup per (chunk, sequence); 8 waves, wave w owns heads 16w ..
-// 16w+15 (heads past H idle).  The chunk's cache rows stream through a ring of
-// 4 LDS tile buffers of 32 tokens x 576 latent columns (direct buffer->LDS
-// loads by 4 loader waves, 3 tiles in flight).  Per tile each wave computes
-//   S^T[t][h] = C[t][:576] . q~[h]          (16x16x32 bf16 MFMA, q~ in VGPRs)
-//   online softmax in the log2 domain       (each lane owns one head)
-//   O^T[d][h] += C^T[d][t] P^T[t][h]        (16x16x32 bf16 MFMA, P in VGPRs)
-// so P never leaves registers: the first product's result layout (token rows
-// 4q4 + r of each 16-token half) is the k-slot layout the second product needs
-// once C^T is read with the LDS transpose read (ds_read_b64_tr_b16).
+// One workgroup of 4 waves (one per SIMD, the whole register file each) per
+// (chunk, sequence).  The chunk's cache rows stream through a ring of 4 LDS
+// tile buffers of 32 tokens x 576 latent columns, filled by direct
+// buffer->LDS loads (every lane issues 9 loads of 16 bytes per tile; 2 to 3
+// tiles are in flight while one is computed).  Each tile goes through two
+// products:
+//
+//   scores: wave w owns head groups 2w and 2w+1 (32 heads, q~ in VGPRs) and
+//     computes S^T[t][h] = C[t][:576] . q~[h] on 16x16x32 bf16 MFMA, then the
+//     online softmax in the log2 domain (each lane owns one head of each
+//     group); P^T (bf16) and, when a head's reference max moved, its rescale
+//     factor go to LDS;
+//   values: wave w owns latent columns 128w .. 128w+127 of every head and
+//     accumulates O^T[d][h] += C^T[d][t] P^T[t][h] (16x16x32 bf16 MFMA,
+//     accumulators in AGPRs).
+//
+// Splitting the value product by latent column means the tile's 512 value
+// columns are read from LDS once per tile in total (with the transposed LDS
+// read, ds_read_b64_tr_b16), and P^T for all heads is only 8 KB; the score
+// product reads the tile once per 32 heads.  While a tile is computed, the
+// next three are in flight, so the cache stream does not wait for the MFMAs.
+//
+// The score result layout (token rows 4q4 + r of each 16-token half) is kept
+// as the k-slot order of the value product: P^T slot 8q4 + u of a head is
+// token 4q4 + u (u < 4) or 16 + 4q4 + u - 4 (u >= 4), and the transposed
+// reads of C^T use the same permutation, so a score lane writes its 8
+// probabilities as one 16-byte chunk that a value lane reads back unchanged.
 // The reference max of a head only moves when a tile exceeds it by more than
 // 8 (log2 units), which skips the accumulator rescale on most tiles; the
 // result is exact either way because l and O share the same reference.
@@ -89,9 +106,13 @@ absorb_bf16_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
 constexpr int TT = 32;                   // tokens per tile
 constexpr int NBUF = 4;                  // tile ring depth
 constexpr int CHUNKS = DLAT / 8;         // 16-byte chunks per row (72)
-constexpr int NTHREADS = 512;
-constexpr int LOADERS = 4;               // waves that issue the tile loads
-constexpr int LOADS = TT * CHUNKS / (LOADERS * 64);   // loads per loader wave per tile (9)
+constexpr int NTHREADS = 256;
+constexpr int NW = NTHREADS / 64;        // waves
+constexpr int MAXG = 8;                  // head groups of 16 (128 heads)
+constexpr int LOADS = TT * CHUNKS / NTHREADS;         // loads per lane per tile (9)
+constexpr int DT_W = DC / 16 / NW;       // value-product d-tiles per wave (8)
+constexpr int KS = DLAT / 32;            // score k-steps (18)
+constexpr int SPF = 4;                   // score fragments read ahead of their MFMAs
 constexpr float RESCALE_TAU = 8.f;       // log2 units
 
 typedef short lds_v4s __attribute__((__vector_size__(4 * sizeof(short))));
@@ -100,175 +121,315 @@ typedef short lds_v4s __attribute__((__vector_size__(4 * sizeof(short))));
 // both the row reads and the transposed reads below)
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
+// acc += A B on the 16x16x32 bf16 MFMA, with the accumulator held in AGPRs.
+// Written as inline assembly so that the value-product accumulators (256
+// registers) stay in the AGPR file while the score accumulators, which the
+// softmax reads, are VGPRs.  Every compiler-generated access to these AGPRs
+// (zeroing, the rescale, the final read) is separated from the MFMAs by a
+// barrier or an explicit s_nop, which covers the MFMA result latency.
+__device__ __forceinline__ void mfma_agpr(f32x4_t& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::); }
+// acc = 0 (0 x 0 + 0 on the same MFMA, so the accumulator never leaves the
+// AGPRs).  The zero operand is written by VALU moves that the compiler may
+// place right before this statement; the s_nop gives the MFMA the wait states
+// that a VALU write needs before an MFMA reads the register.
+__device__ __forceinline__ void mfma_agpr_zero(f32x4_t& acc) {
+  const bf16x8_t z = {};
+  asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
+}
+
 __device__ __forceinline__ bf16x8_t cat_bf16(lds_v4s lo, lds_v4s hi) {
   u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
   u32x4_t r = {a[0], a[1], b[0], b[1]};
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
-__global__ void __launch_bounds__(NTHREADS)
+// max / sum over the 4 lanes l16 + 16 q4 (q4 = 0..3) that share a head
+__device__ __forceinline__ float quad_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return half_pair_max(v);
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  return half_pair_sum(v);
+}
+
+template <int NHT>       // head groups of 16 (H = 16 NHT)
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __restrict__ lse_part,
                     float* __restrict__ o_part) {
   __shared__ __attribute__((aligned(16))) uint16_t Cs[NBUF][TT * DLAT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[MAXG * 16 * TT];   // P^T [h][k-slot]
+  __shared__ float linv_s[MAXG * 16];   // 1 / softmax denominator at the end
+  __shared__ int redo_s;                // a reference max was exceeded by more than tau
 
   const int k = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int h = wave * 16 + l16;
-  const bool wave_active = wave * 16 < a.H;     // H is a multiple of 16
+  const int hg0 = 2 * wave;                     // first head group of this wave's scores
+  const bool score_wave = hg0 < NHT;
 
   const int L = min(max(a.cache_len[b], 0), a.max_len);
   const int csz = (L + a.n_splits - 1) / a.n_splits;
   const int t0 = min(L, k * csz), t1 = min(L, (k + 1) * csz);
   const int ntile = (t1 - t0 + TT - 1) / TT;
 
-  // q~ as the B operand: lane holds q~[h][32ks + 8q4 .. +8]
-  bf16x8_t qf[DLAT / 32];
-  {
-    const uint16_t* qrow = qt + ((int64_t)b * a.H + (wave_active ? h : 0)) * DLAT;
+  // q~ as the B operand: lane holds q~[h][32ks + 8q4 .. +8] for h = 16g + l16
+  // of groups g = hg0, hg0 + 1 (zero for a group past H)
+  bf16x8_t qf[2][KS];
 #pragma unroll
-    for (int ks = 0; ks < DLAT / 32; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 32 + q4 * 8);
+  for (int hg = 0; hg < 2; ++hg) {
+    const int g = hg0 + hg;
+    const uint16_t* qrow = qt + ((int64_t)b * a.H + 16 * min(g, NHT - 1) + l16) * DLAT + q4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 32);
+      qf[hg][ks] = (g < NHT) ? v : bf16x8_t{};
+    }
   }
+  wait_vmcnt<0>();      // q~ has landed; from here on vmcnt counts tile loads only
 
-  // Tile loads: loader wave w, instruction i fills tile slots (w*LOADS+i)*64 +
-  // lane, i.e. row slot/72 and swizzled chunk slot%72.  The buffer range ends
-  // at the chunk's last row, so rows past it read as zero.
+  // Tile loads: lane instruction i fills tile slot s = (wave*9 + i)*64 + lane,
+  // i.e. row s/72 and swizzled chunk s%72.  The buffer range ends at the
+  // chunk's last row, so rows past it read as zero.
   const uint16_t* cbase = static_cast<const uint16_t*>(a.cache) + (int64_t)b * a.cache_stride;
   const i32x4_t rsrc = make_rsrc(cbase, (uint32_t)t1 * (DLAT * 2));
-  int voff[LOADS];
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);      // wave index as a scalar
+  const uint32_t cs_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&Cs[0][0];
+  // byte offset inside a tile of the lane's 9 slots (< 36864, two per register)
+  uint32_t slot_off[(LOADS + 1) / 2];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int slot = ((wave & (LOADERS - 1)) * LOADS + i) * 64 + lane;
+    const int slot = (wave * LOADS + i) * 64 + lane;
     const int r = slot / CHUNKS, pc = slot - r * CHUNKS;
-    voff[i] = r * (DLAT * 2) + swz(r, pc) * 16;
+    const uint32_t off = (uint32_t)(r * (DLAT * 2) + swz(r, pc) * 16);
+    if (i & 1) slot_off[i >> 1] |= off << 16;
+    else slot_off[i >> 1] = off;
   }
   auto issue_tile = [&](int tile) {
-    if (wave >= LOADERS) return;
-    const int tbyte = (t0 + tile * TT) * (DLAT * 2);
-    uint16_t* dst = &Cs[tile & (NBUF - 1)][0];
+    const int tbyte = __builtin_amdgcn_readfirstlane((t0 + tile * TT) * (DLAT * 2));
+    const uint32_t dst = cs_lds + (uint32_t)((tile & (NBUF - 1)) * (TT * DLAT * 2) + wave_s * (LOADS * 1024));
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      mla_raw_buffer_load_lds(rsrc, (LDS_AS void*)(dst + (wave * LOADS + i) * 512), 16, voff[i] + tbyte, 0, 0, 0);
+    for (int i = 0; i < LOADS; ++i) {
+      const int voff_i = (int)((i & 1) ? (slot_off[i >> 1] >> 16) : (slot_off[i >> 1] & 0xffffu));
+      lds_dma_b128(rsrc, dst + i * 1024, voff_i, tbyte);
+    }
+  };
+  // wait until the loads of tile `tile` (issued in order) have landed, given
+  // that tiles up to `last_issued` have been issued
+  auto wait_tile = [&](int tile, int last_issued) {
+    const int after = last_issued - tile;
+    if (after >= 3) wait_vmcnt<3 * LOADS>();
+    else if (after == 2) wait_vmcnt<2 * LOADS>();
+    else if (after == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
   };
 
-  const float c_log2 = a.scale * MLA_LOG2E;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t oacc[DC / 16];
+  // Score-product row reads.  The read for k-step ks is logical chunk 4ks + q4
+  // of row l16 (+16 for the second token half, which shares the swizzle); with
+  // s = l16 & 7 that is physical chunk 4(ks ^ s/4) + (q4 ^ s%4), so even and
+  // odd k-steps each walk a fixed base in steps of 8 chunks.
+  int soff_e, soff_o;
+  {
+    const int rsw = l16 & 7;
+    const int rp = l16 * DLAT + 8 * (q4 ^ (rsw & 3));
+    soff_e = rp + 32 * (rsw >> 2);
+    soff_o = rp + 32 * (1 - (rsw >> 2));
+  }
+  auto sfrag = [&](const uint16_t* C, int s) -> bf16x8_t {   // s = 2 ks + st
+    const int ks = s >> 1, st = s & 1;
+    const int off = ((ks & 1) ? soff_o : soff_e) + 64 * (ks >> 1) + st * 16 * DLAT;
+    return *reinterpret_cast<const bf16x8_t*>(C + off);
+  };
+  // Value-product transposed reads.  Lane (row d = 16dt + l16, k-slots 8q4 + u)
+  // holds C[token][d] for tokens 4q4 + u (u < 4) and 16 + 4q4 + u - 4 (u >= 4):
+  // two reads of 4 rows x 16 columns per 16-lane group, rows ra and ra + 16
+  // (same swizzle).  Element 16dt + 4(l16&3) sits in chunk 2dt + x,
+  // x = (l16&3)>>1, which the row swizzle s maps to 2(dt ^ s/2) + (x ^ s%2);
+  // this wave's d-tiles are dt = 8 wave + i, so dt & 3 = i & 3 and
+  // dt >> 2 = 2 wave + i/4.
+  int voff[4];
+  {
+    const int ra = 4 * q4 + (l16 >> 2);
+    const int sa = ra & 7;
+    const int x = (l16 & 3) >> 1, w4 = 4 * (l16 & 1);
 #pragma unroll
-  for (int d = 0; d < DC / 16; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int i = 0; i < NBUF - 1 && i < ntile; ++i) issue_tile(i);
-
-  for (int t = 0; t < ntile; ++t) {
-    const int ahead = min(NBUF - 2, ntile - 1 - t);       // tiles issued after tile t
-    if (ahead >= 2) wait_vmcnt<2 * LOADS>();
-    else if (ahead == 1) wait_vmcnt<LOADS>();
-    else wait_vmcnt<0>();
-    // own loads of tile t have landed; the barrier makes that true for all
-    // waves and also fences the reuse of the buffer read in iteration t-1
-    __builtin_amdgcn_s_barrier();
-    if (t + NBUF - 1 < ntile) issue_tile(t + NBUF - 1);
-    if (!wave_active) continue;
-
-    const uint16_t* C = &Cs[t & (NBUF - 1)][0];
-    const int tt = t0 + t * TT;
-
-    // S^T = C q~^T: sacc[st][r] is head h, token 16st + 4q4 + r.  The row read
-    // for k-step ks is chunk (4ks + q4) ^ sw(row); since q4 < 4 this is
-    // 4*(ks ^ sw/4) + (q4 ^ sw%4), so even and odd k-steps each walk a fixed
-    // base in steps of 8 chunks.
-    f32x4_t sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    const uint16_t* pe[2];
-    const uint16_t* po[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int row = st * 16 + l16;
-      const int rsw = row & 7;
-      const uint16_t* rp = C + row * DLAT + 8 * (q4 ^ (rsw & 3));
-      pe[st] = rp + 32 * (rsw >> 2);          // chunk group of even k-steps
-      po[st] = rp + 32 * (1 - (rsw >> 2));    // and of odd ones
-    }
-    // the two 16-token halves are independent accumulation chains; interleave them
-#pragma unroll
-    for (int ks = 0; ks < DLAT / 32; ++ks)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const uint16_t* ap = ((ks & 1) ? po[st] : pe[st]) + 64 * (ks >> 1);
-        bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(ap);
-        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[ks], sacc[st], 0, 0, 0);
-      }
-
-    // online softmax (log2 domain) with a lazily moved reference max
-    const bool tail = (tt + TT > t1);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = sacc[st][r] * c_log2;
-        if (tail && (tt + 16 * st + 4 * q4 + r >= t1)) x = -INFINITY;
-        sacc[st][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool move = mx > m_run + RESCALE_TAU;         // always true on the first tile
-    if (__ballot(move) != 0ull) {
-      const float alpha = move ? fast_exp2(m_run - mx) : 1.f;   // 0 on the first tile
-      const float m_new = move ? mx : m_run;
-      l_run *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < DC / 16; ++d) oacc[d] *= alpha;
-    }
-    bf16x8_t pf;
-    float rs = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float pv = fast_exp2(sacc[st][r] - m_run);
-        rs += pv;
-        pf[4 * st + r] = __builtin_bit_cast(__bf16, float_to_bf16_bits(pv));
-      }
-    l_run += rs;
-
-    // O^T += C^T P^T.  Lane (row d = 16dt + l16, k-slots 8q4 + u) holds
-    // C[token][d] for tokens 4q4 + u (u < 4) and 16 + 4q4 + u - 4 (u >= 4):
-    // two transposed reads of 4 rows x 16 columns per 16-lane group.
-    // Element e0 = 16dt + 4(l16&3) sits in chunk 2dt + x, x = (l16&3)>>1, which
-    // the row swizzle s maps to 2(dt ^ s/2) + (x ^ s%2): within each group of 4
-    // d-tiles the order is permuted, so 4 bases per row walk in steps of 8 chunks.
-    const int ra = 4 * q4 + (l16 >> 2), rb = ra + 16;
-    const int sa = ra & 7, sb = rb & 7;
-    const int x = (l16 & 3) >> 1, w = 4 * (l16 & 1);
-    const uint16_t* pa[4];
-    const uint16_t* pb[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      pa[m] = C + ra * DLAT + 8 * (2 * (m ^ (sa >> 1)) + (x ^ (sa & 1))) + w;
-      pb[m] = C + rb * DLAT + 8 * (2 * (m ^ (sb >> 1)) + (x ^ (sb & 1))) + w;
-    }
-#pragma unroll
-    for (int dt = 0; dt < DC / 16; ++dt) {
-      const int m = dt & 3, j = dt >> 2;
-      lds_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(pa[m] + 64 * j));
-      lds_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(pb[m] + 64 * j));
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat_bf16(lo, hi), pf, oacc[dt], 0, 0, 0);
-    }
+    for (int m = 0; m < 4; ++m)
+      voff[m] = ra * DLAT + 8 * (2 * (m ^ (sa >> 1)) + (x ^ (sa & 1))) + w4 + 128 * wave;
   }
 
-  if (!wave_active) return;
-  float l = l_run + __shfl_xor(l_run, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  const int64_t pidx = ((int64_t)b * a.n_splits + k) * a.H + h;
-  float* dst = o_part + pidx * DC;
+  const float c_log2 = a.scale * MLA_LOG2E;
+  float m_ref[2] = {-INFINITY, -INFINITY}, m_max[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4_t oacc[DT_W][NHT];                      // [d-tile of this wave][head group]
+  f32x4_t sacc[2][2];                           // [token half][head group]
+
+  // Score product of the tile in Csc: S^T[t][h] for 32 tokens x this wave's
+  // 32 heads, 72 MFMAs in four accumulation chains; fragments are read SPF
+  // ahead of their MFMAs.
+  auto score_phase = [&](const uint16_t* Csc) {
+    bf16x8_t af[SPF + 1];
 #pragma unroll
-  for (int d = 0; d < DC / 16; ++d)
-    *reinterpret_cast<f32x4_t*>(dst + d * 16 + 4 * q4) = oacc[d] * inv;
-  if (q4 == 0) lse_part[pidx] = (l > 0.f) ? (m_run + __log2f(l)) * MLA_LN2 : -INFINITY;
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg) sacc[st][hg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SPF; ++s) af[s] = sfrag(Csc, s);
+#pragma unroll
+    for (int s = 0; s < 2 * KS; ++s) {
+      if (s + SPF < 2 * KS) af[(s + SPF) % (SPF + 1)] = sfrag(Csc, s + SPF);
+      const int ks = s >> 1, st = s & 1;
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg)
+        sacc[st][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s % (SPF + 1)], qf[hg][ks], sacc[st][hg], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Value product of the tile in Cv: O^T for this wave's 128 latent columns
+  // and every head group, 8 NHT MFMAs.  C^T fragments are read for half of
+  // the d-tiles at a time, P^T fragments one head group ahead.
+  auto value_phase = [&](const uint16_t* Cv) {
+    bf16x8_t cf[DT_W / 2];
+    bf16x8_t pg[2];
+    auto load_cf = [&](int half) {
+#pragma unroll
+      for (int j = 0; j < DT_W / 2; ++j) {
+        const int i = half * (DT_W / 2) + j;
+        const int off = voff[i & 3] + 64 * (i >> 2);
+        lds_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(Cv + off));
+        lds_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(Cv + off + 16 * DLAT));
+        cf[j] = cat_bf16(lo, hi);
+      }
+    };
+    auto load_pg = [&](int g, int slot) {
+      pg[slot] = *reinterpret_cast<const bf16x8_t*>(&Ps[(16 * g + l16) * TT + 8 * q4]);
+    };
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      load_cf(half);
+      load_pg(0, 0);
+#pragma unroll
+      for (int g = 0; g < NHT; ++g) {
+        if (g + 1 < NHT) load_pg(g + 1, (g + 1) & 1);
+#pragma unroll
+        for (int j = 0; j < DT_W / 2; ++j) mfma_agpr(oacc[half * (DT_W / 2) + j][g], cf[j], pg[g & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Softmax of the tile whose scores are in sacc (first token tt) against the
+  // pass's reference max m_ref: publishes P^T = exp2(s - m_ref) in bf16 and
+  // adds the row sums to l_run.  The reference is the first tile's max (or,
+  // on a second pass, the chunk's max); a later tile whose max exceeds it by
+  // more than tau flags the pass for a redo instead of rescaling the
+  // accumulators, so the accumulators are only ever touched by MFMAs and P
+  // stays below 2^tau.
+  auto softmax_publish = [&](int tt) {
+    if (tt + TT > t1) {          // tail tile: tokens past the chunk end get no weight
+#pragma unroll
+      for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (tt + 16 * st + 4 * q4 + r >= t1) sacc[st][hg][r] = -INFINITY;
+    }
+    bool exceeded = false;
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sacc[st][hg][r] *= c_log2;
+          mx = fmaxf(mx, sacc[st][hg][r]);
+        }
+      mx = quad_max(mx);
+      m_max[hg] = fmaxf(m_max[hg], mx);
+      if (m_ref[hg] == -INFINITY) m_ref[hg] = mx;        // first tile of the first pass
+      else exceeded |= mx > m_ref[hg] + RESCALE_TAU;
+      const int h = 16 * (hg0 + hg) + l16;
+      bf16x8_t pf;
+      float rs = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = fast_exp2(sacc[st][hg][r] - m_ref[hg]);
+          rs += pv;
+          pf[4 * st + r] = (__bf16)pv;      // round to nearest even
+        }
+      l_run[hg] += rs;
+      *reinterpret_cast<bf16x8_t*>(&Ps[h * TT + 8 * q4]) = pf;
+    }
+    if (__ballot(exceeded) != 0ull && lane == 0) redo_s = 1;
+  };
+
+  // Iteration T computes tile T: scores, softmax, then the value product.
+  // Only tile T's buffer is in use meanwhile, so tiles T+1 .. T+3 are in
+  // flight (tile T+3 is issued into the buffer released by tile T-1).  A redo
+  // (second pass) starts from the chunk max seen by the first pass, which no
+  // tile exceeds.
+  for (int pass = 0; pass < 2; ++pass) {
+    if (tid == 0) redo_s = 0;
+#pragma unroll
+    for (int i = 0; i < DT_W; ++i)
+#pragma unroll
+      for (int g = 0; g < NHT; ++g) mfma_agpr_zero(oacc[i][g]);
+    l_run[0] = l_run[1] = 0.f;
+    for (int i = 0; i < NBUF - 1 && i < ntile; ++i) issue_tile(i);
+    for (int T = 0; T < ntile; ++T) {
+      wait_tile(T, min(T + NBUF - 2, ntile - 1));
+      // tile T has landed for every wave; every wave is done with tile T-1
+      // and with P^T of tile T-1
+      __syncthreads();
+      if (T + NBUF - 1 < ntile) issue_tile(T + NBUF - 1);
+      const uint16_t* C = &Cs[T & (NBUF - 1)][0];
+      if (score_wave) {
+        score_phase(C);
+        softmax_publish(t0 + T * TT);
+      }
+      __syncthreads();      // P^T of tile T is visible
+      value_phase(C);
+    }
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(redo_s)) break;
+    m_ref[0] = m_max[0];
+    m_ref[1] = m_max[1];
+    __syncthreads();      // every wave has read the flag before it is cleared
+  }
+
+  if (score_wave) {
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) {
+      if (hg0 + hg >= NHT) break;
+      const float l = quad_sum(l_run[hg]);
+      const int h = 16 * (hg0 + hg) + l16;
+      if (q4 == 0) {
+        linv_s[h] = (l > 0.f) ? 1.f / l : 0.f;
+        lse_part[((int64_t)b * a.n_splits + k) * a.H + h] =
+            (l > 0.f) ? (m_ref[hg] + __log2f(l)) * MLA_LN2 : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+  mfma_drain();
+  // lane holds O^T[d = 16 (8 wave + i) + 4q4 + r][h = 16g + l16]
+  float* dst = o_part + ((int64_t)b * a.n_splits + k) * a.H * DC + 128 * wave + 4 * q4;
+#pragma unroll
+  for (int g = 0; g < NHT; ++g) {
+    const int hh = 16 * g + l16;
+    const float inv = linv_s[hh];
+#pragma unroll
+    for (int i = 0; i < DT_W; ++i)
+      *reinterpret_cast<f32x4_t*>(dst + (int64_t)hh * DC + 16 * i) = oacc[i][g] * inv;
+  }
 }
 
 }  // namespace
@@ -282,6 +443,22 @@ hipError_t launch_absorb_bf16(const DecodeArgs& a, uint16_t* qt, hipStream_t str
 hipError_t launch_mfma_splitkv(const DecodeArgs& a, const uint16_t* qt, float* lse_part, float* o_part,
                                hipStream_t stream) {
   dim3 grid(a.n_splits, a.B);
-  hipLaunchKernelGGL(mfma_splitkv_kernel, grid, dim3(NTHREADS), 0, stream, a, qt, lse_part, o_part);
+  switch (a.H >> 4) {
+#define MLA_SPLITKV_CASE(n)                                                                               \
+  case n:                                                                                                 \
+    hipLaunchKernelGGL(mfma_splitkv_kernel<n>, grid, dim3(NTHREADS), 0, stream, a, qt, lse_part, o_part); \
+    break;
+    MLA_SPLITKV_CASE(1)
+    MLA_SPLITKV_CASE(2)
+    MLA_SPLITKV_CASE(3)
+    MLA_SPLITKV_CASE(4)
+    MLA_SPLITKV_CASE(5)
+    MLA_SPLITKV_CASE(6)
+    MLA_SPLITKV_CASE(7)
+    MLA_SPLITKV_CASE(8)
+#undef MLA_SPLITKV_CASE
+    default:
+      return hipErrorInvalidValue;   // excluded by the host-side eligibility check
+  }
   return hipGetLastError();
 }
