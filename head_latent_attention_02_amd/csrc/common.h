@@ -125,6 +125,15 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
+// The same resource forced into scalar registers (for values the compiler
+// cannot prove uniform; the caller guarantees they are).
+__device__ __forceinline__ i32x4_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+  i32x4_t r = make_rsrc(base, bytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+  return r;
+}
+
 // s_waitcnt vmcnt(n), leaving the other counters unconstrained
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

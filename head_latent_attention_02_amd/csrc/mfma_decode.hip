@@ -131,6 +131,9 @@ __device__ __forceinline__ void mfma_agpr(f32x4_t& acc, bf16x8_t a, bf16x8_t b) 
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::); }
+// Marks acc as produced here: compiler-generated reads of the accumulator
+// (AGPR -> VGPR copies) cannot move above this point, which follows the drain.
+__device__ __forceinline__ void agpr_fence(f32x4_t& acc) { asm volatile("" : "+a"(acc)); }
 // acc = 0 (0 x 0 + 0 on the same MFMA, so the accumulator never leaves the
 // AGPRs).  The zero operand is written by VALU moves that the compiler may
 // place right before this statement; the s_nop gives the MFMA the wait states
@@ -427,8 +430,10 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
     const int hh = 16 * g + l16;
     const float inv = linv_s[hh];
 #pragma unroll
-    for (int i = 0; i < DT_W; ++i)
+    for (int i = 0; i < DT_W; ++i) {
+      agpr_fence(oacc[i][g]);
       *reinterpret_cast<f32x4_t*>(dst + (int64_t)hh * DC + 16 * i) = oacc[i][g] * inv;
+    }
   }
 }
 

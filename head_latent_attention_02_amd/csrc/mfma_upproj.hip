@@ -7,21 +7,25 @@
 // made it slower at equal FLOPs, so it runs here as one GEMM over all heads:
 //   C[j, n] = sum_c c_kv[b, j, c] * W[n, c],   j < s_vis, n < H * 256.
 // Both operands are contiguous along c (W is stored one row per output
-// feature), which is what the MFMA operand layout wants, so no transpose is
-// needed on the way in.
+// feature), which is the MFMA operand layout, so nothing is transposed on
+// the way in.
 //
 // Outputs (fp16): Kn [B, H, s_pad, 128] and V^T [B, H, 128, s_pad] (key index
 // fastest, the layout the attention kernel's P.V product reads).
 //
-// Tiling: 256 latent rows x 256 output columns (one head) per tile, 4 waves of
-// 128 x 128 (one wave per SIMD, accumulators in the extended register file);
-// waves 0-1 produce the K_nope half (operands swapped so each lane ends with 4
-// consecutive features of one key), waves 2-3 the V half (each lane ends with
-// 4 consecutive keys of one feature).  The reduction runs in 8 steps of 64
-// staged through LDS with a register prefetch of the next step.  The grid is
-// persistent: each workgroup walks tiles so that the stores of one tile drain
-// while the next one computes, and tiles are dealt so that the 32 CUs of one
-// XCD work on neighbouring tiles of the same heads (shared L2).
+// Persistent kernel, one workgroup of 4 waves per CU (one wave per SIMD, the
+// whole register file each).  A tile is 256 latent rows x the 256 output
+// columns of one head; waves 0-1 produce its K_nope half (W rows as the A
+// operand, so each lane ends with 4 consecutive features of one key) and
+// waves 2-3 its V half (latent rows as the A operand, so each lane ends with
+// 4 consecutive keys of one feature), 128 x 128 per wave on 32x32x16 MFMA
+// with the accumulators in AGPRs.  The reduction over the 512 latent columns
+// streams in steps of 32 through a ring of 4 LDS stages (16 KB of latent
+// rows + 16 KB of W rows each) filled by direct buffer->LDS loads; the ring
+// runs across tile boundaries, so the next tile's first steps are in flight
+// while a tile's results are converted and stored.  Tiles are dealt so that
+// the 32 CUs of an XCD work on 4 heads x 8 key tiles at a time (1 MB of W and
+// 2 MB of latent rows, inside that XCD's L2).
 #include "common.h"
 #include "kernels.h"
 
@@ -29,137 +33,184 @@ namespace {
 
 constexpr int TJ = 256;          // latent rows per tile
 constexpr int TN = 256;          // output columns per tile (= one head)
-constexpr int TK = 64;           // reduction step
+constexpr int TK = 32;           // reduction step
 constexpr int DKV = 512;
-constexpr int PITCH = TK + 8;    // bf16 elements per LDS row (bank spread)
+constexpr int NKS = DKV / TK;    // reduction steps per tile (16)
+constexpr int NSTAGE = 4;        // LDS ring depth
 constexpr int NTHREADS = 256;
+constexpr int REG_BYTES = TJ * TK * 2;       // one operand region of a stage (16 KB)
+constexpr int STAGE_BYTES = 2 * REG_BYTES;   // latent rows then W rows
+constexpr int LOADS = 2 * REG_BYTES / 16 / NTHREADS;   // 16-byte copies per lane per step (8)
 
-__global__ void __launch_bounds__(NTHREADS)
+// acc += A B on the 32x32x16 bf16 MFMA with the accumulator held in AGPRs
+// (the 256 accumulator registers fill the AGPR file; operands stay in VGPRs).
+__device__ __forceinline__ void mfma32_agpr(f32x16_t& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// acc = A B (the first product of a tile starts the accumulation)
+__device__ __forceinline__ void mfma32_agpr_first(f32x16_t& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::); }
+// Marks acc as produced here: compiler-generated reads of the accumulator
+// (AGPR -> VGPR copies) cannot move above this point, which follows the
+// drain.  Used one block at a time so that only one block is copied out at
+// once.
+__device__ __forceinline__ void agpr_fence(f32x16_t& acc) { asm volatile("" : "+a"(acc)); }
+
+// tile id -> (batch*head, key tile)
+__device__ __forceinline__ void tile_coords(int tile, int n_jt, bool xcd_deal, int& bh, int& jt) {
+  if (xcd_deal) {
+    // 256 consecutive tile ids = 8 groups of 32 (one per XCD); group c covers
+    // heads 4(c/2) .. 4(c/2)+3 and key tiles 8(c%2) .. 8(c%2)+7 of a 16-tile row
+    const int step = tile >> 8, w = tile & 255;
+    const int xcd = w & 7, m = w >> 3;
+    const int c = step * 8 + xcd;
+    bh = 4 * (c >> 1) + (m >> 3);
+    jt = 8 * (c & 1) + (m & 7);
+  } else {
+    bh = tile / n_jt;
+    jt = tile - bh * n_jt;
+  }
+}
+
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w,
                    uint16_t* __restrict__ kn, uint16_t* __restrict__ vt, int B, int H, int Skv,
-                   int s_vis, int s_pad, int n_jt, int n_tiles) {
-  // rows 0..TJ-1: latent rows (A); rows TJ..TJ+TN-1: W rows of the head (B)
-  __shared__ __attribute__((aligned(16))) uint16_t Ls[(TJ + TN) * PITCH];
+                   int s_vis, int s_pad, int n_jt, int n_tiles, int xcd_deal) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[NSTAGE * STAGE_BYTES / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hb = lane >> 5;
   const int part = wave >> 1;          // 0: K_nope columns, 1: V columns
   const int jq = wave & 1;             // 128-row half of the tile
-  const int l32 = lane & 31, hb = lane >> 5;
-  // Every wave computes acc[i][k] = mfma(F_i, S_k) over 4 x 4 fragments.  For
-  // K_nope waves F are W rows and S latent rows (D[n][j]); for V waves F are
-  // latent rows and S W rows (D[j][n]).
-  const int f_row0 = (part == 0) ? TJ : jq * 128;
-  const int s_row0 = (part == 0) ? jq * 128 : TJ + 128;
-
-  // tile dealing: consecutive tile ids go to the same XCD
   const int G = gridDim.x;
-  const int xcd = blockIdx.x & 7;
-  const int per_xcd = G >> 3;          // grid is a multiple of 8
-  const int local = blockIdx.x >> 3;
+  const int my_tiles = (n_tiles - (int)blockIdx.x + G - 1) / G;
+  const int total_steps = my_tiles * NKS;
 
-  for (int step = 0;; ++step) {
-    int tile = step * G + xcd * per_xcd + local;
-    if (tile >= n_tiles) break;
-    const int jt = tile % n_jt;
-    const int bh = tile / n_jt;
+  // Stage layout: rows of 32 bf16 (64 bytes = 4 chunks of 16 bytes); chunk c
+  // of row r sits at chunk c ^ ((r >> 2) & 3), which spreads the 16 rows that
+  // a 16-lane group reads over all 64 banks.
+  // Copies: lane instruction i covers slot s = 256 i + tid of a region, i.e.
+  // row 64 i + tid/4, physical chunk tid & 3 (the swizzle only depends on
+  // tid, so one per-lane offset serves every row block, step and tile).
+  const int v_lane = (tid >> 2) * (DKV * 2) + (((tid & 3) ^ ((tid >> 4) & 3)) * 16);
+  const uint32_t ls_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&Ls[0];
+
+  // fragment reads: A/B operand of the 32x32x16 MFMA = 8 consecutive bf16
+  // (logical chunk 2kk + hb) of row l32 of a 32-row block; rows 32x + l32 of
+  // a 128-row group share the swizzle (l32 >> 2) & 3
+  const int sw = (l32 >> 2) & 3;
+  const int frag_off0 = l32 * (TK * 2) + ((0 + hb) ^ sw) * 16;   // kk = 0
+  const int frag_off1 = l32 * (TK * 2) + ((2 + hb) ^ sw) * 16;   // kk = 1
+  // first (A) and second (B) operand regions of this wave, byte offsets in a stage
+  const int a_rows = (part == 0) ? (REG_BYTES + 0) : (jq * 128 * TK * 2);
+  const int b_rows = (part == 0) ? (jq * 128 * TK * 2) : (REG_BYTES + 128 * TK * 2);
+
+  // issue the copies of global reduction step g (tile g / NKS, step g % NKS)
+  auto issue_step = [&](int g) {
+    const int t = g / NKS, ks = g - t * NKS;
+    int bh, jt;
+    tile_coords((int)blockIdx.x + t * G, n_jt, xcd_deal != 0, bh, jt);
     const int h = bh % H, b = bh / H;
     const int j0 = jt * TJ;
+    const int rows = max(0, min(TJ, s_vis - j0));
+    const i32x4_t ra = make_rsrc_uniform(c_kv + ((int64_t)b * Skv + j0) * DKV, (uint32_t)rows * (DKV * 2));
+    const i32x4_t rb = make_rsrc_uniform(w + (int64_t)h * TN * DKV, (uint32_t)TN * (DKV * 2));
+    const uint32_t dst = ls_lds + (uint32_t)((g % NSTAGE) * STAGE_BYTES) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+#pragma unroll
+    for (int i = 0; i < LOADS / 2; ++i) {
+      const int so = __builtin_amdgcn_readfirstlane(i * 64 * (DKV * 2) + ks * (TK * 2));
+      lds_dma_b128(ra, dst + i * 4096, v_lane, so);
+      lds_dma_b128(rb, dst + REG_BYTES + i * 4096, v_lane, so);
+    }
+  };
 
-    const uint16_t* abase = c_kv + ((int64_t)b * Skv) * DKV;
-    const uint16_t* bbase = w + (int64_t)h * TN * DKV;
+  f32x16_t acc[4][4];
+  const int ahead = min(NSTAGE - 1, total_steps);
+  for (int g = 0; g < ahead; ++g) issue_step(g);
 
-    f32x16_t acc[4][4];
+  for (int t = 0; t < my_tiles; ++t) {
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int g = t * NKS + ks;
+      // copies of step g have landed (later steps may still be in flight)
+      const int newer = min(NSTAGE - 2, total_steps - 1 - g);
+      static_assert(NSTAGE - 2 <= 3, "wait counts below cover up to 3 newer steps");
+      if (newer >= 3) wait_vmcnt<3 * LOADS>();
+      else if (newer == 2) wait_vmcnt<2 * LOADS>();
+      else if (newer == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+      __syncthreads();           // ... for every wave; stage g-1 is free again
+      if (g + NSTAGE - 1 < total_steps) issue_step(g + NSTAGE - 1);
+
+      const char* st = reinterpret_cast<const char*>(Ls) + (g % NSTAGE) * STAGE_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int fo = kk ? frag_off1 : frag_off0;
+        bf16x8_t fa[4], fb[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          fa[x] = *reinterpret_cast<const bf16x8_t*>(st + a_rows + x * 32 * (TK * 2) + fo);
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          fb[y] = *reinterpret_cast<const bf16x8_t*>(st + b_rows + y * 32 * (TK * 2) + fo);
+        if (kk == 0 && ks == 0) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) mfma32_agpr_first(acc[x][y], fa[x], fb[y]);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) mfma32_agpr(acc[x][y], fa[x], fb[y]);
+        }
+      }
+    }
+
+    // epilogue: fp16 stores straight from the accumulators (the next tile's
+    // first steps are already in flight).  In a 32x32 block a lane holds
+    // 4 consecutive outputs for each of 4 groups gq (8 bytes each); one
+    // permlane32 swap per word gives each lane 8 consecutive outputs of group
+    // 2p (lanes 0-31) or 2p+1 (lanes 32-63), stored as one 16-byte chunk.
+    int bh, jt;
+    tile_coords((int)blockIdx.x + t * G, n_jt, xcd_deal != 0, bh, jt);
+    const int j0 = jt * TJ;
+    mfma_drain();
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int y = 0; y < 4; ++y)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
-
-    u32x4_t pa[8], pb[8];
-    auto gload = [&](int k0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int q = tid + NTHREADS * i;      // 2048 chunks of 16 B per operand
-        int row = q >> 3, c16 = q & 7;
-        // rows past the last visible one repeat it: their results land in
-        // the padding rows, which the attention kernel never lets through
-        int j = min(j0 + row, s_vis - 1);
-        pa[i] = *reinterpret_cast<const u32x4_t*>(abase + (int64_t)j * DKV + k0 + c16 * 8);
-        pb[i] = *reinterpret_cast<const u32x4_t*>(bbase + (int64_t)row * DKV + k0 + c16 * 8);
-      }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int q = tid + NTHREADS * i;
-        int row = q >> 3, c16 = q & 7;
-        *reinterpret_cast<u32x4_t*>(&Ls[row * PITCH + c16 * 8]) = pa[i];
-        *reinterpret_cast<u32x4_t*>(&Ls[(TJ + row) * PITCH + c16 * 8]) = pb[i];
-      }
-    };
-
-    gload(0);
-    for (int ks = 0; ks < DKV / TK; ++ks) {
-      __syncthreads();
-      lstore();
-      __syncthreads();
-      if (ks + 1 < DKV / TK) gload((ks + 1) * TK);
-#pragma unroll
-      for (int kk = 0; kk < TK / 16; ++kk) {
-        bf16x8_t ff[4], sf[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          ff[x] = *reinterpret_cast<const bf16x8_t*>(&Ls[(f_row0 + x * 32 + l32) * PITCH + kk * 16 + hb * 8]);
-#pragma unroll
-        for (int y = 0; y < 4; ++y)
-          sf[y] = *reinterpret_cast<const bf16x8_t*>(&Ls[(s_row0 + y * 32 + l32) * PITCH + kk * 16 + hb * 8]);
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int y = 0; y < 4; ++y)
-            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ff[x], sf[y], acc[x][y], 0, 0, 0);
-      }
-    }
-
-    // epilogue: fp16 stores straight from the accumulators
-    const int64_t head = (int64_t)b * H + h;
-    if (part == 0) {
-      // acc[x][y] holds D[n][j]: n = x*32 + 8g + 4hb + r, j = jq*128 + y*32 + l32
-#pragma unroll
       for (int y = 0; y < 4; ++y) {
-        int j = j0 + jq * 128 + y * 32 + l32;
-        uint16_t* dst = kn + (head * s_pad + j) * 128;
+        agpr_fence(acc[x][y]);
+        uint32_t wd[4][2];
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int gq = 0; gq < 4; ++gq) {
+          wd[gq][0] = pack_f16x2(acc[x][y][4 * gq + 0], acc[x][y][4 * gq + 1]);
+          wd[gq][1] = pack_f16x2(acc[x][y][4 * gq + 2], acc[x][y][4 * gq + 3]);
+        }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            int n = x * 32 + 8 * g + 4 * hb;
-            u32x2_t v2;
-            v2[0] = pack_f16x2(acc[x][y][4 * g + 0], acc[x][y][4 * g + 1]);
-            v2[1] = pack_f16x2(acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]);
-            *reinterpret_cast<u32x2_t*>(dst + n) = v2;
+        for (int pp = 0; pp < 2; ++pp) {
+          u32x4_t chunk;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            auto r = __builtin_amdgcn_permlane32_swap(wd[2 * pp][e], wd[2 * pp + 1][e], false, false);
+            chunk[e] = r[0];
+            chunk[2 + e] = r[1];
           }
-      }
-    } else {
-      // acc[x][y] holds D[j][n]: j = jq*128 + x*32 + 8g + 4hb + r, n = y*32 + l32
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        int n = y * 32 + l32;
-        uint16_t* dst = vt + (head * 128 + n) * s_pad + j0 + jq * 128;
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            int j = x * 32 + 8 * g + 4 * hb;
-            u32x2_t v2;
-            v2[0] = pack_f16x2(acc[x][y][4 * g + 0], acc[x][y][4 * g + 1]);
-            v2[1] = pack_f16x2(acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]);
-            *reinterpret_cast<u32x2_t*>(dst + j) = v2;
+          const int o = x * 32 + 16 * pp + 8 * hb;    // first of the lane's 8 outputs in the block's rows
+          if (part == 0) {
+            // D[n][j]: n = o .. o+7 (features), j = jq*128 + y*32 + l32
+            uint16_t* dst = kn + ((int64_t)bh * s_pad + j0 + jq * 128 + y * 32 + l32) * 128 + o;
+            *reinterpret_cast<u32x4_t*>(dst) = chunk;
+          } else {
+            // D[j][n]: j = jq*128 + o .. +7 (keys), n = y*32 + l32
+            uint16_t* dst = vt + ((int64_t)bh * 128 + y * 32 + l32) * s_pad + j0 + jq * 128 + o;
+            *reinterpret_cast<u32x4_t*>(dst) = chunk;
           }
+        }
+        __builtin_amdgcn_sched_barrier(0);     // one accumulator block at a time
       }
-    }
   }
 }
 
@@ -188,18 +239,20 @@ __global__ void krot_f16_kernel(const uint16_t* __restrict__ k_pe, const float2*
 
 hipError_t launch_mfma_upproj(const ExplicitArgs& a, uint16_t* kn, uint16_t* vt, hipStream_t stream) {
   if (a.s_vis == 0) return hipSuccess;
-  int n_jt = a.s_pad / TJ;
-  int n_tiles = a.B * a.H * n_jt;
+  const int n_jt = a.s_pad / TJ;
+  const int n_tiles = a.B * a.H * n_jt;
   int dev = 0, n_cu = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     n_cu = 256;
   int grid = n_cu;                                   // one workgroup per CU
   if (grid > n_tiles) grid = n_tiles;
-  grid = (grid + 7) & ~7;                            // multiple of 8 for the XCD dealing
+  // the XCD-aware dealing needs whole rounds of 256 tiles over 256 CUs,
+  // heads in groups of 4 and key rows in tiles of 16
+  const int xcd_deal = (grid == 256 && n_tiles % 256 == 0 && n_jt == 16 && (a.B * a.H) % 4 == 0) ? 1 : 0;
   hipLaunchKernelGGL(mfma_upproj_kernel, dim3(grid), dim3(NTHREADS), 0, stream,
                      static_cast<const uint16_t*>(a.c_kv), static_cast<const uint16_t*>(a.w), kn, vt,
-                     a.B, a.H, a.Skv, a.s_vis, a.s_pad, n_jt, n_tiles);
+                     a.B, a.H, a.Skv, a.s_vis, a.s_pad, n_jt, n_tiles, xcd_deal);
   return hipGetLastError();
 }
 
