@@ -21,12 +21,10 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// Round-to-nearest-even float -> bf16 bits (inputs here are finite or +-inf).
+// Round-to-nearest-even float -> bf16 bits (the hardware conversion; NaN
+// stays NaN).
 __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint16_t float_to_f16_bits(float f) {
@@ -38,8 +36,11 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return (uint32_t)float_to_f16_bits(lo) | ((uint32_t)float_to_f16_bits(hi) << 16);
 }
 
+// two floats to packed bf16 (one v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Load element i of a tensor stored as bf16 or fp32, as float.
