@@ -57,14 +57,14 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "140b9edea956bc9d", "fetch_kib": 356707.8, "write_kib": 264578.6,
-                       "fetch_factor": 0.50003, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "804c127f2b8434a7", "fetch_kib": 207065.8, "write_kib": 339206.0,
-                           "fetch_factor": 0.50003, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "121416f8a70d5077", "fetch_kib": 1217212.8, "write_kib": 271347.2,
+    "mfma_attention": {"digest": "3402e2e974c8ba6a", "fetch_kib": 346245.6, "write_kib": 292863.8,
                       "fetch_factor": 0.50003, "write_factor": 1.0},
-    "lse_combine": {"digest": "5752885ed86c67f4", "fetch_kib": 149567.9, "write_kib": 4356.3,
-                    "fetch_factor": 0.50003, "write_factor": 1.0},
+    "mfma_up_projection": {"digest": "3b2b11cb5d03cd61", "fetch_kib": 100886.2, "write_kib": 272884.8,
+                          "fetch_factor": 0.50003, "write_factor": 1.0},
+    "mfma_split_kv": {"digest": "eec60be07a2a9b05", "fetch_kib": 1216625.7, "write_kib": 262656.0,
+                     "fetch_factor": 0.50003, "write_factor": 1.0},
+    "lse_combine": {"digest": "ce99bf396e02953e", "fetch_kib": 149567.2, "write_kib": 4357.6,
+                   "fetch_factor": 0.50003, "write_factor": 1.0},
 }
 
 
