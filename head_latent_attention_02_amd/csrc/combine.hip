@@ -8,7 +8,7 @@
 //
 // One block per (head, group of CB sequences), 256 threads.
 //   1. chunk weights w_k = exp(lse_k - lse) per sequence (one wave each);
-//   2. merge: each thread owns float4 columns of the group's latent rows and
+//   2. merge: each thread owns 16-byte column groups of the group's latent rows and
 //      issues the loads of all chunks of a column before combining them, so
 //      a whole chunk row is in flight at once (the step is bandwidth-bound);
 //   3. un-absorb: thread (v, half) computes out[b, h, v] for half of the
@@ -44,9 +44,9 @@ __device__ __forceinline__ void load8(const void* w, int64_t idx, float (&f)[8])
   }
 }
 
-template <mla_dtype WT, mla_dtype OT>
+template <mla_dtype WT, mla_dtype OT, bool HALFP>
 __global__ void __launch_bounds__(CTHREADS)
-combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const float* __restrict__ o_part) {
+combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const void* __restrict__ o_part) {
   extern __shared__ __attribute__((aligned(16))) float olat[];   // [CB][dkv]
   __shared__ float wk[CB][MAXNS];
   __shared__ float lse_s[CB];
@@ -68,24 +68,39 @@ combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const float* __
   }
   __syncthreads();
 
-  // 2. merge (float4 columns; dkv is a multiple of 4 on this path)
-  const int c4n = dkv / 4;
-  const int64_t kstride = (int64_t)a.H * dkv;             // floats between chunks
-  for (int it = tid; it < nb * c4n; it += CTHREADS) {
-    const int bi = it / c4n, c4 = it - bi * c4n, b = b0 + bi;
-    const float* src = o_part + ((int64_t)b * ns * a.H + h) * dkv + 4 * c4;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // 2. merge: G columns per thread (16-byte loads: 4 fp32 or 8 fp16 partial
+  // elements; dkv is a multiple of 8 on the fp16 path and of 4 otherwise)
+  constexpr int G = HALFP ? 8 : 4;
+  const int cgn = dkv / G;
+  const int64_t kstride = (int64_t)a.H * dkv;             // elements between chunks
+  for (int it = tid; it < nb * cgn; it += CTHREADS) {
+    const int bi = it / cgn, cg = it - bi * cgn, b = b0 + bi;
+    const int64_t src = ((int64_t)b * ns * a.H + h) * dkv + G * cg;
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < ns; k0 += KBATCH) {
-      f32x4_t v[KBATCH];
+      u32x4_t v[KBATCH];
 #pragma unroll
-      for (int j = 0; j < KBATCH; ++j)
-        v[j] = (k0 + j < ns) ? *reinterpret_cast<const f32x4_t*>(src + (k0 + j) * kstride)
-                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < KBATCH; ++j) {
+        const int64_t idx = src + (k0 + j) * kstride;
+        v[j] = (k0 + j >= ns) ? u32x4_t{0u, 0u, 0u, 0u}
+               : HALFP ? *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(o_part) + idx)
+                       : *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(o_part) + idx);
+      }
 #pragma unroll
-      for (int j = 0; j < KBATCH; ++j)
-        if (k0 + j < ns) acc += v[j] * wk[bi][k0 + j];
+      for (int j = 0; j < KBATCH; ++j) {
+        if (k0 + j >= ns) continue;
+        const float wj = wk[bi][k0 + j];
+        if constexpr (HALFP) {
+          const f16x8_t hv = __builtin_bit_cast(f16x8_t, v[j]);
+          acc0 += f32x4_t{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]} * wj;
+          acc1 += f32x4_t{(float)hv[4], (float)hv[5], (float)hv[6], (float)hv[7]} * wj;
+        } else {
+          acc0 += __builtin_bit_cast(f32x4_t, v[j]) * wj;
+        }
+      }
     }
-    *reinterpret_cast<f32x4_t*>(&olat[bi * dkv + 4 * c4]) = acc;
+    *reinterpret_cast<f32x4_t*>(&olat[bi * dkv + G * cg]) = acc0;
+    if constexpr (HALFP) *reinterpret_cast<f32x4_t*>(&olat[bi * dkv + G * cg + 4]) = acc1;
   }
   __syncthreads();
 
@@ -121,24 +136,28 @@ combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const float* __
 
 }  // namespace
 
-hipError_t launch_combine(const DecodeArgs& a, const float* lse_part, const float* o_part,
+hipError_t launch_combine(const DecodeArgs& a, const float* lse_part, const void* o_part, bool half_parts,
                           hipStream_t stream) {
   dim3 grid(a.H, (a.B + CB - 1) / CB);
   size_t smem = sizeof(float) * CB * a.dkv;
+#define MLA_COMBINE(WT, OT)                                                                                    \
+  if (half_parts)                                                                                              \
+    hipLaunchKernelGGL((combine_kernel<WT, OT, true>), grid, dim3(CTHREADS), smem, stream, a, lse_part, o_part); \
+  else                                                                                                         \
+    hipLaunchKernelGGL((combine_kernel<WT, OT, false>), grid, dim3(CTHREADS), smem, stream, a, lse_part, o_part);
   if (a.in_dt == MLA_BF16) {
-    if (a.out_dt == MLA_BF16)
-      hipLaunchKernelGGL((combine_kernel<MLA_BF16, MLA_BF16>), grid, dim3(CTHREADS), smem, stream, a,
-                         lse_part, o_part);
-    else
-      hipLaunchKernelGGL((combine_kernel<MLA_BF16, MLA_FP32>), grid, dim3(CTHREADS), smem, stream, a,
-                         lse_part, o_part);
+    if (a.out_dt == MLA_BF16) {
+      MLA_COMBINE(MLA_BF16, MLA_BF16)
+    } else {
+      MLA_COMBINE(MLA_BF16, MLA_FP32)
+    }
   } else {
-    if (a.out_dt == MLA_BF16)
-      hipLaunchKernelGGL((combine_kernel<MLA_FP32, MLA_BF16>), grid, dim3(CTHREADS), smem, stream, a,
-                         lse_part, o_part);
-    else
-      hipLaunchKernelGGL((combine_kernel<MLA_FP32, MLA_FP32>), grid, dim3(CTHREADS), smem, stream, a,
-                         lse_part, o_part);
+    if (a.out_dt == MLA_BF16) {
+      MLA_COMBINE(MLA_FP32, MLA_BF16)
+    } else {
+      MLA_COMBINE(MLA_FP32, MLA_FP32)
+    }
   }
+#undef MLA_COMBINE
   return hipGetLastError();
 }

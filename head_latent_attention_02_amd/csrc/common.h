@@ -1,5 +1,7 @@
 // Shared device helpers for the gfx950 kernels of libmla.
 #pragma once
+#include <type_traits>
+#include <utility>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -10,6 +12,17 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1: loop indices that
+// are compile-time constants, so register arrays are never indexed at run time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));

@@ -56,12 +56,12 @@ hipError_t launch_mfma_attention(const ExplicitArgs& a, const uint16_t* kn, cons
 
 // ---- decode ---------------------------------------------------------------
 // q~ is fp32 [B,H,dkv+dr] (SIMT) or bf16 (MFMA); lse_part fp32 [B,ns,H];
-// o_part fp32 [B,ns,H,dkv].
+// o_part [B,ns,H,dkv] fp32 (SIMT) or fp16 (MFMA).
 hipError_t launch_simt_absorb(const DecodeArgs& a, float* qt, hipStream_t stream);
 hipError_t launch_simt_splitkv(const DecodeArgs& a, const float* qt, float* lse_part,
                                float* o_part, hipStream_t stream);
 hipError_t launch_absorb_bf16(const DecodeArgs& a, uint16_t* qt, hipStream_t stream);
 hipError_t launch_mfma_splitkv(const DecodeArgs& a, const uint16_t* qt, float* lse_part,
-                               float* o_part, hipStream_t stream);
-hipError_t launch_combine(const DecodeArgs& a, const float* lse_part, const float* o_part,
+                               uint16_t* o_part, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs& a, const float* lse_part, const void* o_part, bool half_parts,
                           hipStream_t stream);

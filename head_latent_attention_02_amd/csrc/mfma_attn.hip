@@ -46,9 +46,6 @@
 //
 // Workgroups are dealt so that all query tiles of one head run on the same
 // XCD (its L2 holds that head's K/V), longest first.
-#include <type_traits>
-#include <utility>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -87,17 +84,6 @@ constexpr int N_PV_OPS = (KT / 16) * (DV / 32) * 2;   // PV MFMAs of a tile (key
 static_assert(LPW * 64 * NW == N_SLOTS + R_SLOTS + V_SLOTS, "tile chunks must split evenly over the waves");
 static_assert(N_SLOTS % (64 * NW) == 0 && R_SLOTS % (64 * NW) == 0, "a copy round must not straddle two parts");
 static_assert(LPW * 2 < 64, "vmcnt range");
-
-// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1: loop indices that
-// are compile-time constants, so register arrays are never indexed at run time.
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // MFMAs with the register files pinned: S^T = K Q^T with Q^T in AGPRs and the
 // result in VGPRs; O^T += V^T P^T with O^T in AGPRs.  Inline assembly keeps the

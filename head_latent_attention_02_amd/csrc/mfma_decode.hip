@@ -15,47 +15,106 @@ namespace {
 
 constexpr int DC = 512, DRP = 64, DLAT = 576, DN = 128, DV = 128;
 
+typedef short lds_v4s __attribute__((__vector_size__(4 * sizeof(short))));
+
+__device__ __forceinline__ bf16x8_t cat_bf16(lds_v4s lo, lds_v4s hi) {
+  u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
+  u32x4_t r = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
 // ---------------------------------------------------------------------------
 // q~[b,h,:512] = W_UK[h]^T q_nope[b,h] (fp32 accumulate, bf16 result) and
-// q~[b,h,512:] = R(q_pe[b,h], L_b - 1).  One block per (head, 16 sequences);
-// each thread owns 2 latent columns for the 16 sequences.
-constexpr int AB = 16;
+// q~[b,h,512:] = R(q_pe[b,h], L_b - 1).
+//
+// Per head this is a small GEMM, q~^T[c][b] = sum_n W[h*256+n][c] q_nope[b][n],
+// run on 16x16x32 bf16 MFMA.  A workgroup takes one head, 256 latent columns
+// and 64 sequences: it copies the head's 128 x 256 block of W (rows n, which
+// is c-contiguous in memory) into LDS and reads it back with the transposed
+// LDS read, which hands each lane 4 consecutive n of one column c; q_nope is
+// read from global memory in the same n order.  In a 32-wide k-step, k-slot
+// 8q4 + u stands for n = 4q4 + u (u < 4) or 16 + 4q4 + u - 4 (u >= 4) on both
+// operands.  Each lane ends with 4 consecutive latent columns of one sequence.
+constexpr int AM = 64;                  // sequences per workgroup
+constexpr int AN = 256;                 // latent columns per workgroup
+constexpr int AWSTR = AN * 2 + 8;       // LDS row stride in bytes (padded against bank conflicts)
+static_assert(DN * (AN / 8) % 256 == 0, "W block chunks must split evenly over the threads");
 __global__ void __launch_bounds__(256)
-absorb_bf16_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
-  __shared__ float qs[AB][DN];
-  const int h = blockIdx.x, b0 = blockIdx.y * AB;
-  const int nb = min(AB, a.B - b0);
-  const int tid = threadIdx.x;
-  const uint16_t* qn = static_cast<const uint16_t*>(a.q_nope);
+absorb_mfma_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
+  __shared__ __attribute__((aligned(16))) uint8_t Ws[DN * AWSTR];
+  const int h = blockIdx.x, c0 = blockIdx.y * AN, b0 = blockIdx.z * AM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, q4 = lane >> 4;
   const uint16_t* w = static_cast<const uint16_t*>(a.w);
-  for (int e = tid; e < AB * DN; e += 256) {
-    int bi = e / DN, n = e % DN;
-    qs[bi][n] = (bi < nb) ? bf16_bits_to_float(qn[((int64_t)(b0 + bi) * a.H + h) * DN + n]) : 0.f;
+  const uint16_t* qn = static_cast<const uint16_t*>(a.q_nope);
+  // W rows h*256 + n, columns c0 .. c0+255 -> LDS row n (16-byte chunks; all
+  // loads are issued before the first LDS write)
+  constexpr int WCH = DN * (AN / 8) / 256;          // chunks per thread (16)
+  u32x4_t wv[WCH];
+#pragma unroll
+  for (int it = 0; it < WCH; ++it) {
+    const int i = tid + 256 * it, n = i / (AN / 8), ch = i % (AN / 8);
+    wv[it] = *reinterpret_cast<const u32x4_t*>(w + ((int64_t)h * (DN + DV) + n) * DC + c0 + 8 * ch);
   }
-  __syncthreads();
-  float acc[AB][2];
 #pragma unroll
-  for (int bi = 0; bi < AB; ++bi) acc[bi][0] = acc[bi][1] = 0.f;
-  const uint16_t* wrow = w + (int64_t)h * (DN + DV) * DC + 2 * tid;
-  for (int n = 0; n < DN; ++n) {
-    uint32_t w2 = *reinterpret_cast<const uint32_t*>(wrow + (int64_t)n * DC);
-    float w0 = bf16_bits_to_float((uint16_t)(w2 & 0xffff)), w1 = bf16_bits_to_float((uint16_t)(w2 >> 16));
+  for (int it = 0; it < WCH; ++it) {
+    const int i = tid + 256 * it, n = i / (AN / 8), ch = i % (AN / 8);
+    *reinterpret_cast<u32x2_t*>(Ws + n * AWSTR + 16 * ch) = u32x2_t{wv[it][0], wv[it][1]};
+    *reinterpret_cast<u32x2_t*>(Ws + n * AWSTR + 16 * ch + 8) = u32x2_t{wv[it][2], wv[it][3]};
+  }
+  // q_nope^T as the B operand: lane holds sequence b0 + 16 mb + l16 (rows past
+  // the batch read the last sequence and are not stored)
+  bf16x8_t qb[AM / 16][DN / 32];
 #pragma unroll
-    for (int bi = 0; bi < AB; ++bi) {
-      float q = qs[bi][n];
-      acc[bi][0] += q * w0;
-      acc[bi][1] += q * w1;
+  for (int mb = 0; mb < AM / 16; ++mb) {
+    const int bc = min(b0 + 16 * mb + l16, a.B - 1);
+    const uint16_t* row = qn + ((int64_t)bc * a.H + h) * DN;
+#pragma unroll
+    for (int ks = 0; ks < DN / 32; ++ks) {
+      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(row + 32 * ks + 4 * q4);
+      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(row + 32 * ks + 16 + 4 * q4);
+      qb[mb][ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
     }
   }
+  __syncthreads();
+  // wave w: latent columns c0 + 64w .. +63 (4 blocks of 16) for all 64 sequences
+  f32x4_t acc[4][AM / 16];
 #pragma unroll
-  for (int bi = 0; bi < AB; ++bi)
-    if (bi < nb)
-      *reinterpret_cast<uint32_t*>(qt + ((int64_t)(b0 + bi) * a.H + h) * DLAT + 2 * tid) =
-          pack_bf16x2(acc[bi][0], acc[bi][1]);
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < AM / 16; ++mb) acc[nb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < DN / 32; ++ks) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      // rows n = 32ks + 4q4 + l16/4 (+16), 4 columns from 64w + 16nb + 4(l16&3):
+      // transposed, lane l16 receives column 64w + 16nb + l16
+      const uint8_t* src = Ws + (32 * ks + 4 * q4 + (l16 >> 2)) * AWSTR + 2 * (64 * wave + 16 * nb + 4 * (l16 & 3));
+      const lds_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(src));
+      const lds_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(src + 16 * AWSTR));
+      const bf16x8_t wf = cat_bf16(lo, hi);
+#pragma unroll
+      for (int mb = 0; mb < AM / 16; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, qb[mb][ks], acc[nb][mb], 0, 0, 0);
+    }
+  }
+  // lane holds q~^T[c = c0 + 64w + 16nb + 4q4 + r][b = b0 + 16mb + l16]
+#pragma unroll
+  for (int mb = 0; mb < AM / 16; ++mb) {
+    const int b = b0 + 16 * mb + l16;
+    if (b >= a.B) continue;
+    uint16_t* dst = qt + ((int64_t)b * a.H + h) * DLAT + c0 + 64 * wave + 4 * q4;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      *reinterpret_cast<u32x2_t*>(dst + 16 * nb) =
+          u32x2_t{pack_bf16x2(acc[nb][mb][0], acc[nb][mb][1]), pack_bf16x2(acc[nb][mb][2], acc[nb][mb][3])};
+  }
   // RoPE band of the query at the new token's position
+  if (blockIdx.y != 0) return;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q_pe);
-  for (int e = tid; e < nb * 32; e += 256) {
-    int bi = e >> 5, m = e & 31, b = b0 + bi;
+  for (int e = tid; e < AM * 32; e += 256) {
+    const int b = b0 + (e >> 5), m = e & 31;
+    if (b >= a.B) break;
     int L = min(max(a.cache_len[b], 0), a.max_len);
     double pos = (double)(L > 0 ? L - 1 : 0);
     double theta = exp(-2.0 * (double)m / (double)DRP * log((double)a.rope_base));
@@ -115,8 +174,6 @@ constexpr int KS = DLAT / 32;            // score k-steps (18)
 constexpr int SPF = 4;                   // score fragments read ahead of their MFMAs
 constexpr float RESCALE_TAU = 8.f;       // log2 units
 
-typedef short lds_v4s __attribute__((__vector_size__(4 * sizeof(short))));
-
 // 16-byte chunk swizzle of a tile row (measured free of LDS bank conflicts for
 // both the row reads and the transposed reads below)
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
@@ -143,12 +200,6 @@ __device__ __forceinline__ void mfma_agpr_zero(f32x4_t& acc) {
   asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
 }
 
-__device__ __forceinline__ bf16x8_t cat_bf16(lds_v4s lo, lds_v4s hi) {
-  u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
-  u32x4_t r = {a[0], a[1], b[0], b[1]};
-  return __builtin_bit_cast(bf16x8_t, r);
-}
-
 // max / sum over the 4 lanes l16 + 16 q4 (q4 = 0..3) that share a head
 __device__ __forceinline__ float quad_max(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -164,7 +215,7 @@ __device__ __forceinline__ float quad_sum(float v) {
 template <int NHT>       // head groups of 16 (H = 16 NHT)
 __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __restrict__ lse_part,
-                    float* __restrict__ o_part) {
+                    uint16_t* __restrict__ o_part) {
   __shared__ __attribute__((aligned(16))) uint16_t Cs[NBUF][TT * DLAT];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[MAXG * 16 * TT];   // P^T [h][k-slot]
   __shared__ float linv_s[MAXG * 16];   // 1 / softmax denominator at the end
@@ -424,7 +475,8 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
   __syncthreads();
   mfma_drain();
   // lane holds O^T[d = 16 (8 wave + i) + 4q4 + r][h = 16g + l16]
-  float* dst = o_part + ((int64_t)b * a.n_splits + k) * a.H * DC + 128 * wave + 4 * q4;
+  // (fp16: the normalised partial is a convex combination of cache rows)
+  uint16_t* dst = o_part + ((int64_t)b * a.n_splits + k) * a.H * DC + 128 * wave + 4 * q4;
 #pragma unroll
   for (int g = 0; g < NHT; ++g) {
     const int hh = 16 * g + l16;
@@ -432,7 +484,8 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
 #pragma unroll
     for (int i = 0; i < DT_W; ++i) {
       agpr_fence(oacc[i][g]);
-      *reinterpret_cast<f32x4_t*>(dst + (int64_t)hh * DC + 16 * i) = oacc[i][g] * inv;
+      const f32x4_t v = oacc[i][g] * inv;
+      *reinterpret_cast<u32x2_t*>(dst + (int64_t)hh * DC + 16 * i) = u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
     }
   }
 }
@@ -440,12 +493,13 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
 }  // namespace
 
 hipError_t launch_absorb_bf16(const DecodeArgs& a, uint16_t* qt, hipStream_t stream) {
-  dim3 grid(a.H, (a.B + AB - 1) / AB);
-  hipLaunchKernelGGL(absorb_bf16_kernel, grid, dim3(256), 0, stream, a, qt);
+  if (a.B == 0) return hipSuccess;
+  dim3 grid(a.H, DC / AN, (a.B + AM - 1) / AM);
+  hipLaunchKernelGGL(absorb_mfma_kernel, grid, dim3(256), 0, stream, a, qt);
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_splitkv(const DecodeArgs& a, const uint16_t* qt, float* lse_part, float* o_part,
+hipError_t launch_mfma_splitkv(const DecodeArgs& a, const uint16_t* qt, float* lse_part, uint16_t* o_part,
                                hipStream_t stream) {
   dim3 grid(a.n_splits, a.B);
   switch (a.H >> 4) {

@@ -204,7 +204,8 @@ mla_status make_decode_plan(const mla_decode_desc* d, DecodePlan* plan) {
   size_t off = 0;
   p.off_qt = off;    off = align_up(off + p.qt_elem * B * H * dlat);
   p.off_lse = off;   off = align_up(off + 4 * B * ns * H);
-  p.off_opart = off; off = align_up(off + 4 * B * ns * H * (size_t)d->d_kv);
+  // the MFMA path keeps its partials in fp16 (their values lie in the cache's range)
+  p.off_opart = off; off = align_up(off + p.qt_elem * B * ns * H * (size_t)d->d_kv);
   p.total = off;
   *plan = p;
   return MLA_OK;
@@ -347,7 +348,7 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc, const void* q_nope, 
   a.q_nope = q_nope; a.q_pe = q_pe; a.cache = kv_cache; a.w = w_kv_b; a.cache_len = cache_len;
   a.out = out; a.lse = lse;
   float* lse_part = reinterpret_cast<float*>(ws + p.off_lse);
-  float* o_part = reinterpret_cast<float*>(ws + p.off_opart);
+  void* o_part = ws + p.off_opart;
   hipError_t e;
   if (p.mfma) {
     uint16_t* qt = reinterpret_cast<uint16_t*>(ws + p.off_qt);
@@ -358,7 +359,7 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc, const void* q_nope, 
     if (e != hipSuccess) return hip_fail(e, "query absorption");
     {
       TimedLaunch t("mfma_split_kv", s);
-      e = launch_mfma_splitkv(a, qt, lse_part, o_part, s);
+      e = launch_mfma_splitkv(a, qt, lse_part, static_cast<uint16_t*>(o_part), s);
     }
     if (e != hipSuccess) return hip_fail(e, "mfma split-KV attention");
   } else {
@@ -370,13 +371,13 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc, const void* q_nope, 
     if (e != hipSuccess) return hip_fail(e, "query absorption");
     {
       TimedLaunch t("simt_split_kv", s);
-      e = launch_simt_splitkv(a, qt, lse_part, o_part, s);
+      e = launch_simt_splitkv(a, qt, lse_part, static_cast<float*>(o_part), s);
     }
     if (e != hipSuccess) return hip_fail(e, "simt split-KV attention");
   }
   {
     TimedLaunch t("lse_combine", s);
-    e = launch_combine(a, lse_part, o_part, s);
+    e = launch_combine(a, lse_part, o_part, p.mfma, s);
   }
   if (e != hipSuccess) return hip_fail(e, "LSE combine");
   return MLA_OK;

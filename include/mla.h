@@ -194,8 +194,11 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc,
  * offsets[4]):
  *   [0] q~        [B, H, d_kv+d_rope]  (bf16 on the MFMA path, fp32 on SIMT)
  *   [1] lse_part  fp32 [B, n_splits, H]
- *   [2] o_part    fp32 [B, n_splits, H, d_kv]   (normalised within the chunk)
- *   [3] bytes per q~ element (2 or 4) */
+ *   [2] o_part    [B, n_splits, H, d_kv]   (normalised within the chunk):
+ *                 fp16 on the MFMA path, fp32 on SIMT.  Each row is a convex
+ *                 combination of cache rows, so on the MFMA path the cache's
+ *                 latent values must lie within fp16 range (|x| < 65504).
+ *   [3] bytes per q~ and per o_part element (2 on the MFMA path, 4 on SIMT) */
 mla_status mla_decode_absorbed_workspace_layout(const mla_decode_desc* desc,
                                                 size_t offsets[4]);
 

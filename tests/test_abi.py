@@ -153,7 +153,7 @@ def test_decode_workspace_and_layout():
     ws = mla.mla_decode_absorbed_workspace_size(d)
     q, l, o, esz = mla.mla_decode_absorbed_workspace_layout(d)
     assert esz == 2 and q < l < o < ws
-    assert ws - o >= 64 * 16 * 128 * 512 * 4
+    assert ws - o >= 64 * 16 * 128 * 512 * esz
     d2 = _dec_desc(in_dtype=mla.MLA_FP32)
     assert mla.mla_decode_absorbed_workspace_layout(d2)[3] == 4
 
