@@ -13,13 +13,14 @@
 // Outputs (fp16): Kn [B, H, s_pad, 128] and V^T [B, H, 128, s_pad] (key index
 // fastest, the layout the attention kernel's P.V product reads).
 //
-// Persistent kernel, one workgroup of 4 waves per CU (one wave per SIMD, the
-// whole register file each).  A tile is 256 latent rows x the 256 output
-// columns of one head; waves 0-1 produce its K_nope half (W rows as the A
-// operand, so each lane ends with 4 consecutive features of one key) and
-// waves 2-3 its V half (latent rows as the A operand, so each lane ends with
-// 4 consecutive keys of one feature), 128 x 128 per wave on 32x32x16 MFMA
-// with the accumulators in AGPRs.  The reduction over the 512 latent columns
+// Persistent kernel, one workgroup of 8 waves per CU (two waves per SIMD:
+// while one is held issuing its tile copies, the other keeps the SIMD's
+// matrix unit busy).  A tile is 256 latent rows x the 256 output columns of
+// one head; waves 0-3 produce its K_nope half (W rows as the A operand, so
+// each lane ends with 4 consecutive features of one key) and waves 4-7 its V
+// half (latent rows as the A operand, so each lane ends with 4 consecutive
+// keys of one feature), 128 x 64 per wave on 32x32x16 MFMA with the
+// accumulators in AGPRs.  The reduction over the 512 latent columns
 // streams in steps of 32 through a ring of 4 LDS stages (16 KB of latent
 // rows + 16 KB of W rows each) filled by direct buffer->LDS loads; the ring
 // runs across tile boundaries, so the next tile's first steps are in flight
@@ -37,13 +38,14 @@ constexpr int TK = 32;           // reduction step
 constexpr int DKV = 512;
 constexpr int NKS = DKV / TK;    // reduction steps per tile (16)
 constexpr int NSTAGE = 4;        // LDS ring depth
-constexpr int NTHREADS = 256;
+constexpr int NTHREADS = 512;
 constexpr int REG_BYTES = TJ * TK * 2;       // one operand region of a stage (16 KB)
 constexpr int STAGE_BYTES = 2 * REG_BYTES;   // latent rows then W rows
-constexpr int LOADS = 2 * REG_BYTES / 16 / NTHREADS;   // 16-byte copies per lane per step (8)
+constexpr int LOADS = 2 * REG_BYTES / 16 / NTHREADS;   // 16-byte copies per lane per step (4)
+constexpr int COPY_ROWS = NTHREADS / 4;                 // 64-byte rows one copy instruction fills (128)
 
 // acc += A B on the 32x32x16 bf16 MFMA with the accumulator held in AGPRs
-// (the 256 accumulator registers fill the AGPR file; operands stay in VGPRs).
+// (the 128 accumulator registers stay in AGPRs; operands stay in VGPRs).
 __device__ __forceinline__ void mfma32_agpr(f32x16_t& acc, bf16x8_t a, bf16x8_t b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
@@ -74,7 +76,7 @@ __device__ __forceinline__ void tile_coords(int tile, int n_jt, bool xcd_deal, i
   }
 }
 
-__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w,
                    uint16_t* __restrict__ kn, uint16_t* __restrict__ vt, int B, int H, int Skv,
                    int s_vis, int s_pad, int n_jt, int n_tiles, int xcd_deal) {
@@ -83,8 +85,9 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hb = lane >> 5;
-  const int part = wave >> 1;          // 0: K_nope columns, 1: V columns
-  const int jq = wave & 1;             // 128-row half of the tile
+  const int part = wave >> 2;          // 0: K_nope columns, 1: V columns
+  const int jq = (wave >> 1) & 1;      // 128-row half of the A side
+  const int nh = wave & 1;             // 64-row half of the B side
   const int G = gridDim.x;
   const int my_tiles = (n_tiles - (int)blockIdx.x + G - 1) / G;
   const int total_steps = my_tiles * NKS;
@@ -92,8 +95,8 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
   // Stage layout: rows of 32 bf16 (64 bytes = 4 chunks of 16 bytes); chunk c
   // of row r sits at chunk c ^ ((r >> 2) & 3), which spreads the 16 rows that
   // a 16-lane group reads over all 64 banks.
-  // Copies: lane instruction i covers slot s = 256 i + tid of a region, i.e.
-  // row 64 i + tid/4, physical chunk tid & 3 (the swizzle only depends on
+  // Copies: lane instruction i covers slot s = 512 i + tid of a region, i.e.
+  // row 128 i + tid/4, physical chunk tid & 3 (the swizzle only depends on
   // tid, so one per-lane offset serves every row block, step and tile).
   const int v_lane = (tid >> 2) * (DKV * 2) + (((tid & 3) ^ ((tid >> 4) & 3)) * 16);
   const uint32_t ls_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&Ls[0];
@@ -106,7 +109,7 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
   const int frag_off1 = l32 * (TK * 2) + ((2 + hb) ^ sw) * 16;   // kk = 1
   // first (A) and second (B) operand regions of this wave, byte offsets in a stage
   const int a_rows = (part == 0) ? (REG_BYTES + 0) : (jq * 128 * TK * 2);
-  const int b_rows = (part == 0) ? (jq * 128 * TK * 2) : (REG_BYTES + 128 * TK * 2);
+  const int b_rows = (part == 0) ? ((jq * 128 + nh * 64) * TK * 2) : (REG_BYTES + (128 + nh * 64) * TK * 2);
 
   // issue the copies of global reduction step g (tile g / NKS, step g % NKS)
   auto issue_step = [&](int g) {
@@ -121,13 +124,13 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
     const uint32_t dst = ls_lds + (uint32_t)((g % NSTAGE) * STAGE_BYTES) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
 #pragma unroll
     for (int i = 0; i < LOADS / 2; ++i) {
-      const int so = __builtin_amdgcn_readfirstlane(i * 64 * (DKV * 2) + ks * (TK * 2));
-      lds_dma_b128(ra, dst + i * 4096, v_lane, so);
-      lds_dma_b128(rb, dst + REG_BYTES + i * 4096, v_lane, so);
+      const int so = __builtin_amdgcn_readfirstlane(i * COPY_ROWS * (DKV * 2) + ks * (TK * 2));
+      lds_dma_b128(ra, dst + i * (NTHREADS * 16), v_lane, so);
+      lds_dma_b128(rb, dst + REG_BYTES + i * (NTHREADS * 16), v_lane, so);
     }
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
   const int ahead = min(NSTAGE - 1, total_steps);
   for (int g = 0; g < ahead; ++g) issue_step(g);
 
@@ -148,23 +151,23 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int fo = kk ? frag_off1 : frag_off0;
-        bf16x8_t fa[4], fb[4];
+        bf16x8_t fa[4], fb[2];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
           fa[x] = *reinterpret_cast<const bf16x8_t*>(st + a_rows + x * 32 * (TK * 2) + fo);
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
+        for (int y = 0; y < 2; ++y)
           fb[y] = *reinterpret_cast<const bf16x8_t*>(st + b_rows + y * 32 * (TK * 2) + fo);
         if (kk == 0 && ks == 0) {
 #pragma unroll
           for (int x = 0; x < 4; ++x)
 #pragma unroll
-            for (int y = 0; y < 4; ++y) mfma32_agpr_first(acc[x][y], fa[x], fb[y]);
+            for (int y = 0; y < 2; ++y) mfma32_agpr_first(acc[x][y], fa[x], fb[y]);
         } else {
 #pragma unroll
           for (int x = 0; x < 4; ++x)
 #pragma unroll
-            for (int y = 0; y < 4; ++y) mfma32_agpr(acc[x][y], fa[x], fb[y]);
+            for (int y = 0; y < 2; ++y) mfma32_agpr(acc[x][y], fa[x], fb[y]);
         }
       }
     }
@@ -181,7 +184,7 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
+      for (int y = 0; y < 2; ++y) {
         agpr_fence(acc[x][y]);
         uint32_t wd[4][2];
 #pragma unroll
@@ -200,12 +203,12 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
           }
           const int o = x * 32 + 16 * pp + 8 * hb;    // first of the lane's 8 outputs in the block's rows
           if (part == 0) {
-            // D[n][j]: n = o .. o+7 (features), j = jq*128 + y*32 + l32
-            uint16_t* dst = kn + ((int64_t)bh * s_pad + j0 + jq * 128 + y * 32 + l32) * 128 + o;
+            // D[n][j]: n = o .. o+7 (features), j = jq*128 + nh*64 + y*32 + l32
+            uint16_t* dst = kn + ((int64_t)bh * s_pad + j0 + jq * 128 + nh * 64 + y * 32 + l32) * 128 + o;
             *reinterpret_cast<u32x4_t*>(dst) = chunk;
           } else {
-            // D[j][n]: j = jq*128 + o .. +7 (keys), n = y*32 + l32
-            uint16_t* dst = vt + ((int64_t)bh * 128 + y * 32 + l32) * s_pad + j0 + jq * 128 + o;
+            // D[j][n]: j = jq*128 + o .. +7 (keys), n = nh*64 + y*32 + l32
+            uint16_t* dst = vt + ((int64_t)bh * 128 + nh * 64 + y * 32 + l32) * s_pad + j0 + jq * 128 + o;
             *reinterpret_cast<u32x4_t*>(dst) = chunk;
           }
         }
