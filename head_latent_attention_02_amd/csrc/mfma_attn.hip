@@ -114,13 +114,6 @@ __device__ __forceinline__ void agpr_fence(f32x16_t& acc) { asm volatile("" : "+
 // v is held in AGPRs from here on (Q^T operand)
 __device__ __forceinline__ void agpr_fence(f16x8_t& v) { asm volatile("s_nop 4" : "+a"(v)); }
 
-// max of three floats in one instruction (fmaxf would first quiet each input)
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 // Chunk swizzle (stored chunk = logical chunk ^ swizzle(row)), measured free of
 // LDS bank conflicts for the 16-byte reads below, where 16 consecutive lanes
 // read 16 consecutive 128-byte rows (two rows per bank sweep, so 8 distinct

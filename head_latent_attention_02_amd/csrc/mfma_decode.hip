@@ -377,7 +377,7 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
   };
 
   // Softmax of the tile whose scores are in sacc (first token tt) against the
-  // pass's reference max m_ref: publishes P^T = exp2(s - m_ref) in bf16 and
+  // pass's reference max m_ref: publishes P^T = exp2((s - m_ref) c_log2) in bf16 and
   // adds the row sums to l_run.  The reference is the first tile's max (or,
   // on a second pass, the chunk's max); a later tile whose max exceeds it by
   // more than tau flags the pass for a redo instead of rescaling the
@@ -396,30 +396,33 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
     bool exceeded = false;
 #pragma unroll
     for (int hg = 0; hg < 2; ++hg) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sacc[st][hg][r] *= c_log2;
-          mx = fmaxf(mx, sacc[st][hg][r]);
-        }
-      mx = quad_max(mx);
-      m_max[hg] = fmaxf(m_max[hg], mx);
+      // max of the raw scores (c_log2 > 0 keeps their order), then over the 4
+      // lanes of the head
+      float mx = max3(max3(sacc[0][hg][0], sacc[0][hg][1], sacc[0][hg][2]),
+                      max3(sacc[0][hg][3], sacc[1][hg][0], sacc[1][hg][1]), max2(sacc[1][hg][2], sacc[1][hg][3]));
+      {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = max2(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+      }
+      m_max[hg] = max2(m_max[hg], mx);
       if (m_ref[hg] == -INFINITY) m_ref[hg] = mx;        // first tile of the first pass
-      else exceeded |= mx > m_ref[hg] + RESCALE_TAU;
+      else exceeded |= (mx - m_ref[hg]) * c_log2 > RESCALE_TAU;
+      const float mc = (m_ref[hg] == -INFINITY) ? 0.f : m_ref[hg] * c_log2;
       const int h = 16 * (hg0 + hg) + l16;
       bf16x8_t pf;
-      float rs = 0.f;
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float pv = fast_exp2(sacc[st][hg][r] - m_ref[hg]);
-          rs += pv;
+          const float pv = fast_exp2(fmaf(sacc[st][hg][r], c_log2, -mc));
+          if (r & 1) rs1 += pv;
+          else rs0 += pv;
           pf[4 * st + r] = (__bf16)pv;      // round to nearest even
         }
-      l_run[hg] += rs;
+      l_run[hg] += rs0 + rs1;
       *reinterpret_cast<bf16x8_t*>(&Ps[h * TT + 8 * q4]) = pf;
     }
     if (__ballot(exceeded) != 0ull && lane == 0) redo_s = 1;
@@ -468,7 +471,7 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
       if (q4 == 0) {
         linv_s[h] = (l > 0.f) ? 1.f / l : 0.f;
         lse_part[((int64_t)b * a.n_splits + k) * a.H + h] =
-            (l > 0.f) ? (m_ref[hg] + __log2f(l)) * MLA_LN2 : -INFINITY;
+            (l > 0.f) ? (m_ref[hg] * c_log2 + __log2f(l)) * MLA_LN2 : -INFINITY;
       }
     }
   }
