@@ -57,13 +57,13 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "3402e2e974c8ba6a", "fetch_kib": 346245.6, "write_kib": 292863.8,
+    "mfma_attention": {"digest": "08647e82ea6065d0", "fetch_kib": 348323.8, "write_kib": 292863.3,
                       "fetch_factor": 0.50003, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "3b2b11cb5d03cd61", "fetch_kib": 100886.2, "write_kib": 272884.8,
+    "mfma_up_projection": {"digest": "348ef7db262673c7", "fetch_kib": 100650.3, "write_kib": 273453.0,
                           "fetch_factor": 0.50003, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "eec60be07a2a9b05", "fetch_kib": 1216625.7, "write_kib": 262656.0,
+    "mfma_split_kv": {"digest": "fd3bfe849c65c4f2", "fetch_kib": 1216645.1, "write_kib": 131585.6,
                      "fetch_factor": 0.50003, "write_factor": 1.0},
-    "lse_combine": {"digest": "ce99bf396e02953e", "fetch_kib": 149567.2, "write_kib": 4357.6,
+    "lse_combine": {"digest": "bcf1eba073225179", "fetch_kib": 83789.8, "write_kib": 4354.4,
                    "fetch_factor": 0.50003, "write_factor": 1.0},
 }
 
