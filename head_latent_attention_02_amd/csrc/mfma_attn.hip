@@ -103,10 +103,12 @@ __device__ __forceinline__ void mfma_pv(f32x16_t& o, f16x8_t v, f16x8_t p) {
 __device__ __forceinline__ void mfma_pv_nop(f32x16_t& o, f16x8_t v, f16x8_t p) {   // after fresh P
   asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
 }
-// zeroes o in place (the registers it already holds)
+// zeroes o in place (the registers it already holds); the result is final
+// when the statement ends, since the compiler may copy it right after
 __device__ __forceinline__ void mfma_zero(f32x16_t& o) {
   const f16x8_t z = {};
-  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0" : "+a"(o) : "v"(z));
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o) : "v"(z));
 }
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::); }
 // compiler-generated reads of acc cannot move above this point

@@ -358,3 +358,21 @@ def test_explicit_logit_jumps(mla):
     ro, rl = _oracle_explicit(cfg, x)
     _compare(o, ro, True, "explicit jumps out")
     _compare_lse(l, rl, True, "explicit jumps", magnitude_scaled=True)
+
+
+def test_explicit_mixed_batch_redo(mla):
+    # Two sequences, 48 heads, a ragged last query tile: in batch 0 the logit
+    # jumps force the second softmax pass on every head, batch 1 is ordinary.
+    cfg = I.small_explicit("mixed_redo", batch=2, s_q=520, s_kv=520, n_heads=48, d_kv=512, d_nope=128, d_rope=64,
+                           d_v=128, dtype="bf16", seed=303)
+    x = I.make_explicit_inputs(cfg)
+    S = cfg.s_q
+    x["q_nope"][0] = 0
+    qb = I.bf16_bits_to_f32(I.round_to_bf16_bits(_unit_rotated(np.arange(S))))
+    x["q_pe"][0] = np.repeat(qb[:, None, :], cfg.n_heads, axis=1)
+    lam = 76.0 * np.minimum(np.arange(S) // 64, 4) - 50.0 * np.maximum(np.arange(S) // 64 - 4, 0)
+    x["k_pe"][0] = I.bf16_bits_to_f32(I.round_to_bf16_bits(_unit_rotated(np.arange(S)) * lam[:, None]))
+    o, l, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA)
+    ro, rl = _oracle_explicit(cfg, x)
+    _compare(o, ro, True, "mixed-redo out")
+    _compare_lse(l, rl, True, "mixed-redo", magnitude_scaled=True)
