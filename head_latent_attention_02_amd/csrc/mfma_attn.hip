@@ -34,9 +34,11 @@
 //
 // Schedule.  Iteration T issues, as one MFMA stream, the S of tile T+1 (48
 // MFMAs) and the PV of tile T (32 MFMAs), and spreads the softmax of tile T
-// over that stream in 16 slices (one every 4 MFMAs): the matrix unit and the
-// vector ALU of the SIMD work at the same time inside the one wave.  The
-// softmax of a key step is done before the PV MFMAs of that step.
+// over that stream in 72 small units, one after each of the first 72 MFMAs
+// (an exponential, a row-sum add and every other step a 3-way max, or the
+// fp16 packing of 8 probabilities): the matrix unit and the vector ALU of the
+// SIMD work at the same time inside the one wave.  The softmax of a key step
+// is done before the PV MFMAs of that step.
 //
 // Softmax reference.  A row's reference max is the max of its first tile
 // with a visible key; P = exp2(s - ref) stays below 2^tau in fp16.  A tile
