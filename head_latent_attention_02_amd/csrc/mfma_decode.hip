@@ -139,9 +139,8 @@ absorb_mfma_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
 //
 //   scores: wave w owns head groups 2w and 2w+1 (32 heads, q~ in VGPRs) and
 //     computes S^T[t][h] = C[t][:576] . q~[h] on 16x16x32 bf16 MFMA, then the
-//     online softmax in the log2 domain (each lane owns one head of each
-//     group); P^T (bf16) and, when a head's reference max moved, its rescale
-//     factor go to LDS;
+//     softmax in the log2 domain (each lane owns one head of each group);
+//     P^T (bf16) goes to LDS;
 //   values: wave w owns latent columns 128w .. 128w+127 of every head and
 //     accumulates O^T[d][h] += C^T[d][t] P^T[t][h] (16x16x32 bf16 MFMA,
 //     accumulators in AGPRs).
@@ -149,17 +148,25 @@ absorb_mfma_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
 // Splitting the value product by latent column means the tile's 512 value
 // columns are read from LDS once per tile in total (with the transposed LDS
 // read, ds_read_b64_tr_b16), and P^T for all heads is only 8 KB; the score
-// product reads the tile once per 32 heads.  While a tile is computed, the
-// next three are in flight, so the cache stream does not wait for the MFMAs.
+// product reads the tile once per 32 heads.
+//
+// Schedule: iteration T issues the score MFMAs of tile T+1 and then the value
+// MFMAs of tile T as one instruction stream, with the softmax of tile T+1 cut
+// into 24 small units placed between the value MFMAs, so the vector ALU works
+// while the matrix unit does.  P^T is double-buffered in LDS (tile T's is read
+// while tile T+1's is written), which leaves one barrier per tile.
+//
+// Softmax reference: a head's reference is the max of its first tile;
+// P = exp2((s - ref) log2(e) scale) stays below 2^8.  A tile whose max
+// exceeds the reference by more than 8 (log2 units) flags the pass, and the
+// workgroup then recomputes its chunk from the chunk max seen by the first
+// pass, so the accumulators are only ever touched by MFMAs.
 //
 // The score result layout (token rows 4q4 + r of each 16-token half) is kept
 // as the k-slot order of the value product: P^T slot 8q4 + u of a head is
 // token 4q4 + u (u < 4) or 16 + 4q4 + u - 4 (u >= 4), and the transposed
 // reads of C^T use the same permutation, so a score lane writes its 8
 // probabilities as one 16-byte chunk that a value lane reads back unchanged.
-// The reference max of a head only moves when a tile exceeds it by more than
-// 8 (log2 units), which skips the accumulator rescale on most tiles; the
-// result is exact either way because l and O share the same reference.
 // Inside a tile row the 16-byte chunks are XOR-swizzled by row&7, measured
 // free of LDS bank conflicts for both the row reads and the transposed reads.
 constexpr int TT = 32;                   // tokens per tile
@@ -216,16 +223,15 @@ template <int NHT>       // head groups of 16 (H = 16 NHT)
 __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __restrict__ lse_part,
                     uint16_t* __restrict__ o_part) {
+  // 4 x 36 KB tile ring + 2 x 8 KB of P^T: the whole 160 KB.  The end-of-pass
+  // flags and the final 1/l go through ring memory once the ring is idle.
   __shared__ __attribute__((aligned(16))) uint16_t Cs[NBUF][TT * DLAT];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[MAXG * 16 * TT];   // P^T [h][k-slot]
-  __shared__ float linv_s[MAXG * 16];   // 1 / softmax denominator at the end
-  __shared__ int redo_s;                // a reference max was exceeded by more than tau
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[2][MAXG * 16 * TT];   // P^T [h][k-slot]
 
   const int k = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int hg0 = 2 * wave;                     // first head group of this wave's scores
-  const bool score_wave = hg0 < NHT;
 
   const int L = min(max(a.cache_len[b], 0), a.max_len);
   const int csz = (L + a.n_splits - 1) / a.n_splits;
@@ -315,9 +321,21 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
     for (int m = 0; m < 4; ++m)
       voff[m] = ra * DLAT + 8 * (2 * (m ^ (sa >> 1)) + (x ^ (sa & 1))) + w4 + 128 * wave;
   }
+  auto vfrag = [&](const uint16_t* Cv, int i) -> bf16x8_t {    // C^T fragment of d-tile 8 wave + i
+    const int off = voff[i & 3] + 64 * (i >> 2);
+    lds_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(Cv + off));
+    lds_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(Cv + off + 16 * DLAT));
+    return cat_bf16(lo, hi);
+  };
+  auto pfrag = [&](const uint16_t* Pv, int g) -> bf16x8_t {    // P^T fragment of head group g
+    return *reinterpret_cast<const bf16x8_t*>(&Pv[(16 * g + l16) * TT + 8 * q4]);
+  };
 
   const float c_log2 = a.scale * MLA_LOG2E;
+  // m_ref / m_max in score units; mc = m_ref * c_log2 (0 while unset)
   float m_ref[2] = {-INFINITY, -INFINITY}, m_max[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float mc[2] = {0.f, 0.f};
+  bool exceeded = false;
   f32x4_t oacc[DT_W][NHT];                      // [d-tile of this wave][head group]
   f32x4_t sacc[2][2];                           // [token half][head group]
 
@@ -343,136 +361,154 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
     }
   };
 
-  // Value product of the tile in Cv: O^T for this wave's 128 latent columns
-  // and every head group, 8 NHT MFMAs.  C^T fragments are read for half of
-  // the d-tiles at a time, P^T fragments one head group ahead.
-  auto value_phase = [&](const uint16_t* Cv) {
-    bf16x8_t cf[DT_W / 2];
-    bf16x8_t pg[2];
-    auto load_cf = [&](int half) {
+  // Softmax of the tile whose scores are in sacc (first token tt), against
+  // the pass's reference: P^T = exp2((s - m_ref) c_log2) in bf16 to Pn, row
+  // sums to l_run.  The reference is the row max of the first tile (or, on a
+  // second pass, the chunk's max); a later tile whose max exceeds it by more
+  // than tau flags the pass for a redo, so the accumulators are only ever
+  // touched by MFMAs and P stays below 2^tau.  Unit j of head group hg is
+  // 12 hg + j; the units run between the value MFMAs of the previous tile.
+  float sm8[2], rs[2], pv_prev[2];
+  bf16x8_t pf[2];
+  auto softmax_unit = [&](auto j_c, int tt, uint16_t* Pn) __attribute__((always_inline)) {
+    constexpr int jj = decltype(j_c)::value, hg = jj / 12, j = jj % 12;
+    if constexpr (j == 0) {
+      if (hg == 0 && tt + TT > t1) {      // tail tile: tokens past the chunk end get no weight
 #pragma unroll
-      for (int j = 0; j < DT_W / 2; ++j) {
-        const int i = half * (DT_W / 2) + j;
-        const int off = voff[i & 3] + 64 * (i >> 2);
-        lds_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(Cv + off));
-        lds_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS lds_v4s*)(Cv + off + 16 * DLAT));
-        cf[j] = cat_bf16(lo, hi);
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (tt + 16 * st + 4 * q4 + r >= t1) sacc[st][h2][r] = -INFINITY;
       }
-    };
-    auto load_pg = [&](int g, int slot) {
-      pg[slot] = *reinterpret_cast<const bf16x8_t*>(&Ps[(16 * g + l16) * TT + 8 * q4]);
-    };
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      load_cf(half);
-      load_pg(0, 0);
-#pragma unroll
-      for (int g = 0; g < NHT; ++g) {
-        if (g + 1 < NHT) load_pg(g + 1, (g + 1) & 1);
-#pragma unroll
-        for (int j = 0; j < DT_W / 2; ++j) mfma_agpr(oacc[half * (DT_W / 2) + j][g], cf[j], pg[g & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  // Softmax of the tile whose scores are in sacc (first token tt) against the
-  // pass's reference max m_ref: publishes P^T = exp2((s - m_ref) c_log2) in bf16 and
-  // adds the row sums to l_run.  The reference is the first tile's max (or,
-  // on a second pass, the chunk's max); a later tile whose max exceeds it by
-  // more than tau flags the pass for a redo instead of rescaling the
-  // accumulators, so the accumulators are only ever touched by MFMAs and P
-  // stays below 2^tau.
-  auto softmax_publish = [&](int tt) {
-    if (tt + TT > t1) {          // tail tile: tokens past the chunk end get no weight
-#pragma unroll
-      for (int hg = 0; hg < 2; ++hg)
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (tt + 16 * st + 4 * q4 + r >= t1) sacc[st][hg][r] = -INFINITY;
-    }
-    bool exceeded = false;
-#pragma unroll
-    for (int hg = 0; hg < 2; ++hg) {
-      // max of the raw scores (c_log2 > 0 keeps their order), then over the 4
-      // lanes of the head
-      float mx = max3(max3(sacc[0][hg][0], sacc[0][hg][1], sacc[0][hg][2]),
-                      max3(sacc[0][hg][3], sacc[1][hg][0], sacc[1][hg][1]), max2(sacc[1][hg][2], sacc[1][hg][3]));
-      {
-        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-        auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = max2(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
-      }
+      sm8[hg] = max3(max3(sacc[0][hg][0], sacc[0][hg][1], sacc[0][hg][2]),
+                     max3(sacc[0][hg][3], sacc[1][hg][0], sacc[1][hg][1]), max2(sacc[1][hg][2], sacc[1][hg][3]));
+    } else if constexpr (j == 1) {
+      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(sm8[hg]), __float_as_uint(sm8[hg]), false, false);
+      sm8[hg] = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    } else if constexpr (j == 2) {
+      auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm8[hg]), __float_as_uint(sm8[hg]), false, false);
+      const float mx = max2(__uint_as_float(r2[0]), __uint_as_float(r2[1]));   // the head's max over the tile
       m_max[hg] = max2(m_max[hg], mx);
       if (m_ref[hg] == -INFINITY) m_ref[hg] = mx;        // first tile of the first pass
       else exceeded |= (mx - m_ref[hg]) * c_log2 > RESCALE_TAU;
-      const float mc = (m_ref[hg] == -INFINITY) ? 0.f : m_ref[hg] * c_log2;
+      mc[hg] = (m_ref[hg] == -INFINITY) ? 0.f : m_ref[hg] * c_log2;
+      rs[hg] = 0.f;
+    } else if constexpr (j < 11) {
+      constexpr int e = j - 3, st = e >> 2, r = e & 3;
+      const float p = fast_exp2(fmaf(sacc[st][hg][r], c_log2, -mc[hg]));
+      if constexpr (e > 0) rs[hg] += pv_prev[hg];
+      pv_prev[hg] = p;
+      pf[hg][e] = (__bf16)p;         // round to nearest even
+    } else {
+      l_run[hg] += rs[hg] + pv_prev[hg];
       const int h = 16 * (hg0 + hg) + l16;
-      bf16x8_t pf;
-      float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv = fast_exp2(fmaf(sacc[st][hg][r], c_log2, -mc));
-          if (r & 1) rs1 += pv;
-          else rs0 += pv;
-          pf[4 * st + r] = (__bf16)pv;      // round to nearest even
-        }
-      l_run[hg] += rs0 + rs1;
-      *reinterpret_cast<bf16x8_t*>(&Ps[h * TT + 8 * q4]) = pf;
+      *reinterpret_cast<bf16x8_t*>(&Pn[h * TT + 8 * q4]) = pf[hg];
     }
-    if (__ballot(exceeded) != 0ull && lane == 0) redo_s = 1;
+  };
+  constexpr int N_UNITS = 24;
+
+  // Iteration T: the score product of tile T+1 and then the value product of
+  // tile T, as one instruction stream, with the softmax of tile T+1 in units
+  // between the value MFMAs.  Tile T+1 past the last one reads a stale ring
+  // stage; all its tokens are past the chunk end, so it adds nothing.
+  auto iteration = [&](int T) __attribute__((always_inline)) {
+    const uint16_t* Cv = &Cs[T & (NBUF - 1)][0];
+    const uint16_t* Cn = &Cs[(T + 1) & (NBUF - 1)][0];
+    const uint16_t* Pv = &Ps[T & 1][0];
+    uint16_t* Pn = &Ps[(T + 1) & 1][0];
+    const int tt = t0 + (T + 1) * TT;
+    bf16x8_t cf[DT_W / 2], pg[2];
+#pragma unroll
+    for (int j = 0; j < DT_W / 2; ++j) cf[j] = vfrag(Cv, j);
+    pg[0] = pfrag(Pv, 0);
+    score_phase(Cn);
+    // value MFMA v = 32 half + 4 g + j; a softmax unit after every second one
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (half == 1) {
+#pragma unroll
+        for (int j = 0; j < DT_W / 2; ++j) cf[j] = vfrag(Cv, DT_W / 2 + j);
+        pg[0] = pfrag(Pv, 0);
+      }
+      static_for<NHT>([&](auto gc) __attribute__((always_inline)) {
+        constexpr int g = decltype(gc)::value;
+        if constexpr (g + 1 < NHT) pg[(g + 1) & 1] = pfrag(Pv, g + 1);
+        static_for<DT_W / 2>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          mfma_agpr(oacc[half * (DT_W / 2) + j][g], cf[j], pg[g & 1]);
+          constexpr int v = 4 * g + j;           // within the half
+          if constexpr (v % 2 == 0) {
+            constexpr int u = (v / 2) + 0;       // units 0 .. 2 NHT - 1 of this half
+            if (half == 0) {
+              if constexpr (u < N_UNITS) softmax_unit(std::integral_constant<int, u>{}, tt, Pn);
+            } else {
+              if constexpr (u + 2 * NHT < N_UNITS) softmax_unit(std::integral_constant<int, u + 2 * NHT>{}, tt, Pn);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+    }
+    // units the value product had no room for (few head groups)
+    static_for<N_UNITS>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u >= 4 * NHT) softmax_unit(uc, tt, Pn);
+    });
   };
 
-  // Iteration T computes tile T: scores, softmax, then the value product.
-  // Only tile T's buffer is in use meanwhile, so tiles T+1 .. T+3 are in
-  // flight (tile T+3 is issued into the buffer released by tile T-1).  A redo
-  // (second pass) starts from the chunk max seen by the first pass, which no
-  // tile exceeds.
+  // Prologue of a pass: scores and softmax of tile 0 (into Ps[0]).  Loop:
+  // at the top of iteration T tile T+1 has landed, P^T of tile T is in
+  // Ps[T&1] for every head, and every wave is done with iteration T-1, so
+  // tile T+3 takes the ring stage of tile T-1.  A redo (second pass) starts
+  // from the chunk max seen by the first pass, which no tile exceeds.
   for (int pass = 0; pass < 2; ++pass) {
-    if (tid == 0) redo_s = 0;
 #pragma unroll
     for (int i = 0; i < DT_W; ++i)
 #pragma unroll
       for (int g = 0; g < NHT; ++g) mfma_agpr_zero(oacc[i][g]);
     l_run[0] = l_run[1] = 0.f;
     for (int i = 0; i < NBUF - 1 && i < ntile; ++i) issue_tile(i);
+    if (ntile > 0) {
+      wait_tile(0, min(NBUF - 2, ntile - 1));
+      __syncthreads();
+      score_phase(&Cs[0][0]);
+      static_for<N_UNITS>([&](auto uc) __attribute__((always_inline)) { softmax_unit(uc, t0, &Ps[0][0]); });
+    }
     for (int T = 0; T < ntile; ++T) {
-      wait_tile(T, min(T + NBUF - 2, ntile - 1));
-      // tile T has landed for every wave; every wave is done with tile T-1
-      // and with P^T of tile T-1
+      if (T + 1 < ntile) wait_tile(T + 1, min(T + NBUF - 2, ntile - 1));
       __syncthreads();
       if (T + NBUF - 1 < ntile) issue_tile(T + NBUF - 1);
-      const uint16_t* C = &Cs[T & (NBUF - 1)][0];
-      if (score_wave) {
-        score_phase(C);
-        softmax_publish(t0 + T * TT);
-      }
-      __syncthreads();      // P^T of tile T is visible
-      value_phase(C);
+      iteration(T);
     }
+    // end of pass: did any head of any wave exceed its reference?
+    __syncthreads();                             // the ring is idle
+    int* flags = reinterpret_cast<int*>(&Cs[0][0]);
+    flags[wave] = (__ballot(exceeded) != 0ull) ? 1 : 0;    // every lane stores the same value
     __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(redo_s)) break;
+    const int redo = flags[0] | flags[1] | flags[2] | flags[3];
+    __syncthreads();                             // flags read before the ring is refilled
+    if (!__builtin_amdgcn_readfirstlane(redo)) break;
     m_ref[0] = m_max[0];
     m_ref[1] = m_max[1];
-    __syncthreads();      // every wave has read the flag before it is cleared
+    mc[0] = (m_ref[0] == -INFINITY) ? 0.f : m_ref[0] * c_log2;
+    mc[1] = (m_ref[1] == -INFINITY) ? 0.f : m_ref[1] * c_log2;
+    exceeded = false;
+    mfma_drain();
   }
 
-  if (score_wave) {
+  // 1/l per head through ring memory (idle since the end of the last pass)
+  float* linv_s = reinterpret_cast<float*>(&Cs[1][0]);
 #pragma unroll
-    for (int hg = 0; hg < 2; ++hg) {
-      if (hg0 + hg >= NHT) break;
-      const float l = quad_sum(l_run[hg]);
-      const int h = 16 * (hg0 + hg) + l16;
-      if (q4 == 0) {
-        linv_s[h] = (l > 0.f) ? 1.f / l : 0.f;
-        lse_part[((int64_t)b * a.n_splits + k) * a.H + h] =
-            (l > 0.f) ? (m_ref[hg] * c_log2 + __log2f(l)) * MLA_LN2 : -INFINITY;
-      }
+  for (int hg = 0; hg < 2; ++hg) {
+    if (hg0 + hg >= NHT) break;
+    const float l = quad_sum(l_run[hg]);
+    const int h = 16 * (hg0 + hg) + l16;
+    if (q4 == 0) {
+      linv_s[h] = (l > 0.f) ? 1.f / l : 0.f;
+      lse_part[((int64_t)b * a.n_splits + k) * a.H + h] =
+          (l > 0.f) ? (m_ref[hg] * c_log2 + __log2f(l)) * MLA_LN2 : -INFINITY;
     }
   }
   __syncthreads();
