@@ -238,21 +238,6 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
   const int t0 = min(L, k * csz), t1 = min(L, (k + 1) * csz);
   const int ntile = (t1 - t0 + TT - 1) / TT;
 
-  // q~ as the B operand: lane holds q~[h][32ks + 8q4 .. +8] for h = 16g + l16
-  // of groups g = hg0, hg0 + 1 (zero for a group past H)
-  bf16x8_t qf[2][KS];
-#pragma unroll
-  for (int hg = 0; hg < 2; ++hg) {
-    const int g = hg0 + hg;
-    const uint16_t* qrow = qt + ((int64_t)b * a.H + 16 * min(g, NHT - 1) + l16) * DLAT + q4 * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 32);
-      qf[hg][ks] = (g < NHT) ? v : bf16x8_t{};
-    }
-  }
-  wait_vmcnt<0>();      // q~ has landed; from here on vmcnt counts tile loads only
-
   // Tile loads: lane instruction i fills tile slot s = (wave*9 + i)*64 + lane,
   // i.e. row s/72 and swizzled chunk s%72.  The buffer range ends at the
   // chunk's last row, so rows past it read as zero.
@@ -288,6 +273,24 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
     else if (after == 1) wait_vmcnt<LOADS>();
     else wait_vmcnt<0>();
   };
+
+  // q~ as the B operand: lane holds q~[h][32ks + 8q4 .. +8] for h = 16g + l16
+  // of groups g = hg0, hg0 + 1 (zero for a group past H)
+  for (int i = 0; i < NBUF - 1 && i < ntile; ++i) issue_tile(i);
+  bf16x8_t qf[2][KS];
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg) {
+    const int g = hg0 + hg;
+    const uint16_t* qrow = qt + ((int64_t)b * a.H + 16 * min(g, NHT - 1) + l16) * DLAT + q4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 32);
+      qf[hg][ks] = (g < NHT) ? v : bf16x8_t{};
+    }
+  }
+  // The first tiles go out before q~ is loaded, so that both latencies
+  // overlap; after this wait vmcnt counts tile loads only.
+  wait_vmcnt<0>();
 
   // Score-product row reads.  The read for k-step ks is logical chunk 4ks + q4
   // of row l16 (+16 for the second token half, which shares the swizzle); with
@@ -469,7 +472,8 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
 #pragma unroll
       for (int g = 0; g < NHT; ++g) mfma_agpr_zero(oacc[i][g]);
     l_run[0] = l_run[1] = 0.f;
-    for (int i = 0; i < NBUF - 1 && i < ntile; ++i) issue_tile(i);
+    if (pass > 0)
+      for (int i = 0; i < NBUF - 1 && i < ntile; ++i) issue_tile(i);
     if (ntile > 0) {
       wait_tile(0, min(NBUF - 2, ntile - 1));
       __syncthreads();
@@ -498,8 +502,14 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
     mfma_drain();
   }
 
-  // 1/l per head through ring memory (idle since the end of the last pass)
-  float* linv_s = reinterpret_cast<float*>(&Cs[1][0]);
+  // The ring is idle now.  Each wave stages its O^T block as rows of heads
+  // (fp16, rows padded by 16 bytes against bank conflicts) in its own 34 KB of
+  // ring memory, then stores whole 256-byte row pieces of o_part; 1/l per head
+  // sits after the four staging areas.
+  constexpr int OSTR = 128 * 2 + 16;                      // staging row stride (bytes)
+  uint8_t* ring = reinterpret_cast<uint8_t*>(&Cs[0][0]);
+  static_assert(4 * MAXG * 16 * OSTR + MAXG * 16 * 4 <= NBUF * TT * DLAT * 2, "staging fits in the ring");
+  float* linv_s = reinterpret_cast<float*>(ring + 4 * MAXG * 16 * OSTR);
 #pragma unroll
   for (int hg = 0; hg < 2; ++hg) {
     if (hg0 + hg >= NHT) break;
@@ -515,7 +525,7 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
   mfma_drain();
   // lane holds O^T[d = 16 (8 wave + i) + 4q4 + r][h = 16g + l16]
   // (fp16: the normalised partial is a convex combination of cache rows)
-  uint16_t* dst = o_part + ((int64_t)b * a.n_splits + k) * a.H * DC + 128 * wave + 4 * q4;
+  uint8_t* stg = ring + wave * (MAXG * 16 * OSTR);
 #pragma unroll
   for (int g = 0; g < NHT; ++g) {
     const int hh = 16 * g + l16;
@@ -524,8 +534,18 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
     for (int i = 0; i < DT_W; ++i) {
       agpr_fence(oacc[i][g]);
       const f32x4_t v = oacc[i][g] * inv;
-      *reinterpret_cast<u32x2_t*>(dst + (int64_t)hh * DC + 16 * i) = u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+      *reinterpret_cast<u32x2_t*>(stg + hh * OSTR + (16 * i + 4 * q4) * 2) =
+          u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
     }
+  }
+  // a wave reads back only its own rows (LDS accesses of one wave complete in
+  // order): 4 heads x 256 bytes per instruction
+  uint16_t* dst = o_part + ((int64_t)b * a.n_splits + k) * a.H * DC + 128 * wave;
+#pragma unroll
+  for (int it = 0; it < 4 * NHT; ++it) {
+    const int row = 4 * it + (lane >> 4), c = lane & 15;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + row * OSTR + 16 * c);
+    *reinterpret_cast<u32x4_t*>(dst + (int64_t)row * DC + 8 * c) = v;
   }
 }
 
