@@ -45,7 +45,7 @@ __device__ __forceinline__ void load8(const void* w, int64_t idx, float (&f)[8])
 }
 
 template <mla_dtype WT, mla_dtype OT, bool HALFP>
-__global__ void __launch_bounds__(CTHREADS)
+__global__ void __launch_bounds__(CTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
 combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const void* __restrict__ o_part) {
   extern __shared__ __attribute__((aligned(16))) float olat[];   // [CB][dkv]
   __shared__ float wk[CB][MAXNS];
@@ -55,6 +55,27 @@ combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const void* __r
   const int nb = min(CB, a.B - b0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ns = a.n_splits, dkv = a.dkv;
+
+  // The MFMA un-absorb (step 3, bf16 weights, d_v = 128, d_kv = 512) takes
+  // its W_UV fragments in registers: the first half is loaded here, so that
+  // its latency passes during the merge, the second half at the start of
+  // step 3, while the first half is multiplied.
+  constexpr int UKS = 512 / 32;                 // k-steps of the MFMA un-absorb
+  const bool mfma_unabsorb = WT == MLA_BF16 && a.dv == 2 * 16 * (CTHREADS / 64) && dkv == 32 * UKS;
+  const int64_t wrow0 = (int64_t)h * (a.dn + a.dv) + a.dn;
+  const int l16 = lane & 15, q4 = lane >> 4;
+  bf16x8_t wfr[UKS][2];
+  const uint16_t* wv = static_cast<const uint16_t*>(a.w) + (wrow0 + 32 * wave + l16) * dkv + 8 * q4;
+  auto load_w = [&](int ks0) {
+#pragma unroll
+    for (int ks = ks0; ks < ks0 + UKS / 2; ++ks)
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb)
+        wfr[ks][vb] = *reinterpret_cast<const bf16x8_t*>(wv + (int64_t)16 * vb * dkv + 32 * ks);
+  };
+  if constexpr (WT == MLA_BF16) {
+    if (mfma_unabsorb) load_w(0);
+  }
 
   // 1. chunk weights
   for (int bi = wave; bi < nb; bi += CTHREADS / 64) {
@@ -105,8 +126,50 @@ combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const void* __r
   __syncthreads();
 
   // 3. un-absorb: out[b, h, v] = W_UV[h][v] . o_lat[b]
+  if constexpr (WT == MLA_BF16) {
+    if (mfma_unabsorb) {
+      // On 16x16x32 bf16 MFMA: out^T[v][s] = W_UV[h][v][:] . o_lat[s][:], 16 rows
+      // v x 16 sequence columns (8 used) per product; wave w owns v-blocks 2w
+      // and 2w+1.  A lane holds 8 consecutive latent columns of one W row (the
+      // 16 lanes of a k-group read 16 rows, 64 contiguous bytes each), and the
+      // fp32 o_lat enters as two bf16 terms, hi = bf16(x) and lo = bf16(x - hi),
+      // so the product keeps about 16 bits of o_lat.
+      f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      load_w(UKS / 2);
+#pragma unroll
+      for (int ks = 0; ks < UKS; ++ks) {
+        bf16x8_t bhi = {}, blo = {};
+        if (l16 < nb) {
+          const f32x4_t* o = reinterpret_cast<const f32x4_t*>(&olat[l16 * dkv + 32 * ks + 8 * q4]);
+          const f32x4_t o0 = o[0], o1 = o[1];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = (e < 4) ? o0[e] : o1[e - 4];
+            const __bf16 hi = (__bf16)x;
+            bhi[e] = hi;
+            blo[e] = (__bf16)(x - (float)hi);
+          }
+        }
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb) {
+          acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfr[ks][vb], bhi, acc[vb], 0, 0, 0);
+          acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfr[ks][vb], blo, acc[vb], 0, 0, 0);
+        }
+      }
+      // lane holds out^T[v = 32 wave + 16 vb + 4 q4 + r][s = l16]
+      if (l16 < nb) {
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            store_elem<OT>(a.out, ((int64_t)(b0 + l16) * a.H + h) * a.dv + 32 * wave + 16 * vb + 4 * q4 + r,
+                           acc[vb][r]);
+      }
+      if (a.lse != nullptr && tid < nb) a.lse[(int64_t)(b0 + tid) * a.H + h] = lse_s[tid];
+      return;
+    }
+  }
   constexpr int HALF = CB / 2;
-  const int64_t wrow0 = (int64_t)h * (a.dn + a.dv) + a.dn;
   for (int it = tid; it < a.dv * 2; it += CTHREADS) {
     const int v = it % a.dv, half = it / a.dv;
     float acc[HALF];
