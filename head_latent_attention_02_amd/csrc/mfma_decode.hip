@@ -110,16 +110,23 @@ absorb_mfma_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
           u32x2_t{pack_bf16x2(acc[nb][mb][0], acc[nb][mb][1]), pack_bf16x2(acc[nb][mb][2], acc[nb][mb][3])};
   }
   // RoPE band of the query at the new token's position
-  if (blockIdx.y != 0) return;
+  // (both column blocks of the head share the work; a thread's pair index m
+  // is fixed, so its frequency is formed once).  The angle is formed and
+  // reduced to [-pi, pi] in fp64 (so large positions lose no accuracy), then
+  // the fp32 sine and cosine of the reduced angle carry a few fp32 ulps.
   const uint16_t* qp = static_cast<const uint16_t*>(a.q_pe);
-  for (int e = tid; e < AM * 32; e += 256) {
-    const int b = b0 + (e >> 5), m = e & 31;
+  constexpr double TWO_PI_HI = 6.283185307179586, TWO_PI_LO = 2.4492935982947064e-16;
+  const int m = tid & 31;
+  const double theta = exp(-2.0 * (double)m / (double)DRP * log((double)a.rope_base));
+  for (int e = tid + 256 * blockIdx.y; e < AM * 32; e += 256 * gridDim.y) {
+    const int b = b0 + (e >> 5);
     if (b >= a.B) break;
     int L = min(max(a.cache_len[b], 0), a.max_len);
-    double pos = (double)(L > 0 ? L - 1 : 0);
-    double theta = exp(-2.0 * (double)m / (double)DRP * log((double)a.rope_base));
-    double s, c;
-    sincos(pos * theta, &s, &c);
+    const double ang = (double)(L > 0 ? L - 1 : 0) * theta;
+    const double k = rint(ang * (1.0 / TWO_PI_HI));
+    const float r = (float)fma(-k, TWO_PI_LO, fma(-k, TWO_PI_HI, ang));
+    float s, c;
+    sincosf(r, &s, &c);
     const int64_t row = (int64_t)b * a.H + h;
     float lo = bf16_bits_to_float(qp[row * DRP + m]), hi = bf16_bits_to_float(qp[row * DRP + m + 32]);
     qt[row * DLAT + DC + m] = float_to_bf16_bits(lo * (float)c - hi * (float)s);
