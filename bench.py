@@ -57,14 +57,14 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "08647e82ea6065d0", "fetch_kib": 348323.8, "write_kib": 292863.3,
-                      "fetch_factor": 0.50003, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "348ef7db262673c7", "fetch_kib": 100650.3, "write_kib": 273453.0,
-                          "fetch_factor": 0.50003, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "fd3bfe849c65c4f2", "fetch_kib": 1216645.1, "write_kib": 131585.6,
-                     "fetch_factor": 0.50003, "write_factor": 1.0},
-    "lse_combine": {"digest": "bcf1eba073225179", "fetch_kib": 83789.8, "write_kib": 4354.4,
-                   "fetch_factor": 0.50003, "write_factor": 1.0},
+    "mfma_attention": {"digest": "e6591f8ff76a3cf6", "fetch_kib": 350409.4, "write_kib": 292862.6,
+                      "fetch_factor": 0.50002, "write_factor": 1.0},
+    "mfma_up_projection": {"digest": "348ef7db262673c7", "fetch_kib": 100647.2, "write_kib": 274472.3,
+                          "fetch_factor": 0.50002, "write_factor": 1.0},
+    "mfma_split_kv": {"digest": "e284382585a9403a", "fetch_kib": 1216693.2, "write_kib": 131584.0,
+                     "fetch_factor": 0.50002, "write_factor": 1.0},
+    "lse_combine": {"digest": "e502c80568202f3c", "fetch_kib": 84069.8, "write_kib": 4352.0,
+                   "fetch_factor": 0.50002, "write_factor": 1.0},
 }
 
 
