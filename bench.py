@@ -165,8 +165,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs the MLA hot path on one GPU; multi-GPU runs are not "
-                                   "part of this build (--gpus must be 1)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs the MLA hot path on one GPU; the library has no "
+                                   "multi-GPU path (--gpus must be 1)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch

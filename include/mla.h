@@ -64,7 +64,7 @@ extern "C" {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad enum   */
-  MLA_ERR_UNSUPPORTED = 2,        /* valid request this build does not implement */
+  MLA_ERR_UNSUPPORTED = 2,        /* valid request the library does not implement */
   MLA_ERR_WORKSPACE_TOO_SMALL = 3,
   MLA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed  */
 } mla_status;
