@@ -186,7 +186,7 @@ constexpr int LOADS = TT * CHUNKS / NTHREADS;         // loads per lane per tile
 constexpr int DT_W = DC / 16 / NW;       // value-product d-tiles per wave (8)
 constexpr int KS = DLAT / 32;            // score k-steps (18)
 constexpr int SPF = 4;                   // score fragments read ahead of their MFMAs
-constexpr float RESCALE_TAU = 8.f;       // log2 units
+constexpr float TAU = 8.f;               // log2 units: a tile past the reference by more flags a redo
 
 // 16-byte chunk swizzle of a tile row (measured free of LDS bank conflicts for
 // both the row reads and the transposed reads below)
@@ -196,7 +196,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7
 // Written as inline assembly so that the value-product accumulators (256
 // registers) stay in the AGPR file while the score accumulators, which the
 // softmax reads, are VGPRs.  Every compiler-generated access to these AGPRs
-// (zeroing, the rescale, the final read) is separated from the MFMAs by a
+// (zeroing, the final read) is separated from the MFMAs by a
 // barrier or an explicit s_nop, which covers the MFMA result latency.
 __device__ __forceinline__ void mfma_agpr(f32x4_t& acc, bf16x8_t a, bf16x8_t b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
@@ -402,7 +402,7 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
       const float mx = max2(__uint_as_float(r2[0]), __uint_as_float(r2[1]));   // the head's max over the tile
       m_max[hg] = max2(m_max[hg], mx);
       if (m_ref[hg] == -INFINITY) m_ref[hg] = mx;        // first tile of the first pass
-      else exceeded |= (mx - m_ref[hg]) * c_log2 > RESCALE_TAU;
+      else exceeded |= (mx - m_ref[hg]) * c_log2 > TAU;
       mc[hg] = (m_ref[hg] == -INFINITY) ? 0.f : m_ref[hg] * c_log2;
       rs[hg] = 0.f;
     } else if constexpr (j < 11) {
