@@ -61,7 +61,7 @@ HBM_COUNTERS: dict = {
                       "fetch_factor": 0.50002, "write_factor": 1.0},
     "mfma_up_projection": {"digest": "348ef7db262673c7", "fetch_kib": 100647.2, "write_kib": 274472.3,
                           "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "e284382585a9403a", "fetch_kib": 1216693.2, "write_kib": 131584.0,
+    "mfma_split_kv": {"digest": "170a0ea3db39ea06", "fetch_kib": 1216693.2, "write_kib": 131584.0,
                      "fetch_factor": 0.50002, "write_factor": 1.0},
     "lse_combine": {"digest": "e502c80568202f3c", "fetch_kib": 84069.8, "write_kib": 4352.0,
                    "fetch_factor": 0.50002, "write_factor": 1.0},
