@@ -376,3 +376,28 @@ def test_explicit_mixed_batch_redo(mla):
     ro, rl = _oracle_explicit(cfg, x)
     _compare(o, ro, True, "mixed-redo out")
     _compare_lse(l, rl, True, "mixed-redo", magnitude_scaled=True)
+
+
+def test_decode_tiny_fp32(mla):
+    # The tiny fp32 shapes in absorbed form (fp32 inputs, the SIMT split-KV
+    # kernels and the fp32 merge + un-absorb of the combine), against the
+    # oracle at the fp32 bar; ragged lengths and more splits than some rows.
+    cfg = I.small_decode("tiny_fp32_decode", batch=3, cache_len=64, n_heads=4, d_kv=32, d_nope=16, d_rope=8,
+                         d_v=16, n_splits=4, seed=205)
+    x = I.make_decode_inputs(cfg, cache_len=np.array([64, 17, 1], dtype=np.int32))
+    cache = torch.from_numpy(I.bf16_bits_to_f32(x["cache_bits"])).cuda()
+    qn = _dev(x["q_nope"], torch.float32)
+    qp = _dev(x["q_pe"], torch.float32)
+    w = _dev(x["w_kv_b"], torch.float32)
+    cl = torch.from_numpy(x["cache_len"]).cuda()
+    desc = mla.decode_desc(batch=cfg.batch, n_heads=cfg.n_heads, d_kv=cfg.d_kv, d_nope=cfg.d_nope,
+                           d_rope=cfg.d_rope, d_v=cfg.d_v, max_cache_len=cfg.cache_len, n_splits=cfg.n_splits,
+                           softmax_scale=cfg.softmax_scale, in_dtype=mla.MLA_FP32)
+    ws = _poisoned(mla.mla_decode_absorbed_workspace_size(desc))
+    _say(f"decode {cfg.name}: B={cfg.batch} L={cfg.cache_len} H={cfg.n_heads} fp32 inputs")
+    out, lse, _ = mla.mla_decode_absorbed(qn, qp, cache, cl, w, n_splits=cfg.n_splits, d_kv=cfg.d_kv,
+                                          softmax_scale=cfg.softmax_scale, workspace=ws)
+    torch.cuda.synchronize()
+    r = _oracle_decode(cfg, x)
+    _compare(out.cpu().numpy(), r["out"], False, "tiny fp32 decode out")
+    _compare_lse(lse.cpu().numpy(), r["lse"], False, "tiny fp32 decode")
