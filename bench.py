@@ -10,9 +10,16 @@ One step = one pass of the whole hot path over one batch of synthetic input:
 Prints ONE JSON line.  `value` is the explicit forward's algorithmic TFLOP/s
 (causally visible pairs plus the up-projection of the visible latent rows,
 divided by the time of the explicit part of each step); the decode part is
-reported as tokens/s and algorithmic HBM GB/s.  Per-kernel durations come from
-HIP events the library records around each of its launches on the stream the
-kernels run on (mla_timing_*), inside the timed region.
+reported as tokens/s and algorithmic HBM GB/s.
+
+Two timed regions of K steps each follow the warm-up:
+  1. eager calls, with HIP events that the library records around each of its
+     launches on the stream the kernels run on (mla_timing_*): the per-kernel
+     durations and roofline figures;
+  2. the same step captured once as two HIP graphs (explicit, decode; checked
+     bit-identical to the eager result) and replayed K times: the step time,
+     `value`, tokens/s and GB/s, without per-launch host overhead between the
+     kernels.  `--no-graph` reports the eager region's step time instead.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--copy-calibration]
@@ -98,6 +105,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle baseline sample")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time the step as eager calls (no HIP graph replay)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run a plain 1 GiB device copy (3 times) before the warm-up, as the "
                         "reference reading for HBM byte counters")
@@ -247,6 +256,61 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     e_ms = float(np.mean(exp_ms))
     d_ms = float(np.mean(dec_ms))
+    eager = {"ms_per_step": ms_step, "explicit_ms": e_ms, "decode_ms": d_ms}
+    graph = None
+    if not args.no_graph:
+        # the reference outputs of one eager step
+        step(False)
+        torch.cuda.synchronize()
+        ref = [out.clone(), lse.clone(), dout.clone(), dlse.clone()]
+        g_exp, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(False)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        log("capturing the explicit and decode steps as HIP graphs")
+        with torch.cuda.graph(g_exp):
+            mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"],
+                                 q_pos0=ecfg.q_pos0, kv_pos0=ecfg.kv_pos0, causal=ecfg.causal,
+                                 softmax_scale=ecfg.softmax_scale, out=out, lse=lse, workspace=ws)
+        with torch.cuda.graph(g_dec):
+            mla.mla_decode_absorbed(dq_nope, dq_pe, cache, dlen, dw, n_splits=dcfg.n_splits,
+                                    softmax_scale=dcfg.softmax_scale, out=dout, lse=dlse, workspace=dws)
+        torch.cuda.synchronize()
+        for buf in (out, lse, dout, dlse):
+            buf.fill_(float("nan"))
+        g_exp.replay()
+        g_dec.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(torch.nan_to_num(a, neginf=-1e30), torch.nan_to_num(b, neginf=-1e30))
+                   for a, b in zip((out, lse, dout, dlse), ref))
+        if not same:
+            raise RuntimeError("graph replay differs from the eager step")
+        for _ in range(args.warmup):
+            g_exp.replay()
+            g_dec.replay()
+        log(f"timing {args.steps} graph replays")
+        g_exp_ms, g_dec_ms = [], []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            ev[0].record()
+            g_exp.replay()
+            ev[1].record()
+            g_dec.replay()
+            ev[2].record()
+            torch.cuda.synchronize()
+            g_exp_ms.append(ev[0].elapsed_time(ev[1]))
+            g_dec_ms.append(ev[1].elapsed_time(ev[2]))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_step = (t1 - t0) * 1e3 / args.steps
+        e_ms = float(np.mean(g_exp_ms))
+        d_ms = float(np.mean(g_dec_ms))
+        graph = {"ms_per_step": ms_step, "explicit_ms": e_ms, "decode_ms": d_ms,
+                 "check": "replay bit-identical to the eager step"}
     fl = ecfg.flops()
     dflops = dcfg.flops()
     dbytes = dcfg.algorithmic_bytes()
@@ -320,6 +384,8 @@ def main():
         "roofline": roofline,
         "roofline_decode": roofline_decode,
         "kernels": kernels,
+        "timing": {"step": "hip_graph_replay" if graph is not None else "eager", "eager": eager,
+                   "graph": graph},
     }
 
     if not args.no_cpu_baseline:
