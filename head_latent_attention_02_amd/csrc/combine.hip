@@ -55,6 +55,10 @@ combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const void* __r
   const int nb = min(CB, a.B - b0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ns = a.n_splits, dkv = a.dkv;
+  auto lse_index = [&](int bb) -> int64_t {
+    return a.lse_seq > 0 ? ((int64_t)(bb / a.lse_seq) * a.H + h) * a.lse_seq + bb % a.lse_seq
+                         : (int64_t)bb * a.H + h;
+  };
 
   // The MFMA un-absorb (step 3, bf16 weights, d_v = 128, d_kv = 512) takes
   // its W_UV fragments in registers: the first half is loaded here, so that
@@ -165,7 +169,7 @@ combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const void* __r
             store_elem<OT>(a.out, ((int64_t)(b0 + l16) * a.H + h) * a.dv + 32 * wave + 16 * vb + 4 * q4 + r,
                            acc[vb][r]);
       }
-      if (a.lse != nullptr && tid < nb) a.lse[(int64_t)(b0 + tid) * a.H + h] = lse_s[tid];
+      if (a.lse != nullptr && tid < nb) a.lse[lse_index(b0 + tid)] = lse_s[tid];
       return;
     }
   }
@@ -194,7 +198,7 @@ combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const void* __r
       if (bi < nb) store_elem<OT>(a.out, ((int64_t)(b0 + bi) * a.H + h) * a.dv + v, acc[j]);
     }
   }
-  if (a.lse != nullptr && tid < nb) a.lse[(int64_t)(b0 + tid) * a.H + h] = lse_s[tid];
+  if (a.lse != nullptr && tid < nb) a.lse[lse_index(b0 + tid)] = lse_s[tid];
 }
 
 }  // namespace

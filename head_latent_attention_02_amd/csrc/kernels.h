@@ -32,7 +32,19 @@ struct DecodeArgs {
   const int32_t* cache_len;
   void* out;
   float* lse;
+  // Absorbed prefill runs every query row as its own sequence (defaults keep
+  // the decode step's meaning):
+  int seq_per_cache = 1;            // consecutive sequences sharing one cache entry
+  const int64_t* q_pos = nullptr;   // RoPE position per sequence (nullptr: cache_len - 1)
+  int reverse = 0;                  // split-KV takes sequences last to first
+  int lse_seq = 0;                  // > 0: lse is [B / lse_seq, H, lse_seq], else [B, H]
 };
+
+// Absorbed prefill: latent cache rows cache[b][j] = c_kv[b][j] || R(k_pe[b][j],
+// kv_pos0 + j) (in_dt), and per query row i of batch entry b (sequence
+// b * Sq + i) its visible key count and RoPE position.
+hipError_t launch_latent_cache(const ExplicitArgs& a, void* cache, int32_t* cache_len, int64_t* q_pos,
+                               hipStream_t stream);
 
 // RoPE cos/sin table: table[p*(dr/2)+m] = (cos, sin)((pos0+p) * base^(-2m/dr)),
 // angles formed in fp64.

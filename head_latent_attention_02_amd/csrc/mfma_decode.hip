@@ -122,7 +122,7 @@ absorb_mfma_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
     const int b = b0 + (e >> 5);
     if (b >= a.B) break;
     int L = min(max(a.cache_len[b], 0), a.max_len);
-    const double ang = (double)(L > 0 ? L - 1 : 0) * theta;
+    const double ang = (a.q_pos != nullptr ? (double)a.q_pos[b] : (double)(L > 0 ? L - 1 : 0)) * theta;
     const double k = rint(ang * (1.0 / TWO_PI_HI));
     const float r = (float)fma(-k, TWO_PI_LO, fma(-k, TWO_PI_HI, ang));
     float s, c;
@@ -235,7 +235,7 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
   __shared__ __attribute__((aligned(16))) uint16_t Cs[NBUF][TT * DLAT];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[2][MAXG * 16 * TT];   // P^T [h][k-slot]
 
-  const int k = blockIdx.x, b = blockIdx.y;
+  const int k = blockIdx.x, b = a.reverse ? a.B - 1 - (int)blockIdx.y : (int)blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int hg0 = 2 * wave;                     // first head group of this wave's scores
@@ -248,7 +248,7 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
   // Tile loads: lane instruction i fills tile slot s = (wave*9 + i)*64 + lane,
   // i.e. row s/72 and swizzled chunk s%72.  The buffer range ends at the
   // chunk's last row, so rows past it read as zero.
-  const uint16_t* cbase = static_cast<const uint16_t*>(a.cache) + (int64_t)b * a.cache_stride;
+  const uint16_t* cbase = static_cast<const uint16_t*>(a.cache) + (int64_t)(b / a.seq_per_cache) * a.cache_stride;
   const i32x4_t rsrc = make_rsrc(cbase, (uint32_t)t1 * (DLAT * 2));
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);      // wave index as a scalar
   const uint32_t cs_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&Cs[0][0];

@@ -1,6 +1,7 @@
 // C ABI of libmla: argument validation, workspace carving and the launch
 // sequence of each entry point.  Every check runs on the host before the first
 // launch, so an invalid call enqueues nothing.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -211,6 +212,94 @@ mla_status make_decode_plan(const mla_decode_desc* d, DecodePlan* plan) {
   return MLA_OK;
 }
 
+
+void fill_decode_args(const mla_decode_desc* desc, const void* q_nope, const void* q_pe, const void* kv_cache,
+                      const int32_t* cache_len, const void* w_kv_b, void* out, float* lse, DecodeArgs* pa) {
+  DecodeArgs& a = *pa;
+  a.B = desc->batch; a.H = desc->n_heads; a.dkv = desc->d_kv; a.dn = desc->d_nope;
+  a.dr = desc->d_rope; a.dv = desc->d_v; a.max_len = desc->max_cache_len;
+  a.cache_stride = desc->cache_batch_stride; a.n_splits = desc->n_splits;
+  a.scale = desc->softmax_scale; a.rope_base = desc->rope_base;
+  a.in_dt = desc->in_dtype; a.out_dt = desc->out_dtype;
+  a.q_nope = q_nope; a.q_pe = q_pe; a.cache = kv_cache; a.w = w_kv_b; a.cache_len = cache_len;
+  a.out = out; a.lse = lse;
+}
+
+// absorb, split-KV and combine for a validated plan
+mla_status run_decode(const DecodePlan& p, const DecodeArgs& a, char* ws, hipStream_t s) {
+  float* lse_part = reinterpret_cast<float*>(ws + p.off_lse);
+  void* o_part = ws + p.off_opart;
+  hipError_t e;
+  if (p.mfma) {
+    uint16_t* qt = reinterpret_cast<uint16_t*>(ws + p.off_qt);
+    {
+      TimedLaunch t("absorb", s);
+      e = launch_absorb_bf16(a, qt, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "query absorption");
+    {
+      TimedLaunch t("mfma_split_kv", s);
+      e = launch_mfma_splitkv(a, qt, lse_part, static_cast<uint16_t*>(o_part), s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mfma split-KV attention");
+  } else {
+    float* qt = reinterpret_cast<float*>(ws + p.off_qt);
+    {
+      TimedLaunch t("simt_absorb", s);
+      e = launch_simt_absorb(a, qt, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "query absorption");
+    {
+      TimedLaunch t("simt_split_kv", s);
+      e = launch_simt_splitkv(a, qt, lse_part, static_cast<float*>(o_part), s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "simt split-KV attention");
+  }
+  {
+    TimedLaunch t("lse_combine", s);
+    e = launch_combine(a, lse_part, o_part, p.mfma, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "LSE combine");
+  return MLA_OK;
+}
+
+// ------------------------------------------------------- absorbed prefill --
+// The decode problem that an absorbed-form forward maps to: one sequence per
+// query row (B * Sq of them), one chunk each, the batch entry's latent rows
+// as every one of its rows' cache.
+struct AbsorbedPlan {
+  mla_decode_desc dd{};
+  DecodePlan dec;
+  size_t off_cache = 0, off_len = 0, off_pos = 0, total = 0;
+};
+
+mla_status make_absorbed_plan(const mla_explicit_desc* d, AbsorbedPlan* plan) {
+  if (!explicit_shape_ok(d)) return MLA_ERR_INVALID_ARGUMENT;
+  AbsorbedPlan p;
+  const int64_t rows = (int64_t)d->batch * d->s_q;
+  if (rows > (int64_t)1 << 30 || (int64_t)d->s_kv > ((int64_t)1 << 31) - 1) return MLA_ERR_UNSUPPORTED;
+  if (rows == 0) {
+    *plan = p;
+    return MLA_OK;
+  }
+  const int64_t dlat = (int64_t)d->d_kv + d->d_rope;
+  p.dd.batch = (int32_t)rows;
+  p.dd.n_heads = d->n_heads; p.dd.d_kv = d->d_kv; p.dd.d_nope = d->d_nope; p.dd.d_rope = d->d_rope;
+  p.dd.d_v = d->d_v; p.dd.max_cache_len = d->s_kv; p.dd.cache_batch_stride = (int64_t)d->s_kv * dlat;
+  p.dd.n_splits = 1;
+  p.dd.softmax_scale = d->softmax_scale; p.dd.rope_base = d->rope_base;
+  p.dd.in_dtype = d->in_dtype; p.dd.out_dtype = d->out_dtype; p.dd.algo = d->algo;
+  mla_status st = make_decode_plan(&p.dd, &p.dec);
+  if (st != MLA_OK) return st;
+  const size_t esz = d->in_dtype == MLA_BF16 ? 2 : 4;
+  size_t off = p.dec.total;
+  p.off_cache = off; off = align_up(off + esz * (size_t)d->batch * d->s_kv * dlat);
+  p.off_len = off;   off = align_up(off + 4 * (size_t)rows);
+  p.off_pos = off;   off = align_up(off + 8 * (size_t)rows);
+  p.total = off;
+  *plan = p;
+  return MLA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -338,49 +427,61 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc, const void* q_nope, 
       if (q != nullptr && !aligned16(q)) return MLA_ERR_INVALID_ARGUMENT;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
   DecodeArgs a;
-  a.B = desc->batch; a.H = desc->n_heads; a.dkv = desc->d_kv; a.dn = desc->d_nope;
-  a.dr = desc->d_rope; a.dv = desc->d_v; a.max_len = desc->max_cache_len;
-  a.cache_stride = desc->cache_batch_stride; a.n_splits = desc->n_splits;
-  a.scale = desc->softmax_scale; a.rope_base = desc->rope_base;
-  a.in_dt = desc->in_dtype; a.out_dt = desc->out_dtype;
-  a.q_nope = q_nope; a.q_pe = q_pe; a.cache = kv_cache; a.w = w_kv_b; a.cache_len = cache_len;
-  a.out = out; a.lse = lse;
-  float* lse_part = reinterpret_cast<float*>(ws + p.off_lse);
-  void* o_part = ws + p.off_opart;
+  fill_decode_args(desc, q_nope, q_pe, kv_cache, cache_len, w_kv_b, out, lse, &a);
+  return run_decode(p, a, static_cast<char*>(workspace), s);
+}
+
+size_t mla_fwd_absorbed_workspace_size(const mla_explicit_desc* desc) {
+  AbsorbedPlan p;
+  if (make_absorbed_plan(desc, &p) != MLA_OK) return 0;
+  return std::max<size_t>(p.total, 1);
+}
+
+mla_status mla_fwd_absorbed(const mla_explicit_desc* desc, const void* q_nope, const void* q_pe,
+                            const void* c_kv, const void* k_pe, const void* w_kv_b, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  AbsorbedPlan p;
+  mla_status st = make_absorbed_plan(desc, &p);
+  if (st != MLA_OK) return st;
+  const bool has_q = desc->s_q > 0, has_kv = desc->s_kv > 0;
+  if (w_kv_b == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (has_q && (q_nope == nullptr || q_pe == nullptr || out == nullptr)) return MLA_ERR_INVALID_ARGUMENT;
+  if (has_kv && (c_kv == nullptr || k_pe == nullptr)) return MLA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (p.total > 0 && workspace == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (!has_q) return MLA_OK;
+  if (!aligned16(w_kv_b) || !aligned16(workspace)) return MLA_ERR_INVALID_ARGUMENT;
+  if (p.dec.mfma) {
+    const void* ptrs[] = {q_nope, q_pe, out};
+    for (const void* q : ptrs)
+      if (!aligned16(q)) return MLA_ERR_INVALID_ARGUMENT;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  ExplicitArgs ea{};
+  ea.B = desc->batch; ea.Sq = desc->s_q; ea.Skv = desc->s_kv; ea.H = desc->n_heads;
+  ea.dkv = desc->d_kv; ea.dn = desc->d_nope; ea.dr = desc->d_rope; ea.dv = desc->d_v;
+  ea.q_pos0 = desc->q_pos0; ea.kv_pos0 = desc->kv_pos0; ea.causal = desc->causal;
+  ea.scale = desc->softmax_scale; ea.rope_base = desc->rope_base;
+  ea.in_dt = desc->in_dtype; ea.out_dt = desc->out_dtype;
+  ea.c_kv = c_kv; ea.k_pe = k_pe;
+  void* cache = ws + p.off_cache;
+  int32_t* len = reinterpret_cast<int32_t*>(ws + p.off_len);
+  int64_t* pos = reinterpret_cast<int64_t*>(ws + p.off_pos);
   hipError_t e;
-  if (p.mfma) {
-    uint16_t* qt = reinterpret_cast<uint16_t*>(ws + p.off_qt);
-    {
-      TimedLaunch t("absorb", s);
-      e = launch_absorb_bf16(a, qt, s);
-    }
-    if (e != hipSuccess) return hip_fail(e, "query absorption");
-    {
-      TimedLaunch t("mfma_split_kv", s);
-      e = launch_mfma_splitkv(a, qt, lse_part, static_cast<uint16_t*>(o_part), s);
-    }
-    if (e != hipSuccess) return hip_fail(e, "mfma split-KV attention");
-  } else {
-    float* qt = reinterpret_cast<float*>(ws + p.off_qt);
-    {
-      TimedLaunch t("simt_absorb", s);
-      e = launch_simt_absorb(a, qt, s);
-    }
-    if (e != hipSuccess) return hip_fail(e, "query absorption");
-    {
-      TimedLaunch t("simt_split_kv", s);
-      e = launch_simt_splitkv(a, qt, lse_part, static_cast<float*>(o_part), s);
-    }
-    if (e != hipSuccess) return hip_fail(e, "simt split-KV attention");
-  }
   {
-    TimedLaunch t("lse_combine", s);
-    e = launch_combine(a, lse_part, o_part, p.mfma, s);
+    TimedLaunch t("latent_cache", s);
+    e = launch_latent_cache(ea, cache, len, pos, s);
   }
-  if (e != hipSuccess) return hip_fail(e, "LSE combine");
-  return MLA_OK;
+  if (e != hipSuccess) return hip_fail(e, "latent rows");
+  DecodeArgs a;
+  fill_decode_args(&p.dd, q_nope, q_pe, cache, len, w_kv_b, out, lse, &a);
+  a.seq_per_cache = desc->s_q;
+  a.q_pos = pos;
+  a.reverse = 1;          // longest rows first
+  a.lse_seq = desc->s_q;  // lse [B, H, s_q] as in the explicit form
+  return run_decode(p.dec, a, ws, s);
 }
 
 mla_status mla_timing_begin(void) {

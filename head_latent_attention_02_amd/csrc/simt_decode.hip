@@ -26,7 +26,7 @@ simt_absorb_kernel(DecodeArgs a, float* __restrict__ qt) {
     qt[bh * dlat + c] = acc;
   }
   int L = min(max(a.cache_len[b], 0), a.max_len);
-  double pos = (double)(L > 0 ? L - 1 : 0);
+  double pos = a.q_pos != nullptr ? (double)a.q_pos[b] : (double)(L > 0 ? L - 1 : 0);
   for (int m = threadIdx.x; m < half; m += blockDim.x) {
     double theta = exp(-2.0 * (double)m / (double)a.dr * log((double)a.rope_base));
     double s, c;
@@ -67,7 +67,7 @@ simt_splitkv_kernel(DecodeArgs a, const float* __restrict__ qt, float* __restric
     int t = tt + tid;
     float s = -INFINITY;
     if (t < t1) {
-      const void* row = base + ((int64_t)b * a.cache_stride + (int64_t)t * dlat) * esz;
+      const void* row = base + ((int64_t)(b / a.seq_per_cache) * a.cache_stride + (int64_t)t * dlat) * esz;
       float dot = 0.f;
       for (int d = 0; d < dlat; ++d) dot += qs[d] * load_elem<DT>(row, d);
       s = dot * a.scale;
@@ -94,7 +94,7 @@ simt_splitkv_kernel(DecodeArgs a, const float* __restrict__ qt, float* __restric
       if (c >= a.dkv) break;
       float o = acc[u] * alpha;
       for (int q = 0; q < nt; ++q) {
-        const void* row = base + ((int64_t)b * a.cache_stride + (int64_t)(tt + q) * dlat) * esz;
+        const void* row = base + ((int64_t)(b / a.seq_per_cache) * a.cache_stride + (int64_t)(tt + q) * dlat) * esz;
         o += ps[q] * load_elem<DT>(row, c);
       }
       acc[u] = o;

@@ -31,6 +31,7 @@ MLA_ALGO_MFMA = 2
 EXPORTED_SYMBOLS = (
     "mla_fwd_explicit_workspace_size", "mla_fwd_explicit", "mla_fwd_explicit_workspace_layout",
     "mla_decode_absorbed_workspace_size", "mla_decode_absorbed", "mla_decode_absorbed_workspace_layout",
+    "mla_fwd_absorbed_workspace_size", "mla_fwd_absorbed",
     "mla_status_string", "mla_last_error", "mla_build_info",
     "mla_timing_begin", "mla_timing_end", "mla_timing_reset", "mla_timing_count", "mla_timing_get",
 )
@@ -80,6 +81,10 @@ def _lib() -> ctypes.CDLL:
         lib.mla_fwd_explicit_workspace_size.restype = sz
         lib.mla_fwd_explicit.argtypes = [ctypes.POINTER(MlaExplicitDesc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.mla_fwd_explicit.restype = ctypes.c_int
+        lib.mla_fwd_absorbed_workspace_size.argtypes = [ctypes.POINTER(MlaExplicitDesc)]
+        lib.mla_fwd_absorbed_workspace_size.restype = sz
+        lib.mla_fwd_absorbed.argtypes = [ctypes.POINTER(MlaExplicitDesc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.mla_fwd_absorbed.restype = ctypes.c_int
         lib.mla_fwd_explicit_workspace_layout.argtypes = [ctypes.POINTER(MlaExplicitDesc), ctypes.POINTER(sz)]
         lib.mla_fwd_explicit_workspace_layout.restype = ctypes.c_int
         lib.mla_decode_absorbed_workspace_size.argtypes = [ctypes.POINTER(MlaDecodeDesc)]
@@ -156,18 +161,36 @@ def mla_fwd_explicit_workspace_layout(desc: MlaExplicitDesc) -> tuple:
     return tuple(int(x) for x in off)
 
 
+def mla_fwd_absorbed_workspace_size(desc: MlaExplicitDesc) -> int:
+    return int(_lib().mla_fwd_absorbed_workspace_size(ctypes.byref(desc)))
+
+
+def mla_fwd_absorbed(q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
+                     w_kv_b: torch.Tensor, **kw):
+    """Absorbed-form forward of the explicit problem; see mla_fwd_absorbed in
+    include/mla.h.  Same arguments and results as mla_fwd_explicit."""
+    return _fwd(False, q_nope, q_pe, c_kv, k_pe, w_kv_b, **kw)
+
+
 def mla_fwd_explicit(q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
-                     w_kv_b: torch.Tensor, *, q_pos0: int = 0, kv_pos0: int = 0, causal: bool = True,
-                     softmax_scale: Optional[float] = None, rope_base: float = 10000.0,
-                     out_dtype: torch.dtype = torch.float32, algo: int = MLA_ALGO_AUTO,
-                     return_lse: bool = True, out: Optional[torch.Tensor] = None,
-                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                     w_kv_b: torch.Tensor, **kw):
     """Explicit-form MLA forward; see mla_fwd_explicit in include/mla.h.
 
     Shapes: q_nope [B,S_q,H,d_nope], q_pe [B,S_q,H,d_rope], c_kv [B,S_kv,d_kv],
-    k_pe [B,S_kv,d_rope], w_kv_b [H*(d_nope+d_v), d_kv].  Returns (out, lse,
-    workspace); lse is None when return_lse is False.
+    k_pe [B,S_kv,d_rope], w_kv_b [H*(d_nope+d_v), d_kv].  Keywords: q_pos0,
+    kv_pos0, causal, softmax_scale, rope_base, out_dtype, algo, return_lse,
+    out, lse, workspace.  Returns (out, lse, workspace); lse is None when
+    return_lse is False.
     """
+    return _fwd(True, q_nope, q_pe, c_kv, k_pe, w_kv_b, **kw)
+
+
+def _fwd(explicit: bool, q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
+         w_kv_b: torch.Tensor, *, q_pos0: int = 0, kv_pos0: int = 0, causal: bool = True,
+         softmax_scale: Optional[float] = None, rope_base: float = 10000.0,
+         out_dtype: torch.dtype = torch.float32, algo: int = MLA_ALGO_AUTO,
+         return_lse: bool = True, out: Optional[torch.Tensor] = None,
+         lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     B, S_q, H, d_nope = q_nope.shape
     S_kv, d_kv = c_kv.shape[1], c_kv.shape[2]
     d_rope = q_pe.shape[-1]
@@ -182,20 +205,21 @@ def mla_fwd_explicit(q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tenso
                          d_v=d_v, q_pos0=q_pos0, kv_pos0=kv_pos0, causal=causal, softmax_scale=softmax_scale,
                          rope_base=rope_base, in_dtype=dt, out_dtype=_dtype_code(out_dtype), algo=algo)
     dev = q_nope.device
-    ws_bytes = mla_fwd_explicit_workspace_size(desc)
+    name = "mla_fwd_explicit" if explicit else "mla_fwd_absorbed"
+    ws_bytes = (mla_fwd_explicit_workspace_size if explicit else mla_fwd_absorbed_workspace_size)(desc)
     if ws_bytes == 0 and S_q > 0:
         _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,
-               "mla_fwd_explicit_workspace_size")
+               name + "_workspace_size")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty((B, S_q, H, d_v), dtype=out_dtype, device=dev)
     if return_lse and lse is None:
         lse = torch.empty((B, H, S_q), dtype=torch.float32, device=dev)
-    st = _lib().mla_fwd_explicit(ctypes.byref(desc), _ptr(q_nope), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe),
-                                 _ptr(w_kv_b), _ptr(out), _ptr(lse) if return_lse else None,
-                                 workspace.data_ptr(), workspace.numel(), _stream(dev))
-    _check(st, "mla_fwd_explicit")
+    st = getattr(_lib(), name)(ctypes.byref(desc), _ptr(q_nope), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe),
+                               _ptr(w_kv_b), _ptr(out), _ptr(lse) if return_lse else None,
+                               workspace.data_ptr(), workspace.numel(), _stream(dev))
+    _check(st, name)
     return out, (lse if return_lse else None), workspace
 
 

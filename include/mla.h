@@ -203,6 +203,39 @@ mla_status mla_decode_absorbed_workspace_layout(const mla_decode_desc* desc,
                                                 size_t offsets[4]);
 
 /* ------------------------------------------------------------------------ */
+/* Absorbed-form forward of the explicit problem                            */
+/* ------------------------------------------------------------------------ */
+
+/* The forward of mla_fwd_explicit computed in absorbed form ("A
+ * Training-Memory Regression in MLA Sequence Parallelism ... LAGA" (Pith
+ * review), Fig. 2 "Absorbed (B2)"): each query is carried into latent space,
+ * q~ = [W_UK[h]^T q_nope ; R(q_pe, q_pos0 + i)], attends to the latent rows
+ * [c_kv[j] ; R(k_pe[j], kv_pos0 + j)] with c_kv[j] as the values, and the
+ * merged latent accumulator is mapped to d_v by W_UV[h].  Mathematically the
+ * same result as the explicit form (equal up to rounding).
+ *
+ * Arguments, layouts, ownership, validation and errors are those of
+ * mla_fwd_explicit: out [B, s_q, H, d_v], lse [B, H, s_q] or NULL.  It runs
+ * the decode path with every query row as its own sequence (one KV chunk
+ * each, longest rows first), so its eligibility for the MFMA kernels is the
+ * decode step's (bf16, d_kv 512, d_nope 128, d_rope 64, d_v 128, n_heads a
+ * multiple of 16 up to 128); other shapes take the SIMT kernels.
+ *
+ * Workspace (mla_fwd_absorbed_workspace_size bytes, 16-byte aligned): the
+ * decode intermediates for B * s_q sequences (q~, lse_part, o_part) followed
+ * by the latent rows [B, s_kv, d_kv + d_rope] (in_dtype) and each row's
+ * visible-key count and RoPE position. */
+size_t mla_fwd_absorbed_workspace_size(const mla_explicit_desc* desc);
+
+mla_status mla_fwd_absorbed(const mla_explicit_desc* desc,
+                            const void* q_nope, const void* q_pe,
+                            const void* c_kv, const void* k_pe,
+                            const void* w_kv_b,
+                            void* out, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Per-kernel timing (profiling aid; not needed for computing)               */
 /* ------------------------------------------------------------------------ */
 /* Between mla_timing_begin() and mla_timing_end() on the calling thread, each

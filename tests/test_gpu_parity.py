@@ -401,3 +401,69 @@ def test_decode_tiny_fp32(mla):
     r = _oracle_decode(cfg, x)
     _compare(out.cpu().numpy(), r["out"], False, "tiny fp32 decode out")
     _compare_lse(lse.cpu().numpy(), r["lse"], False, "tiny fp32 decode")
+
+
+# ------------------------------------------------------ absorbed forward ----
+def _run_absorbed(mla, cfg, x, *, algo=0):
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    t = {k: _dev(v, tdt) for k, v in x.items()}
+    desc = mla.explicit_desc(batch=cfg.batch, s_q=cfg.s_q, s_kv=cfg.s_kv, n_heads=cfg.n_heads, d_kv=cfg.d_kv,
+                             d_nope=cfg.d_nope, d_rope=cfg.d_rope, d_v=cfg.d_v, q_pos0=cfg.q_pos0,
+                             kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale,
+                             in_dtype=mla.MLA_BF16 if cfg.dtype == "bf16" else mla.MLA_FP32, algo=algo)
+    ws = _poisoned(mla.mla_fwd_absorbed_workspace_size(desc))
+    _say(f"absorbed {cfg.name}: B={cfg.batch} Sq={cfg.s_q} Skv={cfg.s_kv} H={cfg.n_heads} q_pos0={cfg.q_pos0} "
+         f"kv_pos0={cfg.kv_pos0} causal={cfg.causal} algo={algo}")
+    o, l, _ = mla.mla_fwd_absorbed(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], q_pos0=cfg.q_pos0,
+                                   kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale,
+                                   algo=algo, workspace=ws)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), l.cpu().numpy()
+
+
+def test_absorbed_tiny_fp32(mla):
+    # the oracle's explicit form is the reference: the two forms agree to 1e-10 there
+    cfg = I.EXPLICIT_CONFIGS["tiny_fp32"]
+    x = I.make_explicit_inputs(cfg)
+    o, l = _run_absorbed(mla, cfg, x)
+    ro, rl = _oracle_explicit(cfg, x)
+    _compare(o, ro, False, "absorbed tiny_fp32 out")
+    _compare_lse(l, rl, False, "absorbed tiny_fp32")
+
+
+ABS_EDGE = [
+    I.small_explicit("abs_ragged", batch=2, s_q=300, s_kv=300, n_heads=16, d_kv=512, d_nope=128, d_rope=64,
+                     d_v=128, dtype="bf16", seed=501),
+    I.small_explicit("abs_offset_q", s_q=100, s_kv=612, n_heads=16, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=512, dtype="bf16", seed=502),
+    I.small_explicit("abs_masked_rows", s_q=96, s_kv=96, n_heads=16, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=0, kv_pos0=40, dtype="bf16", seed=503),
+    I.small_explicit("abs_noncausal", s_q=77, s_kv=131, n_heads=16, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     causal=False, dtype="bf16", seed=504),
+    I.small_explicit("abs_far_pos", s_q=64, s_kv=320, n_heads=32, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=30000, kv_pos0=29744, dtype="bf16", seed=505),
+    I.small_explicit("abs_three_heads", batch=2, s_q=70, s_kv=70, n_heads=3, d_kv=512, d_nope=128, d_rope=64,
+                     d_v=128, dtype="bf16", seed=506),
+]
+
+
+@pytest.mark.parametrize("cfg", ABS_EDGE, ids=lambda c: c.name)
+def test_absorbed_edges(mla, cfg):
+    x = I.make_explicit_inputs(cfg)
+    o, l = _run_absorbed(mla, cfg, x)
+    ro, rl = _oracle_explicit(cfg, x)
+    _compare(o, ro, True, f"{cfg.name} out")
+    _compare_lse(l, rl, True, cfg.name)
+
+
+def test_absorbed_v3_sampled(mla):
+    cfg = I.EXPLICIT_CONFIGS["v3_bf16"]
+    x = I.make_explicit_inputs(cfg)
+    o, l = _run_absorbed(mla, cfg, x)
+    rng = np.random.default_rng(9)
+    heads = [0, 1, 63, 64, 126, 127]
+    rows = _sample_rows(cfg.s_q, rng)
+    ro, rl = _oracle_explicit(cfg, x, heads=heads, rows=rows)
+    _compare(o[:, rows][:, :, heads], ro, True, "absorbed v3 sampled out")
+    _compare_lse(l[:, heads][:, :, rows], rl, True, "absorbed v3")
+    assert np.isfinite(o).all() and np.isfinite(l).all()
