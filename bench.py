@@ -91,6 +91,42 @@ def hbm_traffic(kernel: str):
     return c["fetch_kib"] * 1024 / c["fetch_factor"] + c["write_kib"] * 1024 / c["write_factor"]
 
 
+def absorbed_forward(mla, torch, ecfg, t, fl, args):
+    """The explicit workload in absorbed form (mla_fwd_absorbed): time per call
+    (eager, HIP events around each call, after one untimed call) and the
+    workspace each form needs at 4K / 8K / 16K tokens (sizes from the library)."""
+    log(f"absorbed-form forward: {args.steps} calls")
+    out = torch.empty((ecfg.batch, ecfg.s_q, ecfg.n_heads, ecfg.d_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((ecfg.batch, ecfg.n_heads, ecfg.s_q), dtype=torch.float32, device="cuda")
+    kw = dict(q_pos0=ecfg.q_pos0, kv_pos0=ecfg.kv_pos0, causal=ecfg.causal, softmax_scale=ecfg.softmax_scale,
+              out=out, lse=lse)
+    _, _, ws = mla.mla_fwd_absorbed(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], **kw)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ms = []
+    for _ in range(args.steps):
+        ev[0].record()
+        mla.mla_fwd_absorbed(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], workspace=ws, **kw)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms.append(ev[0].elapsed_time(ev[1]))
+    avg = float(np.mean(ms))
+    H, S = ecfg.n_heads, ecfg.s_q
+    pairs = fl["attention"] / (2 * H * (ecfg.d_nope + ecfg.d_rope + ecfg.d_v))
+    flop = (2 * pairs * H * (ecfg.d_kv + ecfg.d_rope + ecfg.d_kv)
+            + 2 * ecfg.batch * S * H * ecfg.d_nope * ecfg.d_kv + 2 * ecfg.batch * S * H * ecfg.d_kv * ecfg.d_v)
+    mem = []
+    for n in (4096, 8192, 16384):
+        d = mla.explicit_desc(batch=ecfg.batch, s_q=n, s_kv=n, n_heads=H, d_kv=ecfg.d_kv, d_nope=ecfg.d_nope,
+                              d_rope=ecfg.d_rope, d_v=ecfg.d_v, causal=ecfg.causal)
+        mem.append({"tokens": n, "explicit_workspace_bytes": mla.mla_fwd_explicit_workspace_size(d),
+                    "absorbed_workspace_bytes": mla.mla_fwd_absorbed_workspace_size(d)})
+    slope = [(m["absorbed_workspace_bytes"] - m["explicit_workspace_bytes"]) / m["tokens"] for m in mem]
+    return {"ms": avg, "algorithmic_flop": flop, "tflops": flop / (avg * 1e-3) / 1e12,
+            "explicit_equivalent_tflops": fl["total"] / (avg * 1e-3) / 1e12,
+            "workspace": mem, "gap_bytes_per_token": slope}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -105,6 +141,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle baseline sample")
+    p.add_argument("--no-absorbed", action="store_true",
+                   help="skip the absorbed-form forward of the explicit workload")
     p.add_argument("--no-graph", action="store_true",
                    help="time the step as eager calls (no HIP graph replay)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -387,6 +425,9 @@ def main():
         "timing": {"step": "hip_graph_replay" if graph is not None else "eager", "eager": eager,
                    "graph": graph},
     }
+
+    if not args.no_absorbed:
+        res["absorbed_forward"] = absorbed_forward(mla, torch, ecfg, t, fl, args)
 
     if not args.no_cpu_baseline:
         log("oracle CPU baseline on a bounded sample")
