@@ -196,3 +196,37 @@ def test_flop_and_byte_accounting():
     assert sp.visible_pairs() == sum(6144 + i + 1 for i in range(2048))
     dec = I.DECODE_CONFIGS["v3_decode_b64_32k"].algorithmic_bytes()
     assert dec["cache"] == 64 * 32768 * 576 * 2
+
+
+def test_absorbed_workspace_and_validation():
+    lib = mla.library()
+    d = _v3_desc()
+    ws = mla.mla_fwd_absorbed_workspace_size(d)
+    # q~ bf16 and the fp16 per-row latent outputs for 4096 rows x 128 heads,
+    # plus the latent rows and small per-row arrays
+    rows = 4096 * 128
+    need = rows * 576 * 2 + rows * 512 * 2 + 4096 * 576 * 2
+    assert need <= ws < need + (8 << 20)
+    for field, value in [("batch", 0), ("d_rope", 63), ("causal", 2), ("in_dtype", 7), ("algo", 9)]:
+        dd = _v3_desc()
+        setattr(dd, field, value)
+        assert mla.mla_fwd_absorbed_workspace_size(dd) == 0
+        assert lib.mla_fwd_absorbed(ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                    None) == mla.MLA_ERR_INVALID_ARGUMENT
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None]
+    for i in range(6):
+        a = list(args)
+        a[i] = None
+        assert lib.mla_fwd_absorbed(ctypes.byref(d), *a) == mla.MLA_ERR_INVALID_ARGUMENT
+    a = list(args)
+    a[8] = ws - 1
+    assert lib.mla_fwd_absorbed(ctypes.byref(d), *a) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    # the MFMA kernels need a multiple of 16 heads
+    d2 = _v3_desc(n_heads=24, algo=mla.MLA_ALGO_MFMA)
+    assert mla.mla_fwd_absorbed_workspace_size(d2) == 0
+    assert lib.mla_fwd_absorbed(ctypes.byref(d2), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                None) == mla.MLA_ERR_UNSUPPORTED
+    # empty query set: valid and a no-op that touches nothing
+    d0 = _v3_desc(s_q=0)
+    assert lib.mla_fwd_absorbed(ctypes.byref(d0), None, None, FAKE, FAKE, FAKE, None, None, FAKE,
+                                mla.mla_fwd_absorbed_workspace_size(d0), None) == mla.MLA_OK
