@@ -64,14 +64,14 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "2bf9eca3de581d72", "fetch_kib": 349526.1, "write_kib": 292863.9,
-                      "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "68ab45b86f5ca350", "fetch_kib": 100821.9, "write_kib": 273810.3,
-                          "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "ee91aba76685b693", "fetch_kib": 1216715.9, "write_kib": 131584.0,
+    "mfma_attention": {"digest": "2bf9eca3de581d72", "fetch_kib": 351118.4, "write_kib": 292863.7,
                      "fetch_factor": 0.50002, "write_factor": 1.0},
-    "lse_combine": {"digest": "d55fbd5cb131989a", "fetch_kib": 84068.5, "write_kib": 4352.3,
-                   "fetch_factor": 0.50002, "write_factor": 1.0},
+    "mfma_up_projection": {"digest": "68ab45b86f5ca350", "fetch_kib": 100828.7, "write_kib": 273802.5,
+                         "fetch_factor": 0.50002, "write_factor": 1.0},
+    "mfma_split_kv": {"digest": "9b6b211f54df7297", "fetch_kib": 1216723.1, "write_kib": 131584.0,
+                    "fetch_factor": 0.50002, "write_factor": 1.0},
+    "lse_combine": {"digest": "d55fbd5cb131989a", "fetch_kib": 84068.6, "write_kib": 4352.1,
+                  "fetch_factor": 0.50002, "write_factor": 1.0},
 }
 
 

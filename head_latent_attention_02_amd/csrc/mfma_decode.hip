@@ -429,42 +429,30 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
     const uint16_t* Pv = &Ps[T & 1][0];
     uint16_t* Pn = &Ps[(T + 1) & 1][0];
     const int tt = t0 + (T + 1) * TT;
-    bf16x8_t cf[DT_W / 2], pg[2];
+    bf16x8_t cf[DT_W], pg[2];
 #pragma unroll
     for (int j = 0; j < DT_W / 2; ++j) cf[j] = vfrag(Cv, j);
     pg[0] = pfrag(Pv, 0);
     score_phase(Cn);
-    // value MFMA v = 32 half + 4 g + j; a softmax unit after every second one
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (half == 1) {
-#pragma unroll
-        for (int j = 0; j < DT_W / 2; ++j) cf[j] = vfrag(Cv, DT_W / 2 + j);
-        pg[0] = pfrag(Pv, 0);
-      }
-      static_for<NHT>([&](auto gc) __attribute__((always_inline)) {
-        constexpr int g = decltype(gc)::value;
-        if constexpr (g + 1 < NHT) pg[(g + 1) & 1] = pfrag(Pv, g + 1);
-        static_for<DT_W / 2>([&](auto jc) __attribute__((always_inline)) {
-          constexpr int j = decltype(jc)::value;
-          mfma_agpr(oacc[half * (DT_W / 2) + j][g], cf[j], pg[g & 1]);
-          constexpr int v = 4 * g + j;           // within the half
-          if constexpr (v % 2 == 0) {
-            constexpr int u = (v / 2) + 0;       // units 0 .. 2 NHT - 1 of this half
-            if (half == 0) {
-              if constexpr (u < N_UNITS) softmax_unit(std::integral_constant<int, u>{}, tt, Pn);
-            } else {
-              if constexpr (u + 2 * NHT < N_UNITS) softmax_unit(std::integral_constant<int, u + 2 * NHT>{}, tt, Pn);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        });
+    for (int j = DT_W / 2; j < DT_W; ++j) cf[j] = vfrag(Cv, j);
+    // value MFMA v = DT_W g + j (head group major, so each P^T fragment is read
+    // once); a softmax unit after every second one
+    static_for<NHT>([&](auto gc) __attribute__((always_inline)) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g + 1 < NHT) pg[(g + 1) & 1] = pfrag(Pv, g + 1);
+      static_for<DT_W>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        mfma_agpr(oacc[j][g], cf[j], pg[g & 1]);
+        constexpr int v = DT_W * g + j;
+        if constexpr (v % 2 == 0 && v / 2 < N_UNITS) softmax_unit(std::integral_constant<int, v / 2>{}, tt, Pn);
+        __builtin_amdgcn_sched_barrier(0);
       });
-    }
+    });
     // units the value product had no room for (few head groups)
     static_for<N_UNITS>([&](auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;
-      if constexpr (u >= 4 * NHT) softmax_unit(uc, tt, Pn);
+      if constexpr (u >= DT_W * NHT / 2) softmax_unit(uc, tt, Pn);
     });
   };
 
