@@ -260,6 +260,11 @@ DEC_EDGE = [
     (I.small_decode("stride", batch=3, cache_len=515, n_heads=32, n_splits=3, seed=202), [515, 514, 100], 530),
     (I.small_decode("one_split", batch=2, cache_len=300, n_heads=128, n_splits=1, seed=203), [300, 299], None),
     (I.small_decode("many_splits", batch=2, cache_len=100, n_heads=16, n_splits=64, seed=204), [100, 63], None),
+    # head counts whose value loop leaves part of the softmax after it (3 head
+    # groups), fills it exactly (4) or nearly (7)
+    (I.small_decode("heads48", batch=2, cache_len=300, n_heads=48, n_splits=4, seed=205), [300, 45], None),
+    (I.small_decode("heads64", batch=2, cache_len=257, n_heads=64, n_splits=2, seed=206), [257, 33], None),
+    (I.small_decode("heads112", batch=2, cache_len=200, n_heads=112, n_splits=5, seed=207), [200, 199], None),
 ]
 
 
