@@ -92,7 +92,10 @@ bool explicit_shape_ok(const mla_explicit_desc* d) {
   if (d->d_kv < 1 || d->d_nope < 1 || d->d_v < 1 || d->d_rope < 2 || (d->d_rope & 1)) return false;
   if (d->causal != 0 && d->causal != 1) return false;
   if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype) || !valid_algo(d->algo)) return false;
-  if (!std::isfinite(d->softmax_scale) || !std::isfinite(d->rope_base) || !(d->rope_base > 0.f)) return false;
+  // the MFMA kernels take the row max of raw scores, which equals the max of
+  // the scaled logits only for a positive scale
+  if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return false;
+  if (!std::isfinite(d->rope_base) || !(d->rope_base > 0.f)) return false;
   // element counts must stay addressable with 64-bit offsets and 32-bit grids
   const int64_t B = d->batch, H = d->n_heads;
   if (B * d->s_q * H > (int64_t)1 << 40 || B * d->s_kv > (int64_t)1 << 36) return false;
@@ -167,7 +170,10 @@ bool decode_shape_ok(const mla_decode_desc* d) {
   if (d->batch < 1 || d->n_heads < 1 || d->max_cache_len < 0 || d->n_splits < 1) return false;
   if (d->d_kv < 1 || d->d_nope < 1 || d->d_v < 1 || d->d_rope < 2 || (d->d_rope & 1)) return false;
   if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype) || !valid_algo(d->algo)) return false;
-  if (!std::isfinite(d->softmax_scale) || !std::isfinite(d->rope_base) || !(d->rope_base > 0.f)) return false;
+  // the MFMA kernels take the row max of raw scores, which equals the max of
+  // the scaled logits only for a positive scale
+  if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return false;
+  if (!std::isfinite(d->rope_base) || !(d->rope_base > 0.f)) return false;
   const int64_t row = (int64_t)d->d_kv + d->d_rope;
   if (d->cache_batch_stride < (int64_t)d->max_cache_len * row) return false;
   if ((int64_t)d->batch * d->n_heads > (int64_t)1 << 30) return false;

@@ -141,6 +141,34 @@ def _check(status: int, where: str):
         raise MlaError(status, where)
 
 
+def _expect(t, name: str, shape: tuple, dtype: torch.dtype, device: torch.device):
+    """Raise ValueError unless ``t`` is a dense row-major tensor of exactly
+    ``shape`` and ``dtype`` on ``device``: the library reads and writes these
+    buffers through raw pointers with the sizes the descriptor states."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _expect_workspace(ws, device: torch.device):
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.dim() != 1:
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor (its length is its size in bytes)")
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+
+
+def _expect_cuda(device: torch.device):
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {device}")
+
+
 # ----------------------------------------------------------------- explicit --
 def explicit_desc(*, batch, s_q, s_kv, n_heads, d_kv, d_nope, d_rope, d_v, q_pos0=0, kv_pos0=0,
                   causal=True, softmax_scale=None, rope_base=10000.0, in_dtype=MLA_BF16,
@@ -191,20 +219,31 @@ def _fwd(explicit: bool, q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.T
          out_dtype: torch.dtype = torch.float32, algo: int = MLA_ALGO_AUTO,
          return_lse: bool = True, out: Optional[torch.Tensor] = None,
          lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    if q_nope.dim() != 4 or q_pe.dim() != 4 or c_kv.dim() != 3 or k_pe.dim() != 3 or w_kv_b.dim() != 2:
+        raise ValueError("expected q_nope, q_pe [B,S_q,H,*], c_kv, k_pe [B,S_kv,*], w_kv_b [H*(d_nope+d_v), d_kv]")
     B, S_q, H, d_nope = q_nope.shape
     S_kv, d_kv = c_kv.shape[1], c_kv.shape[2]
     d_rope = q_pe.shape[-1]
+    if H < 1 or w_kv_b.shape[0] % H != 0 or w_kv_b.shape[0] // H <= d_nope:
+        raise ValueError(f"w_kv_b rows ({w_kv_b.shape[0]}) must be H*(d_nope+d_v) with H={H}, d_nope={d_nope}")
     d_v = w_kv_b.shape[0] // H - d_nope
     dt = _dtype_code(q_nope.dtype)
-    for t in (q_pe, c_kv, k_pe, w_kv_b):
-        if t.dtype != q_nope.dtype or not t.is_contiguous() or t.device != q_nope.device:
-            raise ValueError("all inputs must share dtype and device and be contiguous")
-    if not q_nope.is_contiguous():
-        raise ValueError("q_nope must be contiguous")
+    dev = q_nope.device
+    _expect(q_nope, "q_nope", (B, S_q, H, d_nope), q_nope.dtype, dev)
+    _expect(q_pe, "q_pe", (B, S_q, H, d_rope), q_nope.dtype, dev)
+    _expect(c_kv, "c_kv", (B, S_kv, d_kv), q_nope.dtype, dev)
+    _expect(k_pe, "k_pe", (B, S_kv, d_rope), q_nope.dtype, dev)
+    _expect(w_kv_b, "w_kv_b", (H * (d_nope + d_v), d_kv), q_nope.dtype, dev)
+    if out is not None:
+        _expect(out, "out", (B, S_q, H, d_v), out_dtype, dev)
+    if return_lse and lse is not None:
+        _expect(lse, "lse", (B, H, S_q), torch.float32, dev)
+    if workspace is not None:
+        _expect_workspace(workspace, dev)
+    _expect_cuda(dev)
     desc = explicit_desc(batch=B, s_q=S_q, s_kv=S_kv, n_heads=H, d_kv=d_kv, d_nope=d_nope, d_rope=d_rope,
                          d_v=d_v, q_pos0=q_pos0, kv_pos0=kv_pos0, causal=causal, softmax_scale=softmax_scale,
                          rope_base=rope_base, in_dtype=dt, out_dtype=_dtype_code(out_dtype), algo=algo)
-    dev = q_nope.device
     name = "mla_fwd_explicit" if explicit else "mla_fwd_absorbed"
     ws_bytes = (mla_fwd_explicit_workspace_size if explicit else mla_fwd_absorbed_workspace_size)(desc)
     if ws_bytes == 0 and S_q > 0:
@@ -259,22 +298,44 @@ def mla_decode_absorbed(q_nope: torch.Tensor, q_pe: torch.Tensor, kv_cache: torc
     sequence stride may exceed L_max rows; rows must be contiguous),
     cache_len [B] int32 on the device, w_kv_b [H*(d_nope+d_v), d_kv].
     """
+    if q_nope.dim() != 3 or q_pe.dim() != 3 or kv_cache.dim() != 3 or w_kv_b.dim() != 2:
+        raise ValueError("expected q_nope, q_pe [B,H,*], kv_cache [B,L_max,d_kv+d_rope], "
+                         "w_kv_b [H*(d_nope+d_v), d_kv]")
     B, H, d_nope = q_nope.shape
     d_rope = q_pe.shape[-1]
     row = kv_cache.shape[-1]
     if d_kv is None:
         d_kv = row - d_rope
+    if d_kv + d_rope != row:
+        raise ValueError(f"kv_cache rows are {row} wide, expected d_kv + d_rope = {d_kv + d_rope}")
+    if H < 1 or w_kv_b.shape[0] % H != 0 or w_kv_b.shape[0] // H <= d_nope:
+        raise ValueError(f"w_kv_b rows ({w_kv_b.shape[0]}) must be H*(d_nope+d_v) with H={H}, d_nope={d_nope}")
     d_v = w_kv_b.shape[0] // H - d_nope
-    if kv_cache.stride(-1) != 1 or kv_cache.stride(-2) != row:
-        raise ValueError("kv_cache rows must be contiguous")
-    if cache_len.dtype != torch.int32:
-        raise ValueError("cache_len must be int32")
+    dev = q_nope.device
+    _expect(q_nope, "q_nope", (B, H, d_nope), q_nope.dtype, dev)
+    _expect(q_pe, "q_pe", (B, H, d_rope), q_nope.dtype, dev)
+    _expect(w_kv_b, "w_kv_b", (H * (d_nope + d_v), d_kv), q_nope.dtype, dev)
+    _expect(cache_len, "cache_len", (B,), torch.int32, dev)
+    if kv_cache.shape[0] != B:
+        raise ValueError(f"kv_cache holds {kv_cache.shape[0]} sequences, expected {B}")
+    if kv_cache.dtype != q_nope.dtype:
+        raise ValueError(f"kv_cache has dtype {kv_cache.dtype}, expected {q_nope.dtype}")
+    if kv_cache.device != dev:
+        raise ValueError(f"kv_cache is on {kv_cache.device}, expected {dev}")
+    if kv_cache.stride(-1) != 1 or kv_cache.stride(-2) != row or kv_cache.stride(0) < kv_cache.shape[1] * row:
+        raise ValueError("kv_cache rows must be contiguous and sequences must not overlap")
+    if out is not None:
+        _expect(out, "out", (B, H, d_v), out_dtype, dev)
+    if return_lse and lse is not None:
+        _expect(lse, "lse", (B, H), torch.float32, dev)
+    if workspace is not None:
+        _expect_workspace(workspace, dev)
+    _expect_cuda(dev)
     dt = _dtype_code(q_nope.dtype)
     desc = decode_desc(batch=B, n_heads=H, d_kv=d_kv, d_nope=d_nope, d_rope=d_rope, d_v=d_v,
                        max_cache_len=kv_cache.shape[1], cache_batch_stride=kv_cache.stride(0),
                        n_splits=n_splits, softmax_scale=softmax_scale, rope_base=rope_base, in_dtype=dt,
                        out_dtype=_dtype_code(out_dtype), algo=algo)
-    dev = q_nope.device
     ws_bytes = mla_decode_absorbed_workspace_size(desc)
     if ws_bytes == 0:
         _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,

@@ -43,7 +43,13 @@
  *     map): W_kv_b is the linear map from d_kv to H*(d_nope+d_v) stored one
  *     row per output feature, i.e. [H*(d_nope+d_v), d_kv].  Rows
  *     h*(d_nope+d_v) .. h*(d_nope+d_v)+d_nope-1 are head h's key part W_UK[h],
- *     the next d_v rows its value part W_UV[h].
+ *     the next d_v rows its value part W_UV[h].  This is the transpose of a
+ *     d_kv-major [d_kv, H*(d_nope+d_v)] layout that the literal "512 x
+ *     (128*256)" would also allow; it is chosen because the LAGA page ("What
+ *     carries the argument") writes the absorbed query as the transpose of
+ *     W_kv_b applied to q_nope, which under this layout is W_UK[h]^T q with
+ *     no reshuffle, and because a head shard is then one contiguous block of
+ *     rows.  A caller holding the d_kv-major form passes its transpose.
  *   - RoPE: rotate-half pairs (m, m + d_rope/2), theta_m = base^(-2m/d_rope),
  *     angle = absolute position * theta_m, angles formed in fp64.
  *   - LSE outputs are natural logs of the sum of exp of the scaled logits;
@@ -92,7 +98,8 @@ typedef struct {
   int64_t q_pos0;       /* absolute position of query row 0                    */
   int64_t kv_pos0;      /* absolute position of latent row 0                   */
   int32_t causal;       /* 1: key j visible to query i iff kv_pos0+j <= q_pos0+i */
-  float softmax_scale;  /* multiplies the whole logit; usually 1/sqrt(d_nope+d_rope) */
+  float softmax_scale;  /* multiplies the whole logit; usually 1/sqrt(d_nope+d_rope).
+                           Finite and > 0, else MLA_ERR_INVALID_ARGUMENT        */
   float rope_base;      /* RoPE base, > 1 (10000)                              */
   mla_dtype in_dtype;   /* dtype of q_nope, q_pe, c_kv, k_pe, w_kv_b            */
   mla_dtype out_dtype;  /* dtype of out (lse is always fp32)                   */
@@ -152,7 +159,7 @@ typedef struct {
   int64_t cache_batch_stride;/* elements between sequences in kv_cache,
                                 >= max_cache_len * (d_kv + d_rope)             */
   int32_t n_splits;          /* chunks per sequence, >= 1                       */
-  float softmax_scale;
+  float softmax_scale;       /* finite and > 0, else MLA_ERR_INVALID_ARGUMENT   */
   float rope_base;
   mla_dtype in_dtype;        /* dtype of q_nope, q_pe, kv_cache, w_kv_b         */
   mla_dtype out_dtype;

@@ -230,3 +230,108 @@ def test_absorbed_workspace_and_validation():
     d0 = _v3_desc(s_q=0)
     assert lib.mla_fwd_absorbed(ctypes.byref(d0), None, None, FAKE, FAKE, FAKE, None, None, FAKE,
                                 mla.mla_fwd_absorbed_workspace_size(d0), None) == mla.MLA_OK
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, float("inf")])
+def test_non_positive_scale_rejected_by_every_entry_point(scale):
+    """The MFMA kernels subtract the row max of raw scores, which is the max
+    of the scaled logits only for a positive scale; every entry point refuses
+    other scales on the host."""
+    lib = mla.library()
+    d = _v3_desc(softmax_scale=scale)
+    assert mla.mla_fwd_explicit_workspace_size(d) == 0
+    assert mla.mla_fwd_absorbed_workspace_size(d) == 0
+    for fn in (lib.mla_fwd_explicit, lib.mla_fwd_absorbed):
+        assert fn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                  None) == mla.MLA_ERR_INVALID_ARGUMENT
+    dd = _dec_desc(softmax_scale=scale)
+    assert mla.mla_decode_absorbed_workspace_size(dd) == 0
+    assert lib.mla_decode_absorbed(ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                   None) == mla.MLA_ERR_INVALID_ARGUMENT
+
+
+# ---- the binding checks every tensor before it reaches the library --------
+def _explicit_tensors(B=1, S=8, Skv=8, H=2, dn=128, dr=64, dv=128, dkv=512, dtype=None):
+    import torch
+    dtype = dtype or torch.bfloat16
+    return dict(q_nope=torch.zeros(B, S, H, dn, dtype=dtype), q_pe=torch.zeros(B, S, H, dr, dtype=dtype),
+                c_kv=torch.zeros(B, Skv, dkv, dtype=dtype), k_pe=torch.zeros(B, Skv, dr, dtype=dtype),
+                w_kv_b=torch.zeros(H * (dn + dv), dkv, dtype=dtype))
+
+
+def _call_explicit(t, **kw):
+    return mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], **kw)
+
+
+def test_binding_explicit_valid_tensors_only_fail_on_device():
+    # well-formed host tensors pass every shape / dtype / layout check and are
+    # refused only because they are not on a GPU
+    with pytest.raises(ValueError, match="GPU device"):
+        _call_explicit(_explicit_tensors())
+
+
+def _explicit_mutations():
+    import torch
+    base = _explicit_tensors
+    yield "q_pe shape", dict(base(), q_pe=torch.zeros(1, 8, 3, 64, dtype=torch.bfloat16)), {}, "q_pe"
+    yield "k_pe shape", dict(base(), k_pe=torch.zeros(1, 7, 64, dtype=torch.bfloat16)), {}, "k_pe"
+    yield "c_kv batch", dict(base(), c_kv=torch.zeros(2, 8, 512, dtype=torch.bfloat16)), {}, "c_kv"
+    yield "w_kv_b cols", dict(base(), w_kv_b=torch.zeros(512, 256, dtype=torch.bfloat16)), {}, "w_kv_b"
+    yield "w_kv_b rows", dict(base(), w_kv_b=torch.zeros(511, 512, dtype=torch.bfloat16)), {}, "w_kv_b"
+    yield "dtype mix", dict(base(), c_kv=torch.zeros(1, 8, 512, dtype=torch.float32)), {}, "c_kv"
+    t = base()
+    t["q_nope"] = torch.zeros(1, 8, 128, 2, dtype=torch.bfloat16).transpose(2, 3)
+    yield "q_nope strided", t, {}, "q_nope"
+    yield "out shape", base(), dict(out=torch.zeros(1, 8, 2, 64)), "out"
+    yield "out dtype", base(), dict(out=torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16)), "out"
+    yield "lse shape", base(), dict(lse=torch.zeros(1, 8, 2)), "lse"
+    yield "workspace dtype", base(), dict(workspace=torch.zeros(16, dtype=torch.float32)), "workspace"
+
+
+@pytest.mark.parametrize("case", list(_explicit_mutations()), ids=lambda c: c[0])
+def test_binding_explicit_rejects(case):
+    _, t, kw, what = case
+    with pytest.raises(ValueError, match=what):
+        _call_explicit(t, **kw)
+
+
+def _decode_tensors(B=2, H=16, L=8, dn=128, dr=64, dv=128, dkv=512):
+    import torch
+    bf = torch.bfloat16
+    return dict(q_nope=torch.zeros(B, H, dn, dtype=bf), q_pe=torch.zeros(B, H, dr, dtype=bf),
+                kv_cache=torch.zeros(B, L, dkv + dr, dtype=bf), cache_len=torch.full((B,), L, dtype=torch.int32),
+                w_kv_b=torch.zeros(H * (dn + dv), dkv, dtype=bf))
+
+
+def _call_decode(t, **kw):
+    return mla.mla_decode_absorbed(t["q_nope"], t["q_pe"], t["kv_cache"], t["cache_len"], t["w_kv_b"], **kw)
+
+
+def test_binding_decode_valid_tensors_only_fail_on_device():
+    with pytest.raises(ValueError, match="GPU device"):
+        _call_decode(_decode_tensors())
+
+
+def _decode_mutations():
+    import torch
+    bf = torch.bfloat16
+    base = _decode_tensors
+    yield "cache_len dtype", dict(base(), cache_len=torch.full((2,), 8, dtype=torch.int64)), {}, "cache_len"
+    yield "cache_len shape", dict(base(), cache_len=torch.full((3,), 8, dtype=torch.int32)), {}, "cache_len"
+    yield "cache batch", dict(base(), kv_cache=torch.zeros(3, 8, 576, dtype=bf)), {}, "kv_cache"
+    yield "cache dtype", dict(base(), kv_cache=torch.zeros(2, 8, 576)), {}, "kv_cache"
+    yield "cache row", dict(base(), kv_cache=torch.zeros(2, 8, 600, dtype=bf)[:, :, :576]), {}, "kv_cache"
+    yield "q_pe shape", dict(base(), q_pe=torch.zeros(2, 8, 64, dtype=bf)), {}, "q_pe"
+    yield "w_kv_b rows", dict(base(), w_kv_b=torch.zeros(16 * 256 + 1, 512, dtype=bf)), {}, "w_kv_b"
+    t = base()
+    t["q_nope"] = torch.zeros(2, 128, 16, dtype=bf).transpose(1, 2)
+    yield "q_nope strided", t, {}, "q_nope"
+    yield "out shape", base(), dict(out=torch.zeros(2, 16, 64)), "out"
+    yield "lse dtype", base(), dict(lse=torch.zeros(2, 16, dtype=bf)), "lse"
+
+
+@pytest.mark.parametrize("case", list(_decode_mutations()), ids=lambda c: c[0])
+def test_binding_decode_rejects(case):
+    _, t, kw, what = case
+    with pytest.raises(ValueError, match=what):
+        _call_decode(t, **kw)

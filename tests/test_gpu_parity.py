@@ -61,18 +61,30 @@ def _compare(got, ref, bf16, what):
         assert max_abs <= FP32_MAX_ABS, f"{what}: max|d| {max_abs}"
 
 
-def _compare_lse(got, ref, bf16, what, magnitude_scaled=False):
-    """LSE check.  With magnitude_scaled the bar grows by 2^-9 |LSE|: logits
-    formed from bf16 / fp16 operands carry an absolute error proportional to
-    their size, which only matters for the deliberately huge logits of the
-    jump tests."""
+# Relative rounding of a logit in the jump tests, where one RoPE component
+# carries the whole logit (q_nope = 0 and the key band is lambda_t e_0):
+#   bf16 q~ (decode): the rotated query component lies in [0.5, 1), where bf16
+#     rounds with absolute error <= 2^-9, so |d s_t| <= 2^-9 |s_t|;
+#   fp16 operands (explicit form): query and key components are each rounded
+#     to fp16 (relative error <= 2^-11 each), so |d s_t| <= 2^-10 |s_t|.
+# The LSE is a smooth maximum, so its error is at most the largest error of
+# the logits that carry its weight, which are the ones of size ~|LSE|.
+LSE_REL_BF16_QTILDE = 2.0 ** -9
+LSE_REL_FP16_OPERANDS = 2.0 ** -10
+
+
+def _compare_lse(got, ref, bf16, what, rel=0.0):
+    """LSE check: -inf exactly where the oracle has it, elsewhere
+    |d| <= base + rel * |LSE|, base the spec bar of the configuration and
+    rel the relative logit rounding of the path (0 for ordinary data, whose
+    logits are O(1))."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     fin = np.isfinite(ref)
     assert np.array_equal(np.isneginf(got), ~fin), f"{what}: -inf pattern differs"
     if fin.any():
         err = np.abs(got[fin] - ref[fin])
-        bar = (BF16_MAX_ABS if bf16 else FP32_MAX_ABS) + (2.0 ** -9 * np.abs(ref[fin]) if magnitude_scaled else 0)
+        bar = (BF16_MAX_ABS if bf16 else FP32_MAX_ABS) + rel * np.abs(ref[fin])
         _say(f"{what}: lse max|d|={float(err.max()):.3e} (max |lse| {float(np.abs(ref[fin]).max()):.1f})")
         assert np.all(err <= bar), f"{what}: lse max|d| {float(err.max())}"
 
@@ -192,6 +204,12 @@ def test_v2lite_full(mla):
     _compare_lse(l, rl, True, "v2lite")
 
 
+# The attention kernel places head h on XCD h mod 8 and the absorbed forward
+# deals rows over XCDs by head as well, so the sampled heads cover every
+# residue mod 8 twice (first and last eight heads).
+V3_SAMPLE_HEADS = list(range(8)) + list(range(120, 128))
+
+
 def _sample_rows(n, rng, k=96):
     rows = set(range(min(32, n))) | set(range(max(0, n - 32), n))
     rows |= set(rng.choice(n, size=min(k, n), replace=False).tolist())
@@ -204,7 +222,7 @@ def test_v3_sampled(mla, name):
     x = I.make_explicit_inputs(cfg)
     o, l, _, _ = _run_explicit(mla, cfg, x)
     rng = np.random.default_rng(7)
-    heads = [0, 1, 63, 64, 126, 127]
+    heads = V3_SAMPLE_HEADS
     rows = _sample_rows(cfg.s_q, rng)
     ro, rl = _oracle_explicit(cfg, x, heads=heads, rows=rows)
     _compare(o[:, rows][:, :, heads], ro, True, f"{name} sampled out")
@@ -284,12 +302,30 @@ def test_decode_edges(mla, case, algo):
     odt = torch.float16 if esz == 2 else torch.float32
     op = ws[off_o:off_o + esz * B * ns * H * cfg.d_kv].view(odt).view(B, ns, H, cfg.d_kv).float().cpu().numpy()
     _compare_lse(lp, r["lse_part"], True, f"decode {cfg.name} lse_part")
+    # q~ = [W_UK^T q_nope ; R(q_pe, L-1)] as the split-KV kernels read it.  The
+    # MFMA path stores it in bf16: round-to-nearest keeps |d| <= 2^-8 |q~|,
+    # on top of the fp32 dot products' error (about 2^-24 * 128 * sum|w q|,
+    # below 1e-4 here).  The SIMT path keeps fp32.
+    dl = cfg.d_kv + cfg.d_rope
+    qdt = torch.bfloat16 if esz == 2 else torch.float32
+    qt = ws[off_q:off_q + esz * B * H * dl].view(qdt).view(B, H, dl).float().cpu().numpy()
+    rq = r["q_tilde"]
+    live = x["cache_len"] > 0          # the position of an empty sequence's query is undefined
+    qerr = np.abs(qt[live] - rq[live])
+    qbar = (2.0 ** -8 if esz == 2 else 1e-6) * np.abs(rq[live]) + 1e-4
+    _say(f"decode {cfg.name} q~: max|d|={float(qerr.max()):.3e}")
+    assert np.all(qerr <= qbar), f"{cfg.name}: q~ max|d| {float(qerr.max())}"
     fin = np.isfinite(r["lse_part"])
     assert np.all(op[~fin] == 0)
-    # o_part is an intermediate in latent space: a convex combination of cache
-    # rows whose weights the MFMA path rounds to bf16 (relative 2^-9 each) and
-    # which that path stores in fp16, so its bar is relative to the rows'
-    # size: 1% of max|ref| and rel-L2 5e-3.
+    # o_part is a convex combination sum_t w_t c_t of the chunk's latent rows.
+    # The MFMA path rounds each weight to bf16 before the value product
+    # (relative 2^-8), which moves an element by at most 2^-8 sum_t w_t |c_t|,
+    # and stores the partial in fp16 (2^-11 |o|).  When one row carries the
+    # weight, sum_t w_t |c_t| ~ |c_t*| ~ max|ref|; when many rows share it,
+    # it is the mean |c| (~0.8 for N(0,1) rows) while o shrinks.  The bar
+    # 1e-2 max(1, max|ref|) covers both (2^-8 < 1e-2), with room for the
+    # bf16 rounding of q~, which perturbs the weights by independently signed
+    # amounts of order 1e-3.  rel-L2 keeps the benchmark spec's 5e-3.
     got, ref = op[fin], r["o_part"][fin]
     err = float(np.abs(got - ref).max())
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
@@ -302,7 +338,7 @@ def test_decode_full_config_sampled(mla):
     _say("generating the 2.4 GB latent cache on the host")
     x = I.make_decode_inputs(cfg)
     o, l, _, _ = _run_decode(mla, cfg, x)
-    batches = [0, 31, 63]
+    batches = list(range(8)) + [31, 63]
     r = _oracle_decode(cfg, x, batches=batches)
     _compare(o[batches], r["out"], True, "decode v3 sampled out")
     _compare_lse(l[batches], r["lse"], True, "decode v3 sampled")
@@ -346,7 +382,7 @@ def test_decode_logit_jumps(mla, algo):
     o, l, _, _ = _run_decode(mla, cfg, x, algo=algo)
     r = _oracle_decode(cfg, x)
     _compare(o, r["out"], True, f"decode jumps out ({algo})")
-    _compare_lse(l, r["lse"], True, f"decode jumps ({algo})", magnitude_scaled=True)
+    _compare_lse(l, r["lse"], True, f"decode jumps ({algo})", rel=LSE_REL_BF16_QTILDE)
 
 
 def test_explicit_logit_jumps(mla):
@@ -362,7 +398,7 @@ def test_explicit_logit_jumps(mla):
     o, l, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA)
     ro, rl = _oracle_explicit(cfg, x)
     _compare(o, ro, True, "explicit jumps out")
-    _compare_lse(l, rl, True, "explicit jumps", magnitude_scaled=True)
+    _compare_lse(l, rl, True, "explicit jumps", rel=LSE_REL_FP16_OPERANDS)
 
 
 def test_explicit_mixed_batch_redo(mla):
@@ -380,7 +416,7 @@ def test_explicit_mixed_batch_redo(mla):
     o, l, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA)
     ro, rl = _oracle_explicit(cfg, x)
     _compare(o, ro, True, "mixed-redo out")
-    _compare_lse(l, rl, True, "mixed-redo", magnitude_scaled=True)
+    _compare_lse(l, rl, True, "mixed-redo", rel=LSE_REL_FP16_OPERANDS)
 
 
 def test_decode_tiny_fp32(mla):
@@ -466,7 +502,7 @@ def test_absorbed_v3_sampled(mla):
     x = I.make_explicit_inputs(cfg)
     o, l = _run_absorbed(mla, cfg, x)
     rng = np.random.default_rng(9)
-    heads = [0, 1, 63, 64, 126, 127]
+    heads = V3_SAMPLE_HEADS
     rows = _sample_rows(cfg.s_q, rng)
     ro, rl = _oracle_explicit(cfg, x, heads=heads, rows=rows)
     _compare(o[:, rows][:, :, heads], ro, True, "absorbed v3 sampled out")
