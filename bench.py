@@ -91,6 +91,183 @@ def hbm_traffic(kernel: str):
     return c["fetch_kib"] * 1024 / c["fetch_factor"] + c["write_kib"] * 1024 / c["write_factor"]
 
 
+# The pages' own figures, with the hardware and setting they were measured
+# on.  Context only: none is a single-device MLA forward rate, and none was
+# measured on this hardware.
+CONTEXT = [
+    {"page": "LAGA (Pith review)", "where": "abstract; Table 1",
+     "figure": "collective bytes per layer, explicit 587.2 MB vs LAGA 296.0 MB (1.98x less)",
+     "hardware": "8x Ascend 910B", "setting": "DeepSeek-V3 dims, S=16384, SP=8"},
+    {"page": "LAGA (Pith review)", "where": "\"If this is right\"; Fig. 3",
+     "figure": "communication ratio 1.88x (16 heads) to 1.98x (128 heads)",
+     "hardware": "Ascend 910B", "setting": "SP 4-16, S 4K-16K"},
+    {"page": "LAGA (Pith review)", "where": "abstract; \"If this is right\"",
+     "figure": "attention-block throughput LAGA/explicit 1.04-1.06x in one node, 1.07-1.24x across nodes "
+               "(fused kernel, rising with S)",
+     "hardware": "8x / 16x Ascend 910B", "setting": "n_h=128, S 4K-16K"},
+    {"page": "LAGA (Pith review)", "where": "abstract; referee report",
+     "figure": "activation memory absorbed minus explicit: +9.2 GB eager, +19.2 GB fused",
+     "hardware": "Ascend 910B (A100 cross-check)", "setting": "S=16384, SP=8"},
+    {"page": "TPLA (Pith review)", "where": "\"If this is right\"; abstract",
+     "figure": "decode throughput vs MLA: 1.79x (DeepSeek-V3), 1.93x (Kimi-K2)",
+     "hardware": "GPU type not stated", "setting": "32K context, MoE layers removed"},
+    {"page": "Helix (Pith review)", "where": "core claim; abstract",
+     "figure": "up to 1.5x lower token-to-token latency (DeepSeek-R1) and up to 32x larger batch; "
+               "1.13x lower latency, 4x batch for Llama-405B",
+     "hardware": "simulated GB200 NVL72 (FP4)", "setting": "1M-token KV cache"},
+]
+
+
+def host_info() -> dict:
+    """CPU model, visible CPUs and the BLAS build numpy uses."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')}, " \
+                       f"{os.path.basename(i.get('filepath', ''))})"
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "cpus_visible": len(os.sched_getaffinity(0)), "blas": blas}
+
+
+def pool_size() -> int:
+    """Worker threads for the oracle: the CPUs this process may run on, capped
+    by the thread budget the environment sets (OMP_NUM_THREADS), 16 if unset."""
+    cap = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    return max(1, min(len(os.sched_getaffinity(0)), cap))
+
+
+def explicit_case(mla, torch, cfg, args):
+    """Time one explicit-form configuration on its own: the call as a HIP graph
+    replay (checked bit-identical to the eager call), and per-kernel averages
+    from the library's launch events over eager calls."""
+    log(f"explicit configuration {cfg.name}: inputs, {args.steps} graph replays, {args.steps} eager calls")
+    x = I_mod().make_explicit_inputs(cfg)
+    t = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    del x
+    out = torch.empty((cfg.batch, cfg.s_q, cfg.n_heads, cfg.d_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.batch, cfg.n_heads, cfg.s_q), dtype=torch.float32, device="cuda")
+    kw = dict(q_pos0=cfg.q_pos0, kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale,
+              out=out, lse=lse)
+    _, _, ws = mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], **kw)
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], workspace=ws, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], workspace=ws, **kw)
+    out.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(out, ref[0]) and torch.equal(torch.nan_to_num(lse, neginf=-1e30),
+                                                     torch.nan_to_num(ref[1], neginf=-1e30))):
+        raise RuntimeError(f"{cfg.name}: graph replay differs from the eager call")
+    for _ in range(args.warmup):
+        g.replay()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ms = []
+    for _ in range(args.steps):
+        ev[0].record()
+        g.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms.append(ev[0].elapsed_time(ev[1]))
+    mla.mla_timing_reset()
+    mla.mla_timing_begin()
+    for _ in range(args.steps):
+        mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], workspace=ws, **kw)
+    torch.cuda.synchronize()
+    mla.mla_timing_end()
+    kt = mla.mla_timing_get()
+    mla.mla_timing_reset()
+    fl = cfg.flops()
+    avg = float(np.mean(ms))
+    kernels = {name: {"avg_ms": tot / max(n, 1), "launches_per_call": n / args.steps} for name, (tot, n) in kt.items()}
+    for name, work in (("mfma_attention", fl["attention"]), ("mfma_up_projection", fl["up_proj"])):
+        if name in kernels:
+            a = work / (kernels[name]["avg_ms"] * 1e-3) / 1e12
+            kernels[name].update({"achieved": a, "unit": "TFLOP/s", "frac": a / PEAK_MFMA_TFLOPS,
+                                  "work_per_launch": work})
+    tflops = fl["total"] / (avg * 1e-3) / 1e12
+    del t, out, lse, ws, g
+    torch.cuda.empty_cache()
+    return {"workload": f"{cfg.name} explicit fwd (B={cfg.batch}, S_q={cfg.s_q} at q_pos0={cfg.q_pos0}, "
+                        f"S_kv={cfg.s_kv}, n_h={cfg.n_heads}, causal)",
+            "ms": avg, "algorithmic_flop": fl["total"], "tflops": tflops, "frac_mfma_peak": tflops / PEAK_MFMA_TFLOPS,
+            "timing": "hip_graph_replay", "kernels": kernels}
+
+
+def I_mod():
+    from head_latent_attention_02_amd import inputs as I
+    return I
+
+
+def forms_memory_and_time(mla, torch, names, args):
+    """Explicit and absorbed forms of the same V3 causal forward at several
+    sequence lengths: time per call (HIP events, eager, after one untimed call)
+    and the device memory each call allocates, measured as the rise of
+    torch.cuda.max_memory_allocated over the resident inputs while the binding
+    allocates the outputs and the workspace and the call runs."""
+    I = I_mod()
+    res = []
+    for name in names:
+        cfg = I.EXPLICIT_CONFIGS[name]
+        log(f"explicit vs absorbed form at S={cfg.s_q}: inputs, then {args.form_calls} calls of each")
+        x = I.make_explicit_inputs(cfg)
+        t = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+        del x
+        row = {"tokens": cfg.s_q, "n_heads": cfg.n_heads}
+        for form, fn in (("explicit", mla.mla_fwd_explicit), ("absorbed", mla.mla_fwd_absorbed)):
+            kw = dict(q_pos0=cfg.q_pos0, kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            base = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            out, lse, ws = fn(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], **kw)
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated() - base
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ms = []
+            for _ in range(args.form_calls):
+                ev[0].record()
+                fn(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], out=out, lse=lse, workspace=ws, **kw)
+                ev[1].record()
+                torch.cuda.synchronize()
+                ms.append(ev[0].elapsed_time(ev[1]))
+            row[form] = {"ms": float(np.mean(ms)), "device_bytes": int(peak), "workspace_bytes": int(ws.numel()),
+                         "output_bytes": int(out.numel() * 4 + lse.numel() * 4)}
+            del out, lse, ws
+        row["gap_bytes"] = row["absorbed"]["device_bytes"] - row["explicit"]["device_bytes"]
+        res.append(row)
+        del t
+        torch.cuda.empty_cache()
+    slope = None
+    if len(res) >= 2:
+        slope = (res[-1]["gap_bytes"] - res[0]["gap_bytes"]) / (res[-1]["tokens"] - res[0]["tokens"])
+    cfg0 = I.EXPLICIT_CONFIGS[names[0]]
+    pages = cfg0.n_heads * (cfg0.d_kv - (cfg0.d_nope + cfg0.d_v)) * 2
+    return {"rows": res, "measured_gap_slope_bytes_per_token": slope,
+            "pages_slope_bytes_per_token_bf16": pages,
+            "pages_slope": "n_h * (d_kv - (d_nope + d_v)) values per token, 2 bytes each"}
+
+
 def absorbed_forward(mla, torch, ecfg, t, fl, args):
     """The explicit workload in absorbed form (mla_fwd_absorbed): time per call
     (eager, HIP events around each call, after one untimed call) and the
@@ -145,6 +322,12 @@ def parse():
                    help="skip the absorbed-form forward of the explicit workload")
     p.add_argument("--no-graph", action="store_true",
                    help="time the step as eager calls (no HIP graph replay)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the timing of the V2-Lite and SP=8-rank explicit configurations")
+    p.add_argument("--no-forms", action="store_true",
+                   help="skip the explicit-vs-absorbed memory and time comparison at 4K/8K/16K tokens")
+    p.add_argument("--form-calls", type=int, default=3,
+                   help="timed calls per form and length in the explicit-vs-absorbed comparison")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run a plain 1 GiB device copy (3 times) before the warm-up, as the "
                         "reference reading for HBM byte counters")
@@ -163,21 +346,33 @@ def blas_threads() -> int:
 def cpu_baseline(ecfg, x_host, out_gpu, dcfg, dx_host, dout_gpu, budget_s):
     """Time the fp64 oracle on a bounded sample of the same workload and, on
     the same sample, compare the GPU outputs with it."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+
     from oracle import mla_oracle as O
 
-    # explicit: the first k heads, all query rows
-    t0 = time.perf_counter()
-    ro, _ = O.explicit_fwd(x_host["q_nope"], x_host["q_pe"], x_host["c_kv"], x_host["k_pe"], x_host["w_kv_b"],
-                           q_pos0=ecfg.q_pos0, kv_pos0=ecfg.kv_pos0, causal=ecfg.causal,
-                           softmax_scale=ecfg.softmax_scale, heads=[0])
-    t_one = time.perf_counter() - t0
-    k = int(max(1, min(ecfg.n_heads, (0.7 * budget_s) // max(t_one, 1e-3))))
-    heads = list(range(k))
-    t0 = time.perf_counter()
-    ro, _ = O.explicit_fwd(x_host["q_nope"], x_host["q_pe"], x_host["c_kv"], x_host["k_pe"], x_host["w_kv_b"],
-                           q_pos0=ecfg.q_pos0, kv_pos0=ecfg.kv_pos0, causal=ecfg.causal,
-                           softmax_scale=ecfg.softmax_scale, heads=heads)
-    t_exp = time.perf_counter() - t0
+    workers = pool_size()
+
+    def one_head(h):
+        return O.explicit_fwd(x_host["q_nope"], x_host["q_pe"], x_host["c_kv"], x_host["k_pe"], x_host["w_kv_b"],
+                              q_pos0=ecfg.q_pos0, kv_pos0=ecfg.kv_pos0, causal=ecfg.causal,
+                              softmax_scale=ecfg.softmax_scale, heads=[h])[0]
+
+    # explicit: a pool of single-threaded-BLAS workers, one head per task; the
+    # sample is the first k heads (all query rows), k sized to the budget
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        one_head(0)
+        t_one = time.perf_counter() - t0
+        k = int(max(1, min(ecfg.n_heads, workers * (0.7 * budget_s) // max(t_one, 1e-3))))
+        k = max(1, min(ecfg.n_heads, (k // workers) * workers or k))
+        heads = list(range(k))
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(workers) as ex:
+            parts = list(ex.map(one_head, heads))
+        t_exp = time.perf_counter() - t0
+    ro = np.concatenate(parts, axis=2)
     fl = ecfg.flops()
     flops_sample = fl["total"] * k / ecfg.n_heads
     got = out_gpu[:, :, :k]
@@ -188,6 +383,7 @@ def cpu_baseline(ecfg, x_host, out_gpu, dcfg, dx_host, dout_gpu, budget_s):
     # decode: one sequence, all heads
     bits = dx_host["cache_bits"]
     from head_latent_attention_02_amd import inputs as I
+    dec_threads = blas_threads()
     t0 = time.perf_counter()
     r = O.decode_absorbed(dx_host["q_nope"], dx_host["q_pe"], lambda b: I.bf16_bits_to_f32(bits[b]),
                           dx_host["cache_len"], dx_host["w_kv_b"], n_splits=dcfg.n_splits, d_kv=dcfg.d_kv,
@@ -198,13 +394,14 @@ def cpu_baseline(ecfg, x_host, out_gpu, dcfg, dx_host, dout_gpu, budget_s):
     parity_dec = {"max_abs": float(derr.max()),
                   "rel_l2": float(np.linalg.norm(dg - r["out"]) / np.linalg.norm(r["out"])),
                   "sample": f"sequence 0 of {dcfg.batch}, all {dcfg.n_heads} heads"}
-    cores = blas_threads()
-    return ({"value": flops_sample / t_exp / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    hi = host_info()
+    return ({"value": flops_sample / t_exp / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
              "sample": f"explicit fwd at {ecfg.name} dims, heads 0..{k - 1} of {ecfg.n_heads} (all rows), "
-                       f"{t_exp:.1f} s; fp64 numpy"},
-            {"value": 1.0 / t_dec, "unit": "tok/s", "cores": cores, "kind": "oracle",
+                       f"{t_exp:.1f} s; fp64 numpy, {workers} worker threads over heads, BLAS single-threaded",
+             **hi},
+            {"value": 1.0 / t_dec, "unit": "tok/s", "cores": dec_threads, "kind": "oracle",
              "sample": f"absorbed decode, 1 of {dcfg.batch} sequences (L={dcfg.cache_len}, all heads), "
-                       f"{t_dec:.1f} s; fp64 numpy"},
+                       f"{t_dec:.1f} s; fp64 numpy, BLAS with {dec_threads} threads", **hi},
             {"explicit": parity_exp, "decode": parity_dec})
 
 
@@ -426,8 +623,14 @@ def main():
                    "graph": graph},
     }
 
+    res["context"] = CONTEXT
+
     if not args.no_absorbed:
         res["absorbed_forward"] = absorbed_forward(mla, torch, ecfg, t, fl, args)
+
+    if not args.no_configs:
+        res["configs"] = {name: explicit_case(mla, torch, I.EXPLICIT_CONFIGS[name], args)
+                          for name in ("v3_sp8_rank3", "v2lite_bf16")}
 
     if not args.no_cpu_baseline:
         log("oracle CPU baseline on a bounded sample")
@@ -436,6 +639,11 @@ def main():
         res["cpu_baseline"] = cb_e
         res["cpu_baseline_decode"] = cb_d
         res["parity_sample"] = parity
+
+    if not args.no_forms:
+        del t, cache, dq_nope, dq_pe, dw, dlen, ws, dws
+        torch.cuda.empty_cache()
+        res["forms_memory"] = forms_memory_and_time(mla, torch, ["v3_bf16", "v3_s8k_bf16", "v3_s16k_bf16"], args)
     print(json.dumps(res), flush=True)
 
 

@@ -132,6 +132,10 @@ EXPLICIT_CONFIGS = {
         ExplicitConfig("v2lite_bf16", 1, 4096, 4096, 16, 512, 128, 64, 128, 0, 0, True, "bf16", 1002),
         ExplicitConfig("v3_bf16", 1, 4096, 4096, 128, 512, 128, 64, 128, 0, 0, True, "bf16", 1003),
         ExplicitConfig("v3_sp8_rank3", 1, 2048, 16384, 128, 512, 128, 64, 128, 6144, 0, True, "bf16", 1004),
+        # longer sequences at V3 dims for the explicit-vs-absorbed memory and
+        # time comparison (the LAGA page's 4K / 8K / 16K range)
+        ExplicitConfig("v3_s8k_bf16", 1, 8192, 8192, 128, 512, 128, 64, 128, 0, 0, True, "bf16", 1006),
+        ExplicitConfig("v3_s16k_bf16", 1, 16384, 16384, 128, 512, 128, 64, 128, 0, 0, True, "bf16", 1007),
     ]
 }
 

@@ -46,3 +46,12 @@ def test_source_digest_depends_on_every_listed_file(tmp_path, monkeypatch):
     d0 = bench.source_digest("k")
     (tmp_path / "common.h").write_text("changed")
     assert bench.source_digest("k") != d0
+
+
+def test_host_info_and_pool_size(monkeypatch):
+    info = bench.host_info()
+    assert info["cpus_visible"] == len(os.sched_getaffinity(0)) >= 1
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert bench.pool_size() == min(3, info["cpus_visible"])
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert 1 <= bench.pool_size() <= 16
