@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -306,6 +307,45 @@ mla_status make_absorbed_plan(const mla_explicit_desc* d, AbsorbedPlan* plan) {
   *plan = p;
   return MLA_OK;
 }
+// ------------------------------------------------- allocation-free decode --
+// Fixed scratch for mla_decode_absorbed_noalloc: the decode intermediates (q~,
+// chunk LSEs and partials) live here instead of in a caller workspace.  Each
+// GPU the library runs on holds its own copy for the life of the process.  In
+// host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever handed
+// to kernels.
+constexpr size_t kScratchBytes = MLA_DECODE_NOALLOC_MAX_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up on the
+// first call made on that device.
+mla_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "device index beyond the scratch table";
+    return MLA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) {
+      g_last_error = "hipGetSymbolAddress(scratch) returned a null address";
+      return MLA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -436,6 +476,35 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc, const void* q_nope, 
   DecodeArgs a;
   fill_decode_args(desc, q_nope, q_pe, kv_cache, cache_len, w_kv_b, out, lse, &a);
   return run_decode(p, a, static_cast<char*>(workspace), s);
+}
+
+mla_status mla_decode_absorbed_noalloc(const mla_decode_desc* desc, const void* q_nope, const void* q_pe,
+                                       const void* kv_cache, const int32_t* cache_len, const void* w_kv_b,
+                                       void* out, float* lse, void* stream) {
+  DecodePlan p;
+  mla_status st = make_decode_plan(desc, &p);
+  if (st != MLA_OK) return st;
+  if (q_nope == nullptr || q_pe == nullptr || cache_len == nullptr || w_kv_b == nullptr || out == nullptr)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (desc->max_cache_len > 0 && kv_cache == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (p.total > kScratchBytes) {
+    g_last_error = "decode intermediates need " + std::to_string(p.total) + " bytes; the fixed scratch holds " +
+                   std::to_string(kScratchBytes);
+    return MLA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (!aligned16(w_kv_b)) return MLA_ERR_INVALID_ARGUMENT;
+  if (p.mfma) {
+    const void* ptrs[] = {q_nope, q_pe, kv_cache, out};
+    for (const void* q : ptrs)
+      if (q != nullptr && !aligned16(q)) return MLA_ERR_INVALID_ARGUMENT;
+  }
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != MLA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeArgs a;
+  fill_decode_args(desc, q_nope, q_pe, kv_cache, cache_len, w_kv_b, out, lse, &a);
+  return run_decode(p, a, static_cast<char*>(ws), s);
 }
 
 size_t mla_fwd_absorbed_workspace_size(const mla_explicit_desc* desc) {

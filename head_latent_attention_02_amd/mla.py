@@ -24,6 +24,9 @@ MLA_ERR_HIP = 4
 MLA_BF16 = 0
 MLA_FP32 = 1
 
+# bytes of the library's fixed decode scratch (MLA_DECODE_NOALLOC_MAX_BYTES)
+DECODE_NOALLOC_MAX_BYTES = 64 << 20
+
 MLA_ALGO_AUTO = 0
 MLA_ALGO_SIMT = 1
 MLA_ALGO_MFMA = 2
@@ -31,7 +34,7 @@ MLA_ALGO_MFMA = 2
 EXPORTED_SYMBOLS = (
     "mla_fwd_explicit_workspace_size", "mla_fwd_explicit", "mla_fwd_explicit_workspace_layout",
     "mla_decode_absorbed_workspace_size", "mla_decode_absorbed", "mla_decode_absorbed_workspace_layout",
-    "mla_fwd_absorbed_workspace_size", "mla_fwd_absorbed",
+    "mla_fwd_absorbed_workspace_size", "mla_fwd_absorbed", "mla_decode_absorbed_noalloc",
     "mla_status_string", "mla_last_error", "mla_build_info",
     "mla_timing_begin", "mla_timing_end", "mla_timing_reset", "mla_timing_count", "mla_timing_get",
 )
@@ -91,6 +94,8 @@ def _lib() -> ctypes.CDLL:
         lib.mla_decode_absorbed_workspace_size.restype = sz
         lib.mla_decode_absorbed.argtypes = [ctypes.POINTER(MlaDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.mla_decode_absorbed.restype = ctypes.c_int
+        lib.mla_decode_absorbed_noalloc.argtypes = [ctypes.POINTER(MlaDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.mla_decode_absorbed_noalloc.restype = ctypes.c_int
         lib.mla_decode_absorbed_workspace_layout.argtypes = [ctypes.POINTER(MlaDecodeDesc), ctypes.POINTER(sz)]
         lib.mla_decode_absorbed_workspace_layout.restype = ctypes.c_int
         lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -298,6 +303,53 @@ def mla_decode_absorbed(q_nope: torch.Tensor, q_pe: torch.Tensor, kv_cache: torc
     sequence stride may exceed L_max rows; rows must be contiguous),
     cache_len [B] int32 on the device, w_kv_b [H*(d_nope+d_v), d_kv].
     """
+    desc, d_v = _decode_checked_desc(q_nope, q_pe, kv_cache, cache_len, w_kv_b, n_splits=n_splits, d_kv=d_kv,
+                                     softmax_scale=softmax_scale, rope_base=rope_base, out_dtype=out_dtype,
+                                     algo=algo, return_lse=return_lse, out=out, lse=lse, workspace=workspace)
+    B, H = q_nope.shape[0], q_nope.shape[1]
+    dev = q_nope.device
+    ws_bytes = mla_decode_absorbed_workspace_size(desc)
+    if ws_bytes == 0:
+        _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,
+               "mla_decode_absorbed_workspace_size")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=out_dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = _lib().mla_decode_absorbed(ctypes.byref(desc), _ptr(q_nope), _ptr(q_pe), _ptr(kv_cache),
+                                    _ptr(cache_len), _ptr(w_kv_b), _ptr(out), _ptr(lse) if return_lse else None,
+                                    workspace.data_ptr(), workspace.numel(), _stream(dev))
+    _check(st, "mla_decode_absorbed")
+    return out, (lse if return_lse else None), workspace
+
+
+def mla_decode_absorbed_noalloc(q_nope: torch.Tensor, q_pe: torch.Tensor, kv_cache: torch.Tensor,
+                                cache_len: torch.Tensor, w_kv_b: torch.Tensor, out: torch.Tensor,
+                                lse: Optional[torch.Tensor] = None, *, n_splits: int = 16,
+                                d_kv: Optional[int] = None, softmax_scale: Optional[float] = None,
+                                rope_base: float = 10000.0, algo: int = MLA_ALGO_AUTO) -> None:
+    """The decode step without a workspace, for callers that cannot allocate;
+    see mla_decode_absorbed_noalloc in include/mla.h.  The caller passes the
+    outputs (out [B,H,d_v], lse [B,H] fp32 or None); nothing is allocated here
+    or in the library.  Calls on one GPU share the library's fixed scratch and
+    must not overlap."""
+    if out is None:
+        raise ValueError("out must be given: this entry point allocates nothing")
+    desc, _ = _decode_checked_desc(q_nope, q_pe, kv_cache, cache_len, w_kv_b, n_splits=n_splits, d_kv=d_kv,
+                                   softmax_scale=softmax_scale, rope_base=rope_base, out_dtype=out.dtype,
+                                   algo=algo, return_lse=lse is not None, out=out, lse=lse, workspace=None)
+    st = _lib().mla_decode_absorbed_noalloc(ctypes.byref(desc), _ptr(q_nope), _ptr(q_pe), _ptr(kv_cache),
+                                            _ptr(cache_len), _ptr(w_kv_b), _ptr(out), _ptr(lse),
+                                            _stream(q_nope.device))
+    _check(st, "mla_decode_absorbed_noalloc")
+
+
+def _decode_checked_desc(q_nope, q_pe, kv_cache, cache_len, w_kv_b, *, n_splits, d_kv, softmax_scale, rope_base,
+                         out_dtype, algo, return_lse, out, lse, workspace):
+    """Checks every decode tensor (shapes, dtypes, layouts, device) and
+    returns (descriptor, d_v)."""
     if q_nope.dim() != 3 or q_pe.dim() != 3 or kv_cache.dim() != 3 or w_kv_b.dim() != 2:
         raise ValueError("expected q_nope, q_pe [B,H,*], kv_cache [B,L_max,d_kv+d_rope], "
                          "w_kv_b [H*(d_nope+d_v), d_kv]")
@@ -336,21 +388,7 @@ def mla_decode_absorbed(q_nope: torch.Tensor, q_pe: torch.Tensor, kv_cache: torc
                        max_cache_len=kv_cache.shape[1], cache_batch_stride=kv_cache.stride(0),
                        n_splits=n_splits, softmax_scale=softmax_scale, rope_base=rope_base, in_dtype=dt,
                        out_dtype=_dtype_code(out_dtype), algo=algo)
-    ws_bytes = mla_decode_absorbed_workspace_size(desc)
-    if ws_bytes == 0:
-        _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,
-               "mla_decode_absorbed_workspace_size")
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    if out is None:
-        out = torch.empty((B, H, d_v), dtype=out_dtype, device=dev)
-    if return_lse and lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    st = _lib().mla_decode_absorbed(ctypes.byref(desc), _ptr(q_nope), _ptr(q_pe), _ptr(kv_cache),
-                                    _ptr(cache_len), _ptr(w_kv_b), _ptr(out), _ptr(lse) if return_lse else None,
-                                    workspace.data_ptr(), workspace.numel(), _stream(dev))
-    _check(st, "mla_decode_absorbed")
-    return out, (lse if return_lse else None), workspace
+    return desc, d_v
 
 
 def mla_timing_begin():

@@ -209,6 +209,33 @@ mla_status mla_decode_absorbed(const mla_decode_desc* desc,
 mla_status mla_decode_absorbed_workspace_layout(const mla_decode_desc* desc,
                                                 size_t offsets[4]);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the decode
+ * step of mla_decode_absorbed with the same arguments and results, minus the
+ * workspace.  Its intermediates (q~, chunk LSEs, partials: the bytes that
+ * mla_decode_absorbed_workspace_size reports) go to a fixed device array of
+ * MLA_DECODE_NOALLOC_MAX_BYTES bytes (64 MiB) inside the library, one per
+ * GPU, held until the process ends.  The call allocates and frees
+ * nothing.
+ *   - A step whose intermediates exceed that size returns
+ *     MLA_ERR_WORKSPACE_TOO_SMALL (mla_last_error gives both sizes) and
+ *     launches nothing.  At 128 heads and 16 splits one sequence needs about
+ *     2.3 MB, so up to 28 sequences fit.
+ *   - Every call on one GPU uses that GPU's one array.  Calls whose execution
+ *     overlaps on one GPU (other streams, other threads) race on it and give
+ *     undefined results; serialize them.  The kernels write every
+ *     intermediate before reading it, so nothing needs clearing between calls.
+ *   - The array's device address is looked up on the first call made with a
+ *     device current (a runtime symbol lookup, no allocation). */
+#define MLA_DECODE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
+mla_status mla_decode_absorbed_noalloc(const mla_decode_desc* desc,
+                                       const void* q_nope, const void* q_pe,
+                                       const void* kv_cache, const int32_t* cache_len,
+                                       const void* w_kv_b,
+                                       void* out, float* lse,
+                                       void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Absorbed-form forward of the explicit problem                            */
 /* ------------------------------------------------------------------------ */

@@ -335,3 +335,29 @@ def test_binding_decode_rejects(case):
     _, t, kw, what = case
     with pytest.raises(ValueError, match=what):
         _call_decode(t, **kw)
+
+
+def test_noalloc_decode_rejects_on_the_host():
+    """The allocation-free decode step refuses, before touching any device, a
+    step whose intermediates exceed the fixed scratch, and invalid
+    descriptors."""
+    lib = mla.library()
+    big = _dec_desc()                      # 64 x 128 heads x 16 splits: ~144 MB of intermediates
+    assert mla.mla_decode_absorbed_workspace_size(big) > mla.DECODE_NOALLOC_MAX_BYTES
+    st = lib.mla_decode_absorbed_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert "scratch" in lib.mla_last_error().decode()
+    for field, value in [("batch", 0), ("n_splits", 0), ("softmax_scale", 0.0), ("d_rope", 3)]:
+        d = _dec_desc(batch=4)
+        setattr(d, field, value)
+        assert lib.mla_decode_absorbed_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                               None) == mla.MLA_ERR_INVALID_ARGUMENT
+    d = _dec_desc(batch=4)
+    assert lib.mla_decode_absorbed_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                                           None) == mla.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MLA_DECODE_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mla.DECODE_NOALLOC_MAX_BYTES
