@@ -49,6 +49,9 @@ design notes of the repository):
   R6 Decode chunks: c = ceil(L_b / n_s), chunk k = [k*c, min(L_b, (k+1)*c));
      an empty chunk has lse = -inf and a zero partial.
   R7 LSE is the natural log of the sum of exp of the scaled logits.
+  R13 Backward: the gradient of sum(d_out * O) with respect to the five
+     inputs of the explicit form (q_nope, q_pe, c_kv, k_pe, W_kv_b), all
+     in the inputs' own (un-rotated) coordinates.
 
 Everything is float64 on the exact input values.
 """
@@ -62,7 +65,7 @@ import numpy as np
 __all__ = [
     "rope_theta", "rope_rotate", "weight_slices", "visibility_mask",
     "explicit_fwd", "absorbed_fwd", "decode_absorbed", "lse_merge",
-    "brute_force_explicit",
+    "brute_force_explicit", "explicit_bwd",
 ]
 
 
@@ -310,6 +313,90 @@ def decode_absorbed(q_nope, q_pe, cache, cache_len, w_kv_b, *, n_splits, d_kv,
         res["lse"][bi] = lse
         res["out"][bi] = np.stack([w_uv[h] @ o_lat[hi] for hi, h in enumerate(heads)])
     return res
+
+
+# --------------------------------------------------------------------------
+# Backward of the explicit form (the training setting of [LAGA])
+# --------------------------------------------------------------------------
+def _softmax_bwd(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
+    """Row softmax Jacobian applied to dP: dS = P * (dP - sum_j P dP) per row
+    (rows with no visible key have P = 0 and get dS = 0)."""
+    return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+
+
+def explicit_bwd(q_nope, q_pe, c_kv, k_pe, w_kv_b, d_out, *, q_pos0=0, kv_pos0=0, causal=True,
+                 softmax_scale: Optional[float] = None, rope_base=10000.0):
+    """Gradients of sum(d_out * O) through explicit_fwd, with respect to every
+    input.  [LAGA] is about training: its "If this is right" section states
+    that LAGA's parameter gradients equal the explicit form's, and the Fig. 5
+    caption bounds their difference; this is the explicit form's gradient.
+
+    Reverse mode through the forward's steps, per batch entry and head:
+      O = P V                      -> dV = P^T dO, dP = dO V^T
+      P = softmax(s) over visible  -> dS = P * (dP - rowsum(P * dP))
+      s = sigma (q_n K^T + q_r k_r^T)
+                                   -> dq_n = sigma dS K, dq_r = sigma dS k_r,
+                                      dK = sigma dS^T q_n, dk_r = sigma dS^T q_r
+      K = c W_UK^T, V = c W_UV^T   -> dc = dK W_UK + dV W_UV,
+                                      dW_UK = dK^T c, dW_UV = dV^T c
+      q_r = R(q_pe, p), k_r = R(k_pe, p')
+                                   -> R is a rotation, so its transpose rotates
+                                      back: dq_pe = R(dq_r, -p); the key band is
+                                      shared by the heads, so
+                                      dk_pe = R(sum_h dk_r, -p')
+    Returns a dict with dq_nope [B,S_q,H,d_n], dq_pe [B,S_q,H,d_r],
+    dc_kv [B,S_kv,d_c], dk_pe [B,S_kv,d_r] and dw_kv_b [H*(d_n+d_v), d_c].
+    """
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_pe = np.asarray(q_pe, dtype=np.float64)
+    c_kv = np.asarray(c_kv, dtype=np.float64)
+    k_pe = np.asarray(k_pe, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    B, S_q, H, d_n = q_nope.shape
+    S_kv = c_kv.shape[1]
+    d_r = q_pe.shape[-1]
+    d_v = w_kv_b.shape[0] // H - d_n
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_n + d_r)
+    sig = softmax_scale
+    w_uk, w_uv = weight_slices(w_kv_b, H, d_n, d_v)
+    qpos = _positions(S_q, q_pos0)
+    kpos = _positions(S_kv, kv_pos0)
+    vis = visibility_mask(S_q, S_kv, q_pos0, kv_pos0, causal)
+    g = {"dq_nope": np.zeros_like(q_nope), "dq_pe": np.zeros_like(q_pe), "dc_kv": np.zeros_like(c_kv),
+         "dk_pe": np.zeros_like(k_pe)}
+    dw_uk = np.zeros_like(w_uk)
+    dw_uv = np.zeros_like(w_uv)
+    for b in range(B):
+        k_rot = rope_rotate(k_pe[b], kpos, rope_base)
+        dk_rot = np.zeros_like(k_rot)
+        for h in range(H):
+            k_n = c_kv[b] @ w_uk[h].T
+            v = c_kv[b] @ w_uv[h].T
+            q_rot = rope_rotate(q_pe[b, :, h], qpos, rope_base)
+            s = sig * (q_nope[b, :, h] @ k_n.T + q_rot @ k_rot.T)
+            p, _ = _masked_softmax_rows(s, vis)
+            do = d_out[b, :, h]
+            dv = p.T @ do
+            dp = do @ v.T
+            ds = _softmax_bwd(p, dp)
+            g["dq_nope"][b, :, h] = sig * (ds @ k_n)
+            g["dq_pe"][b, :, h] = rope_rotate(sig * (ds @ k_rot), -qpos, rope_base)
+            dk_n = sig * (ds.T @ q_nope[b, :, h])
+            dk_rot += sig * (ds.T @ q_rot)
+            g["dc_kv"][b] += dk_n @ w_uk[h] + dv @ w_uv[h]
+            dw_uk[h] += dk_n.T @ c_kv[b]
+            dw_uv[h] += dv.T @ c_kv[b]
+        g["dk_pe"][b] = rope_rotate(dk_rot, -kpos, rope_base)
+    g["dw_kv_b"] = _head_grads_to_w_layout(dw_uk, dw_uv)
+    return g
+
+
+def _head_grads_to_w_layout(dw_uk: np.ndarray, dw_uv: np.ndarray) -> np.ndarray:
+    """[H, d_n, d_c] and [H, d_v, d_c] back to W_kv_b's row layout (reading R1):
+    head h's rows are its d_n key rows, then its d_v value rows."""
+    H = dw_uk.shape[0]
+    return np.concatenate([dw_uk, dw_uv], axis=1).reshape(H * (dw_uk.shape[1] + dw_uv.shape[1]), -1)
 
 
 # --------------------------------------------------------------------------

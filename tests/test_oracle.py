@@ -346,3 +346,126 @@ def test_pins_catch_planted_mistakes(monkeypatch, mutation):
         monkeypatch.setattr(O, "rope_rotate", rot)
     o, _ = O.explicit_fwd(**x, **_args(cfg))
     assert np.max(np.abs(o - good)) > 1e-6
+
+
+# ------------------------------------------------------------ backward ----
+# Pins of explicit_bwd: derivatives by central differences of the forward
+# (a different computation: only the forward and the definition of a
+# derivative), closed forms, and planted mistakes.
+_GRADS = [("q_nope", "dq_nope"), ("q_pe", "dq_pe"), ("c_kv", "dc_kv"), ("k_pe", "dk_pe"), ("w_kv_b", "dw_kv_b")]
+
+BWD_CASES = [
+    I.small_explicit("bwd_causal", batch=2, s_q=6, s_kv=9, n_heads=2, d_kv=6, d_nope=4, d_rope=4, d_v=3,
+                     q_pos0=3, seed=71),
+    I.small_explicit("bwd_masked_rows", batch=1, s_q=7, s_kv=7, n_heads=3, d_kv=5, d_nope=3, d_rope=2, d_v=4,
+                     kv_pos0=2, seed=72),
+    I.small_explicit("bwd_noncausal", batch=1, s_q=4, s_kv=6, n_heads=2, d_kv=4, d_nope=2, d_rope=6, d_v=2,
+                     causal=False, seed=73),
+]
+
+
+def _f64(x):
+    return {k: np.asarray(v, dtype=np.float64) for k, v in x.items()}
+
+
+def _loss(x, do, cfg):
+    return float(np.sum(do * O.explicit_fwd(**x, **_args(cfg))[0]))
+
+
+@pytest.mark.parametrize("cfg", BWD_CASES, ids=lambda c: c.name)
+def test_backward_matches_central_differences(cfg):
+    """Every input's gradient against the directional derivative of
+    sum(d_out * O) along a random direction, by central differences."""
+    x = _f64(I.make_explicit_inputs(cfg))
+    rng = np.random.default_rng(cfg.seed)
+    do = rng.standard_normal((cfg.batch, cfg.s_q, cfg.n_heads, cfg.d_v))
+    g = O.explicit_bwd(**x, d_out=do, **_args(cfg))
+    h = 1e-5
+    for name, gname in _GRADS:
+        v = rng.standard_normal(x[name].shape)
+        xp = dict(x, **{name: x[name] + h * v})
+        xm = dict(x, **{name: x[name] - h * v})
+        fd = (_loss(xp, do, cfg) - _loss(xm, do, cfg)) / (2 * h)
+        an = float(np.sum(g[gname] * v))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_backward_elementwise_central_differences():
+    """A few single elements of each gradient, where a wrong index would hide
+    in a directional sum."""
+    cfg = BWD_CASES[0]
+    x = _f64(I.make_explicit_inputs(cfg))
+    rng = np.random.default_rng(5)
+    do = rng.standard_normal((cfg.batch, cfg.s_q, cfg.n_heads, cfg.d_v))
+    g = O.explicit_bwd(**x, d_out=do, **_args(cfg))
+    h = 1e-6
+    for name, gname in _GRADS:
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in x[name].shape)
+            xp = {k: v.copy() for k, v in x.items()}
+            xm = {k: v.copy() for k, v in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd = (_loss(xp, do, cfg) - _loss(xm, do, cfg)) / (2 * h)
+            assert abs(fd - g[gname][idx]) <= 1e-7 * max(1.0, abs(fd)), (name, idx, fd, g[gname][idx])
+
+
+def test_backward_identical_keys_give_zero_query_gradient():
+    """With every key identical (one latent row repeated, zero RoPE band) the
+    softmax is uniform over the visible keys and each row of dS sums to zero,
+    so the query gradients vanish while dV does not."""
+    cfg = I.small_explicit("same_keys", batch=1, s_q=6, s_kv=6, n_heads=2, d_kv=5, d_nope=3, d_rope=4, d_v=3,
+                           seed=74)
+    x = _f64(I.make_explicit_inputs(cfg))
+    x["c_kv"][:] = x["c_kv"][:, :1]
+    x["k_pe"][:] = 0.0
+    do = np.random.default_rng(1).standard_normal((1, 6, 2, 3))
+    g = O.explicit_bwd(**x, d_out=do, **_args(cfg))
+    assert np.abs(g["dq_nope"]).max() < 1e-13 and np.abs(g["dq_pe"]).max() < 1e-13
+    assert np.abs(g["dw_kv_b"]).max() > 1e-3
+
+
+def test_backward_single_key_closed_form():
+    """One key: O = W_UV c_0 for every query, independent of the queries and of
+    W_UK, so dq = 0, dk_pe = 0, dW_UK = 0, dW_UV[h] = sum_i dO_i c_0^T and
+    dc_0 = sum_h W_UV[h]^T sum_i dO_i."""
+    cfg = I.small_explicit("one_key", batch=1, s_q=4, s_kv=1, n_heads=2, d_kv=5, d_nope=3, d_rope=4, d_v=3,
+                           causal=False, seed=75)
+    x = _f64(I.make_explicit_inputs(cfg))
+    do = np.random.default_rng(2).standard_normal((1, 4, 2, 3))
+    g = O.explicit_bwd(**x, d_out=do, **_args(cfg))
+    w = x["w_kv_b"].reshape(2, 6, 5)
+    c0 = x["c_kv"][0, 0]
+    for name in ("dq_nope", "dq_pe", "dk_pe"):
+        assert np.abs(g[name]).max() < 1e-14, name
+    gw = g["dw_kv_b"].reshape(2, 6, 5)
+    assert np.abs(gw[:, :3]).max() < 1e-14
+    for h in range(2):
+        np.testing.assert_allclose(gw[h, 3:], np.outer(do[0, :, h].sum(0), c0), atol=1e-13)
+    dc = sum(w[h, 3:].T @ do[0, :, h].sum(0) for h in range(2))
+    np.testing.assert_allclose(g["dc_kv"][0, 0], dc, atol=1e-13)
+
+
+@pytest.mark.parametrize("mutation", ["no_d_term", "rope_back_sign", "swap_w_grads"])
+def test_backward_pins_catch_planted_mistakes(monkeypatch, mutation):
+    cfg = BWD_CASES[0]
+    x = _f64(I.make_explicit_inputs(cfg))
+    do = np.random.default_rng(3).standard_normal((cfg.batch, cfg.s_q, cfg.n_heads, cfg.d_v))
+    if mutation == "no_d_term":
+        monkeypatch.setattr(O, "_softmax_bwd", lambda p, dp: p * dp)
+    elif mutation == "rope_back_sign":
+        real_rot = O.rope_rotate
+        monkeypatch.setattr(O, "rope_rotate", lambda v, p, b: real_rot(v, np.abs(np.asarray(p, float)), b))
+    else:
+        real = O._head_grads_to_w_layout
+        monkeypatch.setattr(O, "_head_grads_to_w_layout", lambda a, b: real(b, a) if a.shape == b.shape
+                            else real(a[:, ::-1], b))
+    g = O.explicit_bwd(**x, d_out=do, **_args(cfg))
+    rng = np.random.default_rng(9)
+    worst = 0.0
+    for name, gname in _GRADS:
+        v = rng.standard_normal(x[name].shape)
+        fd = (_loss(dict(x, **{name: x[name] + 1e-5 * v}), do, cfg)
+              - _loss(dict(x, **{name: x[name] - 1e-5 * v}), do, cfg)) / 2e-5
+        worst = max(worst, abs(fd - float(np.sum(g[gname] * v))))
+    assert worst > 1e-4
