@@ -21,6 +21,16 @@ struct ExplicitArgs {
   float* lse;
 };
 
+// Explicit-form backward: the forward's arguments plus its saved output and
+// LSE, the output gradient and the five fp32 input gradients.
+struct BackwardArgs {
+  ExplicitArgs f;             // f.out / f.lse unused; f.out_dt is the dtype of out and d_out
+  const void* out;            // [B, Sq, H, dv]
+  const float* lse;           // [B, H, Sq]
+  const void* d_out;          // [B, Sq, H, dv]
+  float *dq_nope, *dq_pe, *dc_kv, *dk_pe, *dw;   // gradients, same shapes as the inputs
+};
+
 struct DecodeArgs {
   int B, H, dkv, dn, dr, dv;
   int max_len;
@@ -65,6 +75,16 @@ hipError_t launch_krot_f16(const ExplicitArgs& a, const float2* ktab, uint16_t* 
                            hipStream_t stream);
 hipError_t launch_mfma_attention(const ExplicitArgs& a, const uint16_t* kn, const uint16_t* vt,
                                  const uint16_t* krot, const float2* qtab, hipStream_t stream);
+
+// ---- explicit-form backward ----------------------------------------------
+// SIMT path.  Workspace (fp32): Kn [B,H,s_vis,dn], V [B,H,s_vis,dv], krot
+// [B,s_vis,dr], qrot [B,Sq,H,dr], P and dS [B,H,Sq,s_vis], dKn [B,H,s_vis,dn],
+// dV [B,H,s_vis,dv]; q / k rope tables.
+struct SimtBwdWorkspace {
+  float *kn, *v, *krot, *qrot, *p, *ds, *dkn, *dv;
+  const float2 *qtab, *ktab;
+};
+hipError_t launch_simt_backward(const BackwardArgs& a, const SimtBwdWorkspace& w, hipStream_t stream);
 
 // ---- decode ---------------------------------------------------------------
 // q~ is fp32 [B,H,dkv+dr] (SIMT) or bf16 (MFMA); lse_part fp32 [B,ns,H];

@@ -270,6 +270,43 @@ mla_status run_decode(const DecodePlan& p, const DecodeArgs& a, char* ws, hipStr
   return MLA_OK;
 }
 
+// ----------------------------------------------------- explicit backward --
+struct BackwardPlan {
+  ExplicitPlan fwd;                 // the forward's plan (s_vis, tables)
+  bool mfma = false;
+  size_t off_qtab = 0, off_ktab = 0, off_kn = 0, off_v = 0, off_krot = 0, off_qrot = 0, off_p = 0,
+         off_ds = 0, off_dkn = 0, off_dv = 0, total = 0;
+};
+
+// The SIMT backward keeps P and dS for every visible pair; its workspace is
+// bounded here so that a call cannot ask for an absurd allocation.
+constexpr size_t kMaxSimtBwdPairs = size_t(1) << 31;
+
+mla_status make_backward_plan(const mla_explicit_desc* d, BackwardPlan* plan) {
+  BackwardPlan p;
+  mla_explicit_desc fd = *d;
+  if (fd.algo == MLA_ALGO_MFMA) return MLA_ERR_UNSUPPORTED;
+  fd.algo = MLA_ALGO_SIMT;
+  mla_status st = make_explicit_plan(&fd, &p.fwd);
+  if (st != MLA_OK) return st;
+  const size_t B = d->batch, H = d->n_heads, Sq = d->s_q, sv = p.fwd.s_vis, half = d->d_rope / 2;
+  if (B * H * Sq * sv > kMaxSimtBwdPairs) return MLA_ERR_UNSUPPORTED;
+  size_t off = 0;
+  p.off_qtab = off; off = align_up(off + sizeof(float2) * Sq * half);
+  p.off_ktab = off; off = align_up(off + sizeof(float2) * sv * half);
+  p.off_kn = off;   off = align_up(off + 4 * B * H * sv * d->d_nope);
+  p.off_v = off;    off = align_up(off + 4 * B * H * sv * d->d_v);
+  p.off_krot = off; off = align_up(off + 4 * B * sv * d->d_rope);
+  p.off_qrot = off; off = align_up(off + 4 * B * Sq * H * d->d_rope);
+  p.off_p = off;    off = align_up(off + 4 * B * H * Sq * sv);
+  p.off_ds = off;   off = align_up(off + 4 * B * H * Sq * sv);
+  p.off_dkn = off;  off = align_up(off + 4 * B * H * sv * d->d_nope);
+  p.off_dv = off;   off = align_up(off + 4 * B * H * sv * d->d_v);
+  p.total = off;
+  *plan = p;
+  return MLA_OK;
+}
+
 // ------------------------------------------------------- absorbed prefill --
 // The decode problem that an absorbed-form forward maps to: one sequence per
 // query row (B * Sq of them), one chunk each, the batch entry's latent rows
@@ -505,6 +542,77 @@ mla_status mla_decode_absorbed_noalloc(const mla_decode_desc* desc, const void* 
   DecodeArgs a;
   fill_decode_args(desc, q_nope, q_pe, kv_cache, cache_len, w_kv_b, out, lse, &a);
   return run_decode(p, a, static_cast<char*>(ws), s);
+}
+
+size_t mla_bwd_explicit_workspace_size(const mla_explicit_desc* desc) {
+  BackwardPlan p;
+  if (make_backward_plan(desc, &p) != MLA_OK) return 0;
+  return std::max<size_t>(p.total, 1);
+}
+
+mla_status mla_bwd_explicit(const mla_explicit_desc* desc, const void* q_nope, const void* q_pe,
+                            const void* c_kv, const void* k_pe, const void* w_kv_b, const void* out,
+                            const float* lse, const void* d_out, float* dq_nope, float* dq_pe, float* dc_kv,
+                            float* dk_pe, float* dw_kv_b, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  BackwardPlan p;
+  mla_status st = make_backward_plan(desc, &p);
+  if (st != MLA_OK) return st;
+  const bool has_q = desc->s_q > 0, has_kv = desc->s_kv > 0;
+  if (w_kv_b == nullptr || dw_kv_b == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (has_q && (q_nope == nullptr || q_pe == nullptr || out == nullptr || lse == nullptr || d_out == nullptr ||
+                dq_nope == nullptr || dq_pe == nullptr))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (has_kv && (c_kv == nullptr || k_pe == nullptr || dc_kv == nullptr || dk_pe == nullptr))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  BackwardArgs a;
+  ExplicitArgs& f = a.f;
+  f.B = desc->batch; f.Sq = desc->s_q; f.Skv = desc->s_kv; f.H = desc->n_heads;
+  f.dkv = desc->d_kv; f.dn = desc->d_nope; f.dr = desc->d_rope; f.dv = desc->d_v;
+  f.q_pos0 = desc->q_pos0; f.kv_pos0 = desc->kv_pos0; f.causal = desc->causal;
+  f.scale = desc->softmax_scale; f.rope_base = desc->rope_base;
+  f.in_dt = desc->in_dtype; f.out_dt = desc->out_dtype;
+  f.s_vis = p.fwd.s_vis; f.s_pad = p.fwd.s_pad;
+  f.q_nope = q_nope; f.q_pe = q_pe; f.c_kv = c_kv; f.k_pe = k_pe; f.w = w_kv_b;
+  f.out = nullptr; f.lse = nullptr;
+  a.out = out; a.lse = lse; a.d_out = d_out;
+  a.dq_nope = dq_nope; a.dq_pe = dq_pe; a.dc_kv = dc_kv; a.dk_pe = dk_pe; a.dw = dw_kv_b;
+  SimtBwdWorkspace w;
+  w.qtab = reinterpret_cast<float2*>(ws + p.off_qtab);
+  w.ktab = reinterpret_cast<float2*>(ws + p.off_ktab);
+  w.kn = reinterpret_cast<float*>(ws + p.off_kn);
+  w.v = reinterpret_cast<float*>(ws + p.off_v);
+  w.krot = reinterpret_cast<float*>(ws + p.off_krot);
+  w.qrot = reinterpret_cast<float*>(ws + p.off_qrot);
+  w.p = reinterpret_cast<float*>(ws + p.off_p);
+  w.ds = reinterpret_cast<float*>(ws + p.off_ds);
+  w.dkn = reinterpret_cast<float*>(ws + p.off_dkn);
+  w.dv = reinterpret_cast<float*>(ws + p.off_dv);
+  hipError_t e;
+  {
+    TimedLaunch t("rope_tables", s);
+    e = launch_rope_table(const_cast<float2*>(w.qtab), f.q_pos0, f.Sq, f.dr, f.rope_base, s);
+    if (e == hipSuccess) e = launch_rope_table(const_cast<float2*>(w.ktab), f.kv_pos0, f.s_vis, f.dr, f.rope_base, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "rope tables");
+  {
+    // K_nope, V and the rotated key band, as in the forward (no query rows)
+    TimedLaunch t("simt_up_projection", s);
+    ExplicitArgs up = f;
+    up.Sq = 0;
+    e = launch_simt_explicit(up, w.kn, w.v, w.krot, w.qtab, w.ktab, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "simt up-projection");
+  {
+    TimedLaunch t("simt_backward", s);
+    e = launch_simt_backward(a, w, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "simt backward");
+  return MLA_OK;
 }
 
 size_t mla_fwd_absorbed_workspace_size(const mla_explicit_desc* desc) {

@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "mla_fwd_explicit_workspace_size", "mla_fwd_explicit", "mla_fwd_explicit_workspace_layout",
     "mla_decode_absorbed_workspace_size", "mla_decode_absorbed", "mla_decode_absorbed_workspace_layout",
     "mla_fwd_absorbed_workspace_size", "mla_fwd_absorbed", "mla_decode_absorbed_noalloc",
+    "mla_bwd_explicit_workspace_size", "mla_bwd_explicit",
     "mla_status_string", "mla_last_error", "mla_build_info",
     "mla_timing_begin", "mla_timing_end", "mla_timing_reset", "mla_timing_count", "mla_timing_get",
 )
@@ -88,6 +89,10 @@ def _lib() -> ctypes.CDLL:
         lib.mla_fwd_absorbed_workspace_size.restype = sz
         lib.mla_fwd_absorbed.argtypes = [ctypes.POINTER(MlaExplicitDesc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.mla_fwd_absorbed.restype = ctypes.c_int
+        lib.mla_bwd_explicit_workspace_size.argtypes = [ctypes.POINTER(MlaExplicitDesc)]
+        lib.mla_bwd_explicit_workspace_size.restype = sz
+        lib.mla_bwd_explicit.argtypes = [ctypes.POINTER(MlaExplicitDesc)] + [vp] * 14 + [sz, vp]
+        lib.mla_bwd_explicit.restype = ctypes.c_int
         lib.mla_fwd_explicit_workspace_layout.argtypes = [ctypes.POINTER(MlaExplicitDesc), ctypes.POINTER(sz)]
         lib.mla_fwd_explicit_workspace_layout.restype = ctypes.c_int
         lib.mla_decode_absorbed_workspace_size.argtypes = [ctypes.POINTER(MlaDecodeDesc)]
@@ -265,6 +270,70 @@ def _fwd(explicit: bool, q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.T
                                workspace.data_ptr(), workspace.numel(), _stream(dev))
     _check(st, name)
     return out, (lse if return_lse else None), workspace
+
+
+def mla_bwd_explicit_workspace_size(desc: MlaExplicitDesc) -> int:
+    return int(_lib().mla_bwd_explicit_workspace_size(ctypes.byref(desc)))
+
+
+def mla_bwd_explicit(q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
+                     w_kv_b: torch.Tensor, out: torch.Tensor, lse: torch.Tensor, d_out: torch.Tensor, *,
+                     q_pos0: int = 0, kv_pos0: int = 0, causal: bool = True,
+                     softmax_scale: Optional[float] = None, rope_base: float = 10000.0,
+                     algo: int = MLA_ALGO_AUTO, grads: Optional[dict] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Explicit-form backward; see mla_bwd_explicit in include/mla.h.
+
+    Inputs as for mla_fwd_explicit plus the forward's out [B,S_q,H,d_v] and
+    lse [B,H,S_q] (fp32) and d_out (out's dtype).  Returns (grads, workspace)
+    with grads a dict of fp32 tensors dq_nope, dq_pe, dc_kv, dk_pe, dw_kv_b
+    (caller-supplied ones in `grads` are checked and written in place).
+    """
+    if q_nope.dim() != 4 or q_pe.dim() != 4 or c_kv.dim() != 3 or k_pe.dim() != 3 or w_kv_b.dim() != 2:
+        raise ValueError("expected q_nope, q_pe [B,S_q,H,*], c_kv, k_pe [B,S_kv,*], w_kv_b [H*(d_nope+d_v), d_kv]")
+    B, S_q, H, d_nope = q_nope.shape
+    S_kv, d_kv = c_kv.shape[1], c_kv.shape[2]
+    d_rope = q_pe.shape[-1]
+    if H < 1 or w_kv_b.shape[0] % H != 0 or w_kv_b.shape[0] // H <= d_nope:
+        raise ValueError(f"w_kv_b rows ({w_kv_b.shape[0]}) must be H*(d_nope+d_v) with H={H}, d_nope={d_nope}")
+    d_v = w_kv_b.shape[0] // H - d_nope
+    dev = q_nope.device
+    _expect(q_nope, "q_nope", (B, S_q, H, d_nope), q_nope.dtype, dev)
+    _expect(q_pe, "q_pe", (B, S_q, H, d_rope), q_nope.dtype, dev)
+    _expect(c_kv, "c_kv", (B, S_kv, d_kv), q_nope.dtype, dev)
+    _expect(k_pe, "k_pe", (B, S_kv, d_rope), q_nope.dtype, dev)
+    _expect(w_kv_b, "w_kv_b", (H * (d_nope + d_v), d_kv), q_nope.dtype, dev)
+    _expect(out, "out", (B, S_q, H, d_v), out.dtype, dev)
+    _expect(d_out, "d_out", (B, S_q, H, d_v), out.dtype, dev)
+    _expect(lse, "lse", (B, H, S_q), torch.float32, dev)
+    shapes = {"dq_nope": (B, S_q, H, d_nope), "dq_pe": (B, S_q, H, d_rope), "dc_kv": (B, S_kv, d_kv),
+              "dk_pe": (B, S_kv, d_rope), "dw_kv_b": (H * (d_nope + d_v), d_kv)}
+    grads = dict(grads or {})
+    for k, shp in shapes.items():
+        if k in grads:
+            _expect(grads[k], k, shp, torch.float32, dev)
+    if workspace is not None:
+        _expect_workspace(workspace, dev)
+    _expect_cuda(dev)
+    desc = explicit_desc(batch=B, s_q=S_q, s_kv=S_kv, n_heads=H, d_kv=d_kv, d_nope=d_nope, d_rope=d_rope,
+                         d_v=d_v, q_pos0=q_pos0, kv_pos0=kv_pos0, causal=causal, softmax_scale=softmax_scale,
+                         rope_base=rope_base, in_dtype=_dtype_code(q_nope.dtype), out_dtype=_dtype_code(out.dtype),
+                         algo=algo)
+    ws_bytes = mla_bwd_explicit_workspace_size(desc)
+    if ws_bytes == 0:
+        _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,
+               "mla_bwd_explicit_workspace_size")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    for k, shp in shapes.items():
+        if k not in grads:
+            grads[k] = torch.empty(shp, dtype=torch.float32, device=dev)
+    st = _lib().mla_bwd_explicit(ctypes.byref(desc), _ptr(q_nope), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe),
+                                 _ptr(w_kv_b), _ptr(out), _ptr(lse), _ptr(d_out), _ptr(grads["dq_nope"]),
+                                 _ptr(grads["dq_pe"]), _ptr(grads["dc_kv"]), _ptr(grads["dk_pe"]),
+                                 _ptr(grads["dw_kv_b"]), workspace.data_ptr(), workspace.numel(), _stream(dev))
+    _check(st, "mla_bwd_explicit")
+    return grads, workspace
 
 
 # ------------------------------------------------------------------- decode --

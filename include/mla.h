@@ -270,6 +270,46 @@ mla_status mla_fwd_absorbed(const mla_explicit_desc* desc,
                             void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Backward of the explicit form                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Gradients of sum(d_out * out) with respect to the five inputs of
+ * mla_fwd_explicit, given the forward's output and LSE ("A Training-Memory
+ * Regression in MLA Sequence Parallelism ... LAGA" (Pith review): the
+ * training setting; "If this is right" states that LAGA's parameter gradients
+ * equal the explicit form's).  With P the softmax of the forward's logits,
+ *   dV = P^T d_out,  dP = d_out V^T,  dS = P (dP - rowsum(d_out * out)),
+ *   dq_nope = s dS K_nope,  dK_nope = s dS^T q_nope  (s = softmax_scale),
+ *   dq_pe = R^T(s dS R(k_pe)),  dk_pe = R^T(s sum_h dS^T R(q_pe)),
+ *   dc_kv = sum_h dK_nope W_UK[h] + dV W_UV[h],  dW_UK[h] = dK_nope^T c_kv,
+ *   dW_UV[h] = dV^T c_kv,
+ * where R^T, the transpose of the RoPE rotation, rotates by the negative
+ * angle.
+ *
+ *   desc, q_nope, q_pe, c_kv, k_pe, w_kv_b: as given to mla_fwd_explicit
+ *   out   [B, s_q, H, d_v] (desc->out_dtype): the forward's output
+ *   lse   [B, H, s_q] fp32: the forward's LSE
+ *   d_out [B, s_q, H, d_v] (desc->out_dtype): gradient with respect to out
+ *   dq_nope [B, s_q, H, d_nope], dq_pe [B, s_q, H, d_rope], dc_kv [B, s_kv, d_kv],
+ *   dk_pe [B, s_kv, d_rope], dw_kv_b [H*(d_nope+d_v), d_kv]: fp32 outputs,
+ *   fully written (latent rows no query sees get zero gradients).
+ * Workspace: mla_bwd_explicit_workspace_size() bytes.  The SIMT kernels
+ * (any head geometry, fp32 arithmetic) keep the probabilities and their
+ * gradients for every visible pair: at most 2^31 pairs per call
+ * (B * H * s_q * visible keys), else MLA_ERR_UNSUPPORTED. */
+size_t mla_bwd_explicit_workspace_size(const mla_explicit_desc* desc);
+
+mla_status mla_bwd_explicit(const mla_explicit_desc* desc,
+                            const void* q_nope, const void* q_pe,
+                            const void* c_kv, const void* k_pe,
+                            const void* w_kv_b,
+                            const void* out, const float* lse, const void* d_out,
+                            float* dq_nope, float* dq_pe, float* dc_kv, float* dk_pe,
+                            float* dw_kv_b,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Per-kernel timing (profiling aid; not needed for computing)               */
 /* ------------------------------------------------------------------------ */
 /* Between mla_timing_begin() and mla_timing_end() on the calling thread, each

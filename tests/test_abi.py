@@ -361,3 +361,23 @@ def test_noalloc_limit_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define MLA_DECODE_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == mla.DECODE_NOALLOC_MAX_BYTES
+
+
+def _header_arity():
+    """Number of parameters of every function include/mla.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(mla_[a-z_]+)\s*\(([^;{]*?)\)\s*;", text):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argtypes_match_header_arity():
+    """Every ctypes prototype has exactly as many parameters as the C
+    declaration, so no call can pass a pointer where a size is expected."""
+    lib = mla.library()
+    arity = _header_arity()
+    assert set(arity) == set(mla.EXPORTED_SYMBOLS)
+    for name, n in arity.items():
+        assert len(getattr(lib, name).argtypes) == n, (name, len(getattr(lib, name).argtypes), n)
