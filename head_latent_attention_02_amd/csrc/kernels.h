@@ -86,6 +86,28 @@ struct SimtBwdWorkspace {
 };
 hipError_t launch_simt_backward(const BackwardArgs& a, const SimtBwdWorkspace& w, hipStream_t stream);
 
+// MFMA path (bf16 inputs, d_kv 512, d_nope 128, d_rope 64, d_v 128).  fp16
+// workspace tensors: the forward's kn [bh][s_pad][128], vt [bh][128][s_pad],
+// krot [b][s_pad][64]; Q = [q_nope ; R(q_pe)] as qf [bh][sq_pad][192] and
+// qft [bh][192][sq_pad]; dO as dof [bh][sq_pad][128] and doft
+// [bh][128][sq_pad]; vrow [bh][s_pad][128]; knt [bh][128][s_pad]; krt
+// [b][64][s_pad]; dkv [b][s_pad][H*256] and dkvt [H*256][b*s_pad] ([dK_nope |
+// dV] per head, scaled); wt [512][H*256]; ct [512][b*s_pad].  fp32: dvec
+// [bh][sq_pad] (dO . out), dkr [bh][s_pad][64].  sq_pad = s_q rounded up to 128.
+struct MfmaBwdWorkspace {
+  float2 *qtab, *ktab;
+  uint16_t *kn, *vt, *krot, *qf, *qft, *dof, *doft, *vrow, *knt, *krt, *dkv, *dkvt, *wt, *ct;
+  float *dvec, *dkr;
+  int sq_pad;
+};
+// Bytes of workspace (base == nullptr) or the carving of `base` into `w`.
+size_t mfma_backward_workspace(const ExplicitArgs& f, MfmaBwdWorkspace* w, char* base);
+hipError_t launch_bwd_prep(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t stream);
+hipError_t launch_bwd_kv(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t stream);
+hipError_t launch_bwd_dq(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t stream);
+hipError_t launch_bwd_dkpe(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t stream);
+hipError_t launch_bwd_gemms(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t stream);
+
 // ---- decode ---------------------------------------------------------------
 // q~ is fp32 [B,H,dkv+dr] (SIMT) or bf16 (MFMA); lse_part fp32 [B,ns,H];
 // o_part [B,ns,H,dkv] fp32 (SIMT) or fp16 (MFMA).

@@ -1,0 +1,796 @@
+// Backward of the explicit-form MLA forward on fp16 MFMA (fp32 accumulate),
+// for d_kv 512, d_nope 128, d_rope 64, d_v 128 and bf16 inputs: the gradient
+// of sum(d_out * out) with respect to q_nope, q_pe, c_kv, k_pe and W_kv_b (the
+// training setting of "A Training-Memory Regression in MLA Sequence
+// Parallelism ... LAGA" (Pith review); "If this is right" on gradients).
+//
+// With sigma the softmax scale, P the softmax of the forward (recomputed from
+// its LSE), D_i = d_out_i . out_i:
+//   dS = P (dO V^T - D),  dV = P^T dO,  dK = sigma dS^T Q,  dQ = sigma dS K
+// over the 192-wide [q_nope ; R(q_pe)] / [K_nope ; R(k_pe)] and the 128-wide V,
+// then dc_kv = dKV W (dKV = [dK_nope | dV] per head), dW = dKV^T c_kv, and the
+// RoPE bands rotated back (the transpose of a rotation turns by the negative
+// angle), the key band summed over heads.
+//
+// Kernels (one launch each):
+//   prep_q      fp16 Q = [q_nope ; R(q_pe)] and dO in row layout [bh][i][d] and
+//               transposed layout [bh][d][i] (query rows padded to 128 with
+//               zeros), and D = dO . out in fp32.
+//   transpose   V [bh][key][128] from the up-projection's V^T, K_nope^T, the
+//               rotated key band transposed, W^T and c_kv^T (fp16).
+//   kv          per (b, h, 128 keys): 4 waves of 32 keys hold K and V as MFMA
+//               B operands and stream 32-query tiles of Q, dO, Q^T, dO^T
+//               through LDS; S = Q K^T, dP = dO V^T, dV^T += dO^T P,
+//               dK^T += Q^T dS.  Writes dKV in both row and column layouts
+//               (fp16, for the two GEMMs) and the per-head key-band gradient.
+//   dq          per (b, h, 128 queries): 4 waves of 32 queries hold Q^T and
+//               dO^T and stream 32-key tiles of K, V and K^T; S^T = K Q^T,
+//               dP^T = V dO^T, dQ^T += K^T dS^T; writes dq_nope and the
+//               rotated-back dq_pe.
+//   dk_pe       the head sum of the key-band gradient, rotated back.
+//   gemm_nt     C = A B^T with A, B fp16 row-major and fp32 C: dc_kv and dW.
+//
+// Operand order.  Rows of the streamed Q / dO (kv kernel) and K / V (dq
+// kernel) tiles sit in LDS in the permuted order rho -> (rho with bits 2 and
+// 3 swapped): the accumulator row that lane half x holds in element 4g + r is
+// 8g + 4x + r, and with that order the 8 elements 8u .. 8u+7 of a lane are the
+// 8 consecutive indices 16u + 8x .. 16u + 8x + 7 that it supplies as the
+// k-slots of the next MFMA, so P and dS go from accumulators to MFMA operands
+// inside the lane.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int DN = 128, DR = 64, DQK = 192, DV = 128, DKV = 512;
+constexpr int HD = DN + DV;          // rows of W_kv_b per head
+
+typedef _Float16 f16;
+
+__device__ __forceinline__ f32x16_t mfma(f16x8_t a, f16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// rho <-> index inside a 32-block: swap bits 2 and 3 (an involution)
+__device__ __forceinline__ int perm32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+__device__ __forceinline__ uint16_t h_bits(float x) { return float_to_f16_bits(x); }
+
+// ---------------------------------------------------------------- prep_q --
+// One block per (b, h, 32 query rows); thread t handles element columns.
+template <mla_dtype OT>
+__global__ void __launch_bounds__(256)
+prep_q_kernel(BackwardArgs a, const float2* __restrict__ qtab, uint16_t* __restrict__ qf, uint16_t* __restrict__ qft,
+              uint16_t* __restrict__ dof, uint16_t* __restrict__ doft, float* __restrict__ dvec, int sq_pad) {
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[32][DQK + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[32][DV + 8];
+  __shared__ float red[32][9];
+  const ExplicitArgs& f = a.f;
+  const int i0 = blockIdx.x * 32, h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = (int64_t)b * f.H + h;
+  const int tid = threadIdx.x;
+  // rows: r = tid / 8 (32 rows), 8 threads per row
+  const int r = tid >> 3, c8 = tid & 7;
+  const int i = i0 + r;
+  const bool live = i < f.Sq;
+  const int64_t row = ((int64_t)b * f.Sq + (live ? i : 0)) * f.H + h;
+  // q_nope: 16 columns per thread
+  for (int k = 0; k < DN / 8; ++k) {
+    const int d = c8 * (DN / 8) + k;
+    const float v = live ? bf16_bits_to_float(static_cast<const uint16_t*>(f.q_nope)[row * DN + d]) : 0.f;
+    Qs[r][d] = h_bits(v);
+  }
+  // rope pairs (m, m + 32): 4 pairs per thread
+  for (int k = 0; k < 4; ++k) {
+    const int m = c8 * 4 + k;
+    float lo = 0.f, hi = 0.f;
+    if (live) {
+      const uint16_t* qp = static_cast<const uint16_t*>(f.q_pe) + row * DR;
+      const float x0 = bf16_bits_to_float(qp[m]), x1 = bf16_bits_to_float(qp[m + 32]);
+      const float2 cs = qtab[(int64_t)i * 32 + m];
+      lo = x0 * cs.x - x1 * cs.y;
+      hi = x1 * cs.x + x0 * cs.y;
+    }
+    Qs[r][DN + m] = h_bits(lo);
+    Qs[r][DN + m + 32] = h_bits(hi);
+  }
+  // dO and D = dO . out
+  float dsum = 0.f;
+  for (int k = 0; k < DV / 8; ++k) {
+    const int d = c8 * (DV / 8) + k;
+    float g = 0.f;
+    if (live) {
+      g = load_elem<OT>(a.d_out, row * DV + d);
+      dsum += g * load_elem<OT>(a.out, row * DV + d);
+    }
+    Ds[r][d] = h_bits(g);
+  }
+  red[r][c8] = dsum;
+  __syncthreads();
+  if (c8 == 0) {
+    float s = 0.f;
+    for (int k = 0; k < 8; ++k) s += red[r][k];
+    dvec[bh * sq_pad + i] = live ? s : 0.f;
+  }
+  // row layouts: 192 / 128 fp16 per row, 16-byte pieces
+  for (int c = tid; c < 32 * (DQK / 8); c += 256) {
+    const int rr = c / (DQK / 8), cc = c % (DQK / 8);
+    *reinterpret_cast<u32x4_t*>(qf + (bh * sq_pad + i0 + rr) * DQK + cc * 8) =
+        *reinterpret_cast<const u32x4_t*>(&Qs[rr][cc * 8]);
+  }
+  for (int c = tid; c < 32 * (DV / 8); c += 256) {
+    const int rr = c / (DV / 8), cc = c % (DV / 8);
+    *reinterpret_cast<u32x4_t*>(dof + (bh * sq_pad + i0 + rr) * DV + cc * 8) =
+        *reinterpret_cast<const u32x4_t*>(&Ds[rr][cc * 8]);
+  }
+  // transposed layouts: column d, 32 queries (8 per 16-byte piece)
+  for (int c = tid; c < DQK * 4; c += 256) {
+    const int d = c >> 2, q8 = (c & 3) * 8;
+    u32x4_t v;
+    for (int e = 0; e < 4; ++e) v[e] = (uint32_t)Qs[q8 + 2 * e][d] | ((uint32_t)Qs[q8 + 2 * e + 1][d] << 16);
+    *reinterpret_cast<u32x4_t*>(qft + (bh * DQK + d) * sq_pad + i0 + q8) = v;
+  }
+  for (int c = tid; c < DV * 4; c += 256) {
+    const int d = c >> 2, q8 = (c & 3) * 8;
+    u32x4_t v;
+    for (int e = 0; e < 4; ++e) v[e] = (uint32_t)Ds[q8 + 2 * e][d] | ((uint32_t)Ds[q8 + 2 * e + 1][d] << 16);
+    *reinterpret_cast<u32x4_t*>(doft + (bh * DV + d) * sq_pad + i0 + q8) = v;
+  }
+}
+
+// ------------------------------------------------------------- transpose --
+// out[z][c][r] = in[z][r][c] for r < rows_valid (0 for rows_valid <= r < rows),
+// fp16 out, in fp16 or bf16 bits.  in: row stride in_ld, batch stride in_bs;
+// out: row stride out_ld, batch stride out_bs.  32 x 32 tiles.
+template <bool IN_BF16>
+__global__ void __launch_bounds__(256)
+transpose_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out, int rows, int rows_valid, int cols,
+                 int64_t in_ld, int64_t in_bs, int64_t out_ld, int64_t out_bs) {
+  __shared__ uint16_t T[32][34];
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32, z = blockIdx.z;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;    // 32 x 8
+  for (int k = 0; k < 32; k += 8) {
+    const int r = r0 + ty + k, c = c0 + tx;
+    uint16_t v = 0;
+    if (r < rows_valid && c < cols) {
+      v = in[z * in_bs + (int64_t)r * in_ld + c];
+      if (IN_BF16) v = h_bits(bf16_bits_to_float(v));
+    }
+    T[ty + k][tx] = v;
+  }
+  __syncthreads();
+  for (int k = 0; k < 32; k += 8) {
+    const int c = c0 + ty + k, r = r0 + tx;
+    if (c < cols && r < rows) out[z * out_bs + (int64_t)c * out_ld + r] = T[tx][ty + k];
+  }
+}
+
+// -------------------------------------------------------------------- kv --
+// LDS stage of one 32-query tile (fp16 elements; rows padded by 8 elements):
+//   Qp  [32][192+8]  rows in permuted order      QT  [192][32+8]
+//   dOp [32][128+8]  rows in permuted order      dOT [128][32+8]
+//   lse, D [32] in permuted order (fp32)
+constexpr int QP_LD = DQK + 8, DOP_LD = DV + 8, QT_LD = 40;
+constexpr int KV_STAGE_H = 32 * QP_LD + 32 * DOP_LD + DQK * QT_LD + DV * QT_LD;   // fp16 elements
+constexpr int KV_STAGE_B = KV_STAGE_H * 2 + 2 * 32 * 4;                           // + lse, D
+constexpr int KV_CHUNKS = 32 * (DQK / 8) + 32 * (DV / 8) + DQK * 4 + DV * 4;      // 16-byte pieces (2560)
+constexpr int KV_PER_THREAD = KV_CHUNKS / 256;                                     // 10
+static_assert(KV_CHUNKS % 256 == 0, "tile pieces must split evenly");
+
+__global__ void __launch_bounds__(256)
+kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __restrict__ qft,
+          const uint16_t* __restrict__ dof, const uint16_t* __restrict__ doft, const float* __restrict__ dvec,
+          const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vt, const uint16_t* __restrict__ krot,
+          uint16_t* __restrict__ dkv, uint16_t* __restrict__ dkvt, float* __restrict__ dkr, int sq_pad,
+          int n_kb) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem_kv[2 * KV_STAGE_B];
+  const ExplicitArgs& f = a.f;
+  // longest first: key block 0 sees the most queries
+  const int kbi = blockIdx.x % n_kb, bhi = blockIdx.x / n_kb;
+  const int b = bhi / f.H, h = bhi % f.H;
+  const int64_t bh = (int64_t)b * f.H + h;
+  const int kb = kbi * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hb = lane >> 5;
+  const int key = kb + wave * 32 + l32;            // this lane's key (accumulator column)
+  const float c2 = f.scale * MLA_LOG2E;
+
+  // K (B operand of S = Q K^T: lane = key, k-slots 16 ks + 8 hb ..) and V
+  // (B operand of dP = dO V^T) of the lane's key, loaded once
+  f16x8_t kb_[DQK / 16], vb_[DV / 16];
+  {
+    const int kk = min(key, f.s_pad - 1);
+    const uint16_t* kr = kn + (bh * f.s_pad + kk) * DN;
+#pragma unroll
+    for (int ks = 0; ks < DN / 16; ++ks)
+      kb_[ks] = *reinterpret_cast<const f16x8_t*>(kr + 16 * ks + 8 * hb);
+    const uint16_t* rr = krot + ((int64_t)b * f.s_pad + kk) * DR;
+#pragma unroll
+    for (int ks = 0; ks < DR / 16; ++ks)
+      kb_[DN / 16 + ks] = *reinterpret_cast<const f16x8_t*>(rr + 16 * ks + 8 * hb);
+    const uint16_t* vc = vt + bh * DV * f.s_pad + kk;
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vb_[ks][e] = __builtin_bit_cast(f16, vc[(int64_t)(16 * ks + 8 * hb + e) * f.s_pad]);
+  }
+
+  // query tiles: from the first one that can see key kb to the last
+  int qt0 = 0;
+  if (f.causal) {
+    const int64_t first = (int64_t)kb + f.kv_pos0 - f.q_pos0;     // first query that sees key kb
+    qt0 = (int)max((int64_t)0, min(first, (int64_t)sq_pad) / 32);
+  }
+  const int nqt = sq_pad / 32;
+
+  f32x16_t dvt[DV / 32], dkt[DQK / 32];
+#pragma unroll
+  for (int d = 0; d < DV / 32; ++d) dvt[d] = f32x16_t{};
+#pragma unroll
+  for (int d = 0; d < DQK / 32; ++d) dkt[d] = f32x16_t{};
+
+  // tile loader: piece c of the tile into registers, then into a stage
+  u32x4_t stg[KV_PER_THREAD];
+  float sl = 0.f, sd = 0.f;                       // lse / D of one query (threads 0..31)
+  auto load_tile = [&](int qt) __attribute__((always_inline)) {
+    const int q0 = qt * 32;
+#pragma unroll
+    for (int k = 0; k < KV_PER_THREAD; ++k) {
+      const int c = tid + 256 * k;
+      const uint16_t* src;
+      if (c < 768) {                                     // Qp: row rho <- query perm(rho)
+        const int rho = c / 24, cc = c % 24;
+        src = qf + (bh * sq_pad + q0 + perm32(rho)) * DQK + cc * 8;
+      } else if (c < 1280) {                             // dOp
+        const int c2_ = c - 768, rho = c2_ / 16, cc = c2_ % 16;
+        src = dof + (bh * sq_pad + q0 + perm32(rho)) * DV + cc * 8;
+      } else if (c < 2048) {                             // QT: row d, 8 queries
+        const int c2_ = c - 1280, d = c2_ >> 2, q8 = (c2_ & 3) * 8;
+        src = qft + (bh * DQK + d) * sq_pad + q0 + q8;
+      } else {                                           // dOT
+        const int c2_ = c - 2048, d = c2_ >> 2, q8 = (c2_ & 3) * 8;
+        src = doft + (bh * DV + d) * sq_pad + q0 + q8;
+      }
+      stg[k] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+    if (tid < 32) {
+      const int i = q0 + perm32(tid);                    // stored at rho = tid
+      sl = (i < f.Sq) ? a.lse[bh * f.Sq + i] : INFINITY;
+      sd = dvec[bh * sq_pad + i];
+    }
+  };
+  auto store_tile = [&](int s) __attribute__((always_inline)) {
+    uint16_t* st = reinterpret_cast<uint16_t*>(smem_kv + s * KV_STAGE_B);
+#pragma unroll
+    for (int k = 0; k < KV_PER_THREAD; ++k) {
+      const int c = tid + 256 * k;
+      uint16_t* dst;
+      if (c < 768) {
+        const int rho = c / 24, cc = c % 24;
+        dst = st + rho * QP_LD + cc * 8;
+      } else if (c < 1280) {
+        const int c2_ = c - 768, rho = c2_ / 16, cc = c2_ % 16;
+        dst = st + 32 * QP_LD + rho * DOP_LD + cc * 8;
+      } else if (c < 2048) {
+        const int c2_ = c - 1280, d = c2_ >> 2, q8 = (c2_ & 3) * 8;
+        dst = st + 32 * QP_LD + 32 * DOP_LD + d * QT_LD + q8;
+      } else {
+        const int c2_ = c - 2048, d = c2_ >> 2, q8 = (c2_ & 3) * 8;
+        dst = st + 32 * QP_LD + 32 * DOP_LD + DQK * QT_LD + d * QT_LD + q8;
+      }
+      *reinterpret_cast<u32x4_t*>(dst) = stg[k];
+    }
+    if (tid < 32) {
+      float* lsd = reinterpret_cast<float*>(smem_kv + s * KV_STAGE_B + KV_STAGE_H * 2);
+      lsd[tid] = sl;
+      lsd[32 + tid] = sd;
+    }
+  };
+
+  if (qt0 < nqt) {
+    load_tile(qt0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int s = (qt - qt0) & 1;
+    if (qt + 1 < nqt) load_tile(qt + 1);
+    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem_kv + s * KV_STAGE_B);
+    const uint16_t* Qp = st;
+    const uint16_t* dOp = st + 32 * QP_LD;
+    const uint16_t* QT = dOp + 32 * DOP_LD;
+    const uint16_t* dOT = QT + DQK * QT_LD;
+    const float* lsd = reinterpret_cast<const float*>(smem_kv + s * KV_STAGE_B + KV_STAGE_H * 2);
+    // S = Qp K^T, dP = dOp V^T  (rows: permuted queries, columns: keys)
+    f32x16_t sacc = {}, pacc = {};
+#pragma unroll
+    for (int ks = 0; ks < DQK / 16; ++ks)
+      sacc = mfma(*reinterpret_cast<const f16x8_t*>(Qp + l32 * QP_LD + 16 * ks + 8 * hb), kb_[ks], sacc);
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks)
+      pacc = mfma(*reinterpret_cast<const f16x8_t*>(dOp + l32 * DOP_LD + 16 * ks + 8 * hb), vb_[ks], pacc);
+    // P and dS; element e is query row rho = 8 (e/4) + 4 hb + e%4
+    f16x8_t pb[2], sb[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
+      const int i = qt * 32 + perm32(rho);
+      const float lse = lsd[rho], dd = lsd[32 + rho];
+      const bool vis = key < f.s_vis && i < f.Sq && lse != -INFINITY &&
+                       (!f.causal || f.kv_pos0 + key <= f.q_pos0 + i);
+      const float p = vis ? fast_exp2(sacc[e] * c2 - lse * MLA_LOG2E) : 0.f;
+      const float ds = p * (pacc[e] - dd);
+      pb[e >> 3][e & 7] = (f16)p;
+      sb[e >> 3][e & 7] = (f16)ds;
+    }
+    // dV^T += dO^T P,  dK^T += Q^T dS  (k-slots: queries 16u + 8hb .. in natural order)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+        dvt[db] = mfma(*reinterpret_cast<const f16x8_t*>(dOT + (db * 32 + l32) * QT_LD + 16 * u + 8 * hb), pb[u],
+                       dvt[db]);
+#pragma unroll
+      for (int db = 0; db < DQK / 32; ++db)
+        dkt[db] = mfma(*reinterpret_cast<const f16x8_t*>(QT + (db * 32 + l32) * QT_LD + 16 * u + 8 * hb), sb[u],
+                       dkt[db]);
+    }
+    __syncthreads();                                     // stage s is no longer read
+    if (qt + 1 < nqt) store_tile(s ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dKV (fp16, both layouts) and the key-band gradient -------
+  // accumulator element e of d-block db is row d = 32 db + 8 (e/4) + 4 hb + e%4
+  if (key < f.s_pad) {
+    uint16_t* rowp = dkv + ((int64_t)b * f.s_pad + key) * ((int64_t)f.H * HD) + (int64_t)h * HD;
+    const int64_t ncol = (int64_t)f.B * f.s_pad;
+#pragma unroll
+    for (int db = 0; db < DQK / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hb;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = f.scale * dkt[db][4 * g + r];
+        if (d < DN) {
+          u32x2_t pk;
+          pk[0] = pack_f16x2(v[0], v[1]);
+          pk[1] = pack_f16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2_t*>(rowp + d) = pk;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            dkvt[((int64_t)h * HD + d + r) * ncol + (int64_t)b * f.s_pad + key] = h_bits(v[r]);
+        } else {
+          *reinterpret_cast<f32x4_t*>(dkr + (bh * f.s_pad + key) * DR + (d - DN)) = f32x4_t{v[0], v[1], v[2], v[3]};
+        }
+      }
+#pragma unroll
+    for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hb;
+        u32x2_t pk;
+        pk[0] = pack_f16x2(dvt[db][4 * g], dvt[db][4 * g + 1]);
+        pk[1] = pack_f16x2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
+        *reinterpret_cast<u32x2_t*>(rowp + DN + d) = pk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dkvt[((int64_t)h * HD + DN + d + r) * ncol + (int64_t)b * f.s_pad + key] = h_bits(dvt[db][4 * g + r]);
+      }
+  }
+}
+
+// -------------------------------------------------------------------- dq --
+// LDS stage of one 32-key tile: Kp [32][192+8] and Vp [32][128+8] in permuted
+// key order, KT [192][32+8] in natural key order.
+constexpr int KP_LD = DQK + 8, VP_LD = DV + 8, KT_LD = 40;
+constexpr int DQ_STAGE_H = 32 * KP_LD + 32 * VP_LD + DQK * KT_LD;
+constexpr int DQ_CHUNKS = 32 * (DQK / 8) + 32 * (DV / 8) + DQK * 4;                 // 2048
+constexpr int DQ_PER_THREAD = DQ_CHUNKS / 256;                                      // 8
+static_assert(DQ_CHUNKS % 256 == 0, "tile pieces must split evenly");
+
+__global__ void __launch_bounds__(256)
+dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __restrict__ dof,
+          const float* __restrict__ dvec, const uint16_t* __restrict__ kn, const uint16_t* __restrict__ krot,
+          const uint16_t* __restrict__ vrow, const uint16_t* __restrict__ knt, const uint16_t* __restrict__ krt,
+          const float2* __restrict__ qtab, int sq_pad, int n_qb) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem_dq[2 * DQ_STAGE_H * 2];
+  const ExplicitArgs& f = a.f;
+  // longest first: the last query block sees the most keys
+  const int qbi = n_qb - 1 - (int)(blockIdx.x % n_qb), bhi = blockIdx.x / n_qb;
+  const int b = bhi / f.H, h = bhi % f.H;
+  const int64_t bh = (int64_t)b * f.H + h;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hb = lane >> 5;
+  const int i = qbi * 128 + wave * 32 + l32;        // this lane's query (accumulator column)
+  const float c2 = f.scale * MLA_LOG2E;
+
+  f16x8_t qb_[DQK / 16], ob_[DV / 16];               // B operands: lane = query, k-slots 16 ks + 8 hb ..
+#pragma unroll
+  for (int ks = 0; ks < DQK / 16; ++ks)
+    qb_[ks] = *reinterpret_cast<const f16x8_t*>(qf + (bh * sq_pad + i) * DQK + 16 * ks + 8 * hb);
+#pragma unroll
+  for (int ks = 0; ks < DV / 16; ++ks)
+    ob_[ks] = *reinterpret_cast<const f16x8_t*>(dof + (bh * sq_pad + i) * DV + 16 * ks + 8 * hb);
+  const float lse = (i < f.Sq) ? a.lse[bh * f.Sq + i] : -INFINITY;
+  const float dd = dvec[bh * sq_pad + i];
+
+  // key tiles visible to the block's last query
+  int kend = f.s_vis;
+  if (f.causal) {
+    const int i_last = min(qbi * 128 + 127, f.Sq - 1);
+    const int64_t lim = f.q_pos0 + i_last - f.kv_pos0 + 1;
+    kend = (int)max((int64_t)0, min(lim, (int64_t)f.s_vis));
+  }
+  const int nkt = (kend + 31) / 32;
+
+  f32x16_t dqt[DQK / 32];
+#pragma unroll
+  for (int d = 0; d < DQK / 32; ++d) dqt[d] = f32x16_t{};
+
+  u32x4_t stg[DQ_PER_THREAD];
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * 32;
+#pragma unroll
+    for (int k = 0; k < DQ_PER_THREAD; ++k) {
+      const int c = tid + 256 * k;
+      const uint16_t* src;
+      if (c < 768) {                                     // Kp: row rho <- key perm(rho)
+        const int rho = c / 24, cc = c % 24, j = k0 + perm32(rho);
+        src = cc < 16 ? kn + (bh * f.s_pad + j) * DN + cc * 8 : krot + ((int64_t)b * f.s_pad + j) * DR + (cc - 16) * 8;
+      } else if (c < 1280) {                             // Vp
+        const int c2_ = c - 768, rho = c2_ / 16, cc = c2_ % 16;
+        src = vrow + (bh * f.s_pad + k0 + perm32(rho)) * DV + cc * 8;
+      } else {                                           // KT: row d, 8 keys
+        const int c2_ = c - 1280, d = c2_ >> 2, k8 = (c2_ & 3) * 8;
+        src = d < DN ? knt + (bh * DN + d) * f.s_pad + k0 + k8 : krt + ((int64_t)b * DR + d - DN) * f.s_pad + k0 + k8;
+      }
+      stg[k] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+  };
+  auto store_tile = [&](int s) __attribute__((always_inline)) {
+    uint16_t* st = reinterpret_cast<uint16_t*>(smem_dq) + s * DQ_STAGE_H;
+#pragma unroll
+    for (int k = 0; k < DQ_PER_THREAD; ++k) {
+      const int c = tid + 256 * k;
+      uint16_t* dst;
+      if (c < 768) {
+        const int rho = c / 24, cc = c % 24;
+        dst = st + rho * KP_LD + cc * 8;
+      } else if (c < 1280) {
+        const int c2_ = c - 768, rho = c2_ / 16, cc = c2_ % 16;
+        dst = st + 32 * KP_LD + rho * VP_LD + cc * 8;
+      } else {
+        const int c2_ = c - 1280, d = c2_ >> 2, k8 = (c2_ & 3) * 8;
+        dst = st + 32 * KP_LD + 32 * VP_LD + d * KT_LD + k8;
+      }
+      *reinterpret_cast<u32x4_t*>(dst) = stg[k];
+    }
+  };
+
+  if (nkt > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int s = kt & 1;
+    if (kt + 1 < nkt) load_tile(kt + 1);
+    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem_dq) + s * DQ_STAGE_H;
+    const uint16_t* Kp = st;
+    const uint16_t* Vp = st + 32 * KP_LD;
+    const uint16_t* KT = Vp + 32 * VP_LD;
+    // S^T = Kp Q^T, dP^T = Vp dO^T  (rows: permuted keys, columns: queries)
+    f32x16_t sacc = {}, pacc = {};
+#pragma unroll
+    for (int ks = 0; ks < DQK / 16; ++ks)
+      sacc = mfma(*reinterpret_cast<const f16x8_t*>(Kp + l32 * KP_LD + 16 * ks + 8 * hb), qb_[ks], sacc);
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks)
+      pacc = mfma(*reinterpret_cast<const f16x8_t*>(Vp + l32 * VP_LD + 16 * ks + 8 * hb), ob_[ks], pacc);
+    f16x8_t sb[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
+      const int j = kt * 32 + perm32(rho);
+      const bool vis = j < f.s_vis && i < f.Sq && lse != -INFINITY && (!f.causal || f.kv_pos0 + j <= f.q_pos0 + i);
+      const float p = vis ? fast_exp2(sacc[e] * c2 - lse * MLA_LOG2E) : 0.f;
+      sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - dd));
+    }
+    // dQ^T += K^T dS^T  (k-slots: keys 16u + 8hb .. in natural order)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < DQK / 32; ++db)
+        dqt[db] = mfma(*reinterpret_cast<const f16x8_t*>(KT + (db * 32 + l32) * KT_LD + 16 * u + 8 * hb), sb[u],
+                       dqt[db]);
+    __syncthreads();
+    if (kt + 1 < nkt) store_tile(s ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dq_nope, and dq_pe rotated back by the negative angle ----
+  if (i < f.Sq) {
+    const int64_t row = ((int64_t)b * f.Sq + i) * f.H + h;
+#pragma unroll
+    for (int db = 0; db < DN / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hb;
+        *reinterpret_cast<f32x4_t*>(a.dq_nope + row * DN + d) =
+            f32x4_t{f.scale * dqt[db][4 * g], f.scale * dqt[db][4 * g + 1], f.scale * dqt[db][4 * g + 2],
+                    f.scale * dqt[db][4 * g + 3]};
+      }
+    // rope rows 128 + m (block 4) and 128 + m + 32 (block 5) sit in the same lane and element
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 8 * g + 4 * hb + r;
+        const float lo = f.scale * dqt[4][4 * g + r], hi = f.scale * dqt[5][4 * g + r];
+        const float2 cs = qtab[(int64_t)i * 32 + m];
+        a.dq_pe[row * DR + m] = lo * cs.x + hi * cs.y;
+        a.dq_pe[row * DR + m + 32] = hi * cs.x - lo * cs.y;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dk_pe --
+// dk_pe[b, j, (m, m+32)] = R^T(sum_h dkr[b, h, j, :]); zero for j >= s_vis
+__global__ void dk_pe_kernel(BackwardArgs a, const float* __restrict__ dkr, const float2* __restrict__ ktab) {
+  const ExplicitArgs& f = a.f;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)f.B * f.Skv * 32) return;
+  const int m = (int)(idx & 31);
+  const int64_t bj = idx >> 5;
+  const int j = (int)(bj % f.Skv), b = (int)(bj / f.Skv);
+  float lo = 0.f, hi = 0.f;
+  if (j < f.s_vis) {
+    for (int h = 0; h < f.H; ++h) {
+      const float* g = dkr + (((int64_t)b * f.H + h) * f.s_pad + j) * DR;
+      lo += g[m];
+      hi += g[m + 32];
+    }
+    const float2 cs = ktab[(int64_t)j * 32 + m];
+    const float l2 = lo * cs.x + hi * cs.y, h2 = hi * cs.x - lo * cs.y;
+    lo = l2;
+    hi = h2;
+  }
+  a.dk_pe[bj * DR + m] = lo;
+  a.dk_pe[bj * DR + m + 32] = hi;
+}
+
+// ---------------------------------------------------------------- gemm_nt --
+// C[m][n] = sum_k A[m][k] B[n][k] for m < M_store (rows m in [M_store, M) are
+// computed but not stored), n < N; A [M][K], B [N][K] fp16 row-major (lda = ldb
+// = K), C fp32 with row stride ldc.  M, N multiples of the tile; K a multiple
+// of 32.  Tile BM x 128, 4 waves of (BM/2) x 64, 32x32x16 MFMAs, K step 32,
+// LDS double buffer with rows padded to 40 elements.
+template <int BM>
+__global__ void __launch_bounds__(256)
+gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ C, int M,
+               int M_store, int N, int K, int64_t ldc, int64_t c_row_map_div, int64_t c_row_map_stride) {
+  constexpr int BN = 128, BK = 32, LD = 40;
+  constexpr int WM = BM / 2, WN = 64;               // per-wave tile
+  constexpr int FM = WM / 32, FN = WN / 32;         // 32x32 blocks per wave
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LD];
+  const int n_tn = N / BN;
+  const int tm = blockIdx.x / n_tn, tn = blockIdx.x % n_tn;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hb = lane >> 5;
+  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+  constexpr int A_PER = BM * BK / 8 / 256, B_PER = BN * BK / 8 / 256;   // 16-byte pieces per thread
+  u32x4_t ra[A_PER], rb[B_PER];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < A_PER; ++p) {
+      const int c = tid + 256 * p, r = c >> 2, q = (c & 3) * 8;
+      ra[p] = *reinterpret_cast<const u32x4_t*>(A + (int64_t)(m0 + r) * K + k0 + q);
+    }
+#pragma unroll
+    for (int p = 0; p < B_PER; ++p) {
+      const int c = tid + 256 * p, r = c >> 2, q = (c & 3) * 8;
+      rb[p] = *reinterpret_cast<const u32x4_t*>(B + (int64_t)(n0 + r) * K + k0 + q);
+    }
+  };
+  auto store = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < A_PER; ++p) {
+      const int c = tid + 256 * p, r = c >> 2, q = (c & 3) * 8;
+      *reinterpret_cast<u32x4_t*>(&As[s][r * LD + q]) = ra[p];
+    }
+#pragma unroll
+    for (int p = 0; p < B_PER; ++p) {
+      const int c = tid + 256 * p, r = c >> 2, q = (c & 3) * 8;
+      *reinterpret_cast<u32x4_t*>(&Bs[s][r * LD + q]) = rb[p];
+    }
+  };
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int x = 0; x < FM; ++x)
+#pragma unroll
+    for (int y = 0; y < FN; ++y) acc[x][y] = f32x16_t{};
+  const int nk = K / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kk = 0; kk < nk; ++kk) {
+    const int s = kk & 1;
+    if (kk + 1 < nk) load((kk + 1) * BK);
+#pragma unroll
+    for (int u = 0; u < BK / 16; ++u) {
+      f16x8_t af[FM], bf[FN];
+#pragma unroll
+      for (int x = 0; x < FM; ++x)
+        af[x] = *reinterpret_cast<const f16x8_t*>(&As[s][(wm + 32 * x + l32) * LD + 16 * u + 8 * hb]);
+#pragma unroll
+      for (int y = 0; y < FN; ++y)
+        bf[y] = *reinterpret_cast<const f16x8_t*>(&Bs[s][(wn + 32 * y + l32) * LD + 16 * u + 8 * hb]);
+#pragma unroll
+      for (int x = 0; x < FM; ++x)
+#pragma unroll
+        for (int y = 0; y < FN; ++y) acc[x][y] = mfma(af[x], bf[y], acc[x][y]);
+    }
+    __syncthreads();
+    if (kk + 1 < nk) store(s ^ 1);
+    __syncthreads();
+  }
+  // D element e of block (x, y): row wm + 32x + 8(e/4) + 4hb + e%4, column wn + 32y + l32.
+  // Row m of C sits at (m / div) * stride + m % div (a batch of row blocks
+  // stored with their own stride), so padded rows of each batch are skipped.
+#pragma unroll
+  for (int x = 0; x < FM; ++x)
+#pragma unroll
+    for (int y = 0; y < FN; ++y)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm + 32 * x + 8 * (e >> 2) + 4 * hb + (e & 3);
+        const int n = n0 + wn + 32 * y + l32;
+        const int64_t mb = m / c_row_map_div, mr = m % c_row_map_div;
+        if (mr < M_store) C[(mb * c_row_map_stride + mr) * ldc + n] = acc[x][y][e];
+      }
+}
+
+}  // namespace
+
+size_t mfma_backward_workspace(const ExplicitArgs& f, MfmaBwdWorkspace* w, char* base) {
+  const size_t B = f.B, H = f.H, sq_pad = (size_t)(f.Sq + 127) / 128 * 128, sp = f.s_pad;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    const size_t o = off;
+    off = (off + bytes + 255) / 256 * 256;
+    return base == nullptr ? nullptr : base + o;
+  };
+  char* p;
+  p = take(8 * (size_t)f.Sq * 32);             if (w) w->qtab = reinterpret_cast<float2*>(p);
+  p = take(8 * sp * 32);                       if (w) w->ktab = reinterpret_cast<float2*>(p);
+  p = take(2 * B * H * sp * DN);               if (w) w->kn = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * B * H * DV * sp);               if (w) w->vt = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * B * sp * DR);                   if (w) w->krot = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * B * H * sq_pad * DQK);          if (w) w->qf = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * B * H * DQK * sq_pad);          if (w) w->qft = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * B * H * sq_pad * DV);           if (w) w->dof = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * B * H * DV * sq_pad);           if (w) w->doft = reinterpret_cast<uint16_t*>(p);
+  p = take(4 * B * H * sq_pad);                if (w) w->dvec = reinterpret_cast<float*>(p);
+  p = take(2 * B * H * sp * DV);               if (w) w->vrow = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * B * H * DN * sp);               if (w) w->knt = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * B * DR * sp);                   if (w) w->krt = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * B * sp * H * HD);               if (w) w->dkv = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * H * HD * B * sp);               if (w) w->dkvt = reinterpret_cast<uint16_t*>(p);
+  p = take(4 * B * H * sp * DR);               if (w) w->dkr = reinterpret_cast<float*>(p);
+  p = take(2 * (size_t)DKV * H * HD);          if (w) w->wt = reinterpret_cast<uint16_t*>(p);
+  p = take(2 * (size_t)DKV * B * sp);          if (w) w->ct = reinterpret_cast<uint16_t*>(p);
+  if (w) w->sq_pad = (int)sq_pad;
+  return off;
+}
+
+namespace {
+// out[z][c][r] = in[z][r][c] over rows x cols (rows >= rows_valid read as 0)
+template <bool IN_BF16>
+hipError_t transpose(const uint16_t* in, uint16_t* out, int rows, int rows_valid, int cols, int64_t in_ld,
+                     int64_t in_bs, int64_t out_ld, int64_t out_bs, int nbatch, hipStream_t s) {
+  if (rows == 0 || cols == 0 || nbatch == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_kernel<IN_BF16>, dim3((cols + 31) / 32, (rows + 31) / 32, nbatch), dim3(256), 0, s,
+                     in, out, rows, rows_valid, cols, in_ld, in_bs, out_ld, out_bs);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, int64_t rows, int64_t row_len, int64_t skip_rows,
+                                 int64_t batch_rows) {
+  // zero rows [skip_rows, batch_rows) of each batch of batch_rows rows
+  const int64_t per = (batch_rows - skip_rows) * row_len;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * per) return;
+  const int64_t z = idx / per, r = idx % per;
+  p[z * batch_rows * row_len + skip_rows * row_len + r] = 0.f;
+}
+}  // namespace
+
+hipError_t launch_bwd_prep(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t s) {
+  const ExplicitArgs& f = a.f;
+  const int sp = f.s_pad, B = f.B, H = f.H;
+  hipError_t e;
+  if (w.sq_pad > 0) {
+    if (f.out_dt == MLA_BF16)
+      hipLaunchKernelGGL(prep_q_kernel<MLA_BF16>, dim3(w.sq_pad / 32, H, B), dim3(256), 0, s, a, w.qtab, w.qf, w.qft,
+                         w.dof, w.doft, w.dvec, w.sq_pad);
+    else
+      hipLaunchKernelGGL(prep_q_kernel<MLA_FP32>, dim3(w.sq_pad / 32, H, B), dim3(256), 0, s, a, w.qtab, w.qf, w.qft,
+                         w.dof, w.doft, w.dvec, w.sq_pad);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // V rows: vt[bh][d][key] -> vrow[bh][key][d]
+  if ((e = transpose<false>(w.vt, w.vrow, DV, DV, sp, sp, (int64_t)DV * sp, DV, (int64_t)sp * DV, B * H, s)) != hipSuccess)
+    return e;
+  // K_nope columns: kn[bh][key][d] -> knt[bh][d][key]
+  if ((e = transpose<false>(w.kn, w.knt, sp, sp, DN, DN, (int64_t)sp * DN, sp, (int64_t)DN * sp, B * H, s)) != hipSuccess)
+    return e;
+  // rotated key band: krot[b][key][d] -> krt[b][d][key]
+  if ((e = transpose<false>(w.krot, w.krt, sp, sp, DR, DR, (int64_t)sp * DR, sp, (int64_t)DR * sp, B, s)) != hipSuccess)
+    return e;
+  // W^T [512][H*256] (fp16)
+  if ((e = transpose<true>(static_cast<const uint16_t*>(f.w), w.wt, H * HD, H * HD, DKV, DKV, 0, (int64_t)H * HD, 0, 1,
+                           s)) != hipSuccess)
+    return e;
+  // c_kv^T [512][B*sp] (fp16), rows past the visible keys zero
+  return transpose<true>(static_cast<const uint16_t*>(f.c_kv), w.ct, sp, f.s_vis, DKV, DKV, (int64_t)f.Skv * DKV,
+                         (int64_t)B * sp, sp, B, s);
+}
+
+hipError_t launch_bwd_kv(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t s) {
+  const ExplicitArgs& f = a.f;
+  if (f.s_pad == 0) return hipSuccess;
+  const int n_kb = f.s_pad / 128;
+  hipLaunchKernelGGL(kv_kernel, dim3(f.B * f.H * n_kb), dim3(256), 0, s, a, w.qf, w.qft, w.dof, w.doft, w.dvec, w.kn,
+                     w.vt, w.krot, w.dkv, w.dkvt, w.dkr, w.sq_pad, n_kb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t s) {
+  const ExplicitArgs& f = a.f;
+  if (f.Sq == 0) return hipSuccess;
+  const int n_qb = w.sq_pad / 128;
+  hipLaunchKernelGGL(dq_kernel, dim3(f.B * f.H * n_qb), dim3(256), 0, s, a, w.qf, w.dof, w.dvec, w.kn, w.krot, w.vrow,
+                     w.knt, w.krt, w.qtab, w.sq_pad, n_qb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkpe(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t s) {
+  const ExplicitArgs& f = a.f;
+  const int64_t n = (int64_t)f.B * f.Skv * 32;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(dk_pe_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, w.dkr, w.ktab);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_gemms(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t s) {
+  const ExplicitArgs& f = a.f;
+  const int B = f.B, H = f.H, sp = f.s_pad;
+  hipError_t e;
+  // dc_kv rows of each batch entry past the computed ones (keys no query sees)
+  if (f.Skv > sp) {
+    const int64_t n = (int64_t)B * (f.Skv - sp) * DKV;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.dc_kv, (int64_t)B,
+                       (int64_t)DKV, (int64_t)sp, (int64_t)f.Skv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (sp > 0) {
+    // dc_kv[b][j][c] = sum_k dKV[b sp + j][k] W^T[c][k]   (rows j < min(sp, Skv) of each entry)
+    const int M = B * sp;
+    hipLaunchKernelGGL(gemm_nt_kernel<64>, dim3((M / 64) * (DKV / 128)), dim3(256), 0, s, w.dkv, w.wt, a.dc_kv, M,
+                       min(sp, f.Skv), DKV, H * HD, (int64_t)DKV, (int64_t)sp, (int64_t)f.Skv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // dW[r][c] = sum_{b, j} dKV^T[r][b sp + j] c^T[c][b sp + j]
+    const int Mw = H * HD;
+    hipLaunchKernelGGL(gemm_nt_kernel<128>, dim3((Mw / 128) * (DKV / 128)), dim3(256), 0, s, w.dkvt, w.ct, a.dw, Mw, Mw,
+                       DKV, B * sp, (int64_t)DKV, (int64_t)Mw, (int64_t)Mw);
+    return hipGetLastError();
+  }
+  // no visible key: every weight gradient is zero
+  const int64_t n = (int64_t)H * HD * DKV;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.dw, (int64_t)1, n,
+                     (int64_t)0, (int64_t)1);
+  return hipGetLastError();
+}

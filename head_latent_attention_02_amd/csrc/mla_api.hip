@@ -282,10 +282,39 @@ struct BackwardPlan {
 // bounded here so that a call cannot ask for an absurd allocation.
 constexpr size_t kMaxSimtBwdPairs = size_t(1) << 31;
 
+ExplicitArgs explicit_args(const mla_explicit_desc* desc, const ExplicitPlan& p) {
+  ExplicitArgs f{};
+  f.B = desc->batch; f.Sq = desc->s_q; f.Skv = desc->s_kv; f.H = desc->n_heads;
+  f.dkv = desc->d_kv; f.dn = desc->d_nope; f.dr = desc->d_rope; f.dv = desc->d_v;
+  f.q_pos0 = desc->q_pos0; f.kv_pos0 = desc->kv_pos0; f.causal = desc->causal;
+  f.scale = desc->softmax_scale; f.rope_base = desc->rope_base;
+  f.in_dt = desc->in_dtype; f.out_dt = desc->out_dtype;
+  f.s_vis = p.s_vis; f.s_pad = p.s_pad;
+  return f;
+}
+
 mla_status make_backward_plan(const mla_explicit_desc* d, BackwardPlan* plan) {
   BackwardPlan p;
   mla_explicit_desc fd = *d;
-  if (fd.algo == MLA_ALGO_MFMA) return MLA_ERR_UNSUPPORTED;
+  // the MFMA backward takes the forward's MFMA shapes, with its GEMM
+  // dimensions (B * s_pad keys, H * 256 weight rows) within 32-bit ints
+  mla_explicit_desc md = *d;
+  md.algo = MLA_ALGO_MFMA;
+  ExplicitPlan mp;
+  const bool mfma_ok = d->algo != MLA_ALGO_SIMT && make_explicit_plan(&md, &mp) == MLA_OK && mp.mfma &&
+                       (int64_t)d->batch * mp.s_pad < ((int64_t)1 << 30) &&
+                       (int64_t)d->batch * ((d->s_q + 127) / 128 * 128) < ((int64_t)1 << 30);
+  if (d->algo == MLA_ALGO_MFMA && !mfma_ok) {
+    if (!explicit_shape_ok(d)) return MLA_ERR_INVALID_ARGUMENT;
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if (mfma_ok) {
+    p.fwd = mp;
+    p.mfma = true;
+    p.total = mfma_backward_workspace(explicit_args(d, mp), nullptr, nullptr);
+    *plan = p;
+    return MLA_OK;
+  }
   fd.algo = MLA_ALGO_SIMT;
   mla_status st = make_explicit_plan(&fd, &p.fwd);
   if (st != MLA_OK) return st;
@@ -570,17 +599,62 @@ mla_status mla_bwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   BackwardArgs a;
+  a.f = explicit_args(desc, p.fwd);
   ExplicitArgs& f = a.f;
-  f.B = desc->batch; f.Sq = desc->s_q; f.Skv = desc->s_kv; f.H = desc->n_heads;
-  f.dkv = desc->d_kv; f.dn = desc->d_nope; f.dr = desc->d_rope; f.dv = desc->d_v;
-  f.q_pos0 = desc->q_pos0; f.kv_pos0 = desc->kv_pos0; f.causal = desc->causal;
-  f.scale = desc->softmax_scale; f.rope_base = desc->rope_base;
-  f.in_dt = desc->in_dtype; f.out_dt = desc->out_dtype;
-  f.s_vis = p.fwd.s_vis; f.s_pad = p.fwd.s_pad;
   f.q_nope = q_nope; f.q_pe = q_pe; f.c_kv = c_kv; f.k_pe = k_pe; f.w = w_kv_b;
   f.out = nullptr; f.lse = nullptr;
   a.out = out; a.lse = lse; a.d_out = d_out;
   a.dq_nope = dq_nope; a.dq_pe = dq_pe; a.dc_kv = dc_kv; a.dk_pe = dk_pe; a.dw = dw_kv_b;
+  hipError_t e;
+  if (p.mfma) {
+    const void* ptrs[] = {q_nope, q_pe, c_kv, k_pe, w_kv_b, out, d_out, dq_nope, dq_pe, dc_kv, dk_pe, dw_kv_b, workspace};
+    for (const void* q : ptrs)
+      if (q != nullptr && !aligned16(q)) return MLA_ERR_INVALID_ARGUMENT;
+    MfmaBwdWorkspace w;
+    mfma_backward_workspace(f, &w, ws);
+    {
+      TimedLaunch t("rope_tables", s);
+      e = launch_rope_table(w.qtab, f.q_pos0, f.Sq, f.dr, f.rope_base, s);
+      if (e == hipSuccess) e = launch_rope_table(w.ktab, f.kv_pos0, f.s_vis, f.dr, f.rope_base, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "rope tables");
+    {
+      TimedLaunch t("mfma_up_projection", s);
+      e = launch_mfma_upproj(f, w.kn, w.vt, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mfma up-projection");
+    {
+      TimedLaunch t("key_rope_band", s);
+      e = launch_krot_f16(f, w.ktab, w.krot, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "key rope band");
+    {
+      TimedLaunch t("bwd_prep", s);
+      e = launch_bwd_prep(a, w, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "backward operand layouts");
+    {
+      TimedLaunch t("bwd_kv", s);
+      e = launch_bwd_kv(a, w, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "backward key/value gradients");
+    {
+      TimedLaunch t("bwd_dq", s);
+      e = launch_bwd_dq(a, w, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "backward query gradients");
+    {
+      TimedLaunch t("bwd_dk_pe", s);
+      e = launch_bwd_dkpe(a, w, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "backward key band gradient");
+    {
+      TimedLaunch t("bwd_gemms", s);
+      e = launch_bwd_gemms(a, w, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "backward latent and weight gradients");
+    return MLA_OK;
+  }
   SimtBwdWorkspace w;
   w.qtab = reinterpret_cast<float2*>(ws + p.off_qtab);
   w.ktab = reinterpret_cast<float2*>(ws + p.off_ktab);
@@ -592,7 +666,6 @@ mla_status mla_bwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
   w.ds = reinterpret_cast<float*>(ws + p.off_ds);
   w.dkn = reinterpret_cast<float*>(ws + p.off_dkn);
   w.dv = reinterpret_cast<float*>(ws + p.off_dv);
-  hipError_t e;
   {
     TimedLaunch t("rope_tables", s);
     e = launch_rope_table(const_cast<float2*>(w.qtab), f.q_pos0, f.Sq, f.dr, f.rope_base, s);

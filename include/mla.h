@@ -293,10 +293,15 @@ mla_status mla_fwd_absorbed(const mla_explicit_desc* desc,
  *   dq_nope [B, s_q, H, d_nope], dq_pe [B, s_q, H, d_rope], dc_kv [B, s_kv, d_kv],
  *   dk_pe [B, s_kv, d_rope], dw_kv_b [H*(d_nope+d_v), d_kv]: fp32 outputs,
  *   fully written (latent rows no query sees get zero gradients).
- * Workspace: mla_bwd_explicit_workspace_size() bytes.  The SIMT kernels
- * (any head geometry, fp32 arithmetic) keep the probabilities and their
- * gradients for every visible pair: at most 2^31 pairs per call
- * (B * H * s_q * visible keys), else MLA_ERR_UNSUPPORTED. */
+ * Workspace: mla_bwd_explicit_workspace_size() bytes, 16-byte aligned.
+ * MLA_ALGO_MFMA (the default where eligible) takes the forward's MFMA shapes
+ * (bf16 inputs, d_kv 512, d_nope 128, d_rope 64, d_v 128) with batch * padded
+ * key and query rows below 2^30; it runs the products on fp16 MFMA with fp32
+ * accumulation and keeps fp16 copies of Q, d_out, K, V and of [dK_nope | dV]
+ * in the workspace (all pointers 16-byte aligned).  The SIMT kernels (any
+ * head geometry, fp32 arithmetic) keep the probabilities and their gradients
+ * for every visible pair: at most 2^31 pairs per call (B * H * s_q * visible
+ * keys), else MLA_ERR_UNSUPPORTED. */
 size_t mla_bwd_explicit_workspace_size(const mla_explicit_desc* desc);
 
 mla_status mla_bwd_explicit(const mla_explicit_desc* desc,

@@ -109,6 +109,34 @@ def test_backward_simt(mla, cfg):
         _compare(got[k], g[k], f"{cfg.name} {k}", 1e-4 if cfg.dtype == "bf16" else 1e-5)
 
 
+MFMA_CASES = [
+    I.small_explicit("mbwd_ragged", batch=2, s_q=300, s_kv=300, n_heads=3, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     dtype="bf16", seed=931),
+    I.small_explicit("mbwd_offset_q", s_q=100, s_kv=612, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=512, dtype="bf16", seed=932),
+    I.small_explicit("mbwd_masked_rows", s_q=96, s_kv=96, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     kv_pos0=40, dtype="bf16", seed=933),
+    I.small_explicit("mbwd_noncausal", s_q=77, s_kv=131, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     causal=False, dtype="bf16", seed=934),
+    # a sequence-parallel rank's rows: keys past the last visible one (and past
+    # the padded tile) get zero gradients
+    I.small_explicit("mbwd_sp_share", s_q=64, s_kv=1024, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=192, dtype="bf16", seed=935),
+    I.small_explicit("mbwd_one_key", s_q=1, s_kv=1, n_heads=2, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     dtype="bf16", seed=936),
+    I.small_explicit("mbwd_multi_tile", s_q=700, s_kv=700, n_heads=1, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     dtype="bf16", seed=937),
+]
+
+
+@pytest.mark.parametrize("cfg", MFMA_CASES, ids=lambda c: c.name)
+def test_backward_mfma(mla, cfg):
+    x, do, out, lse, g = _case(cfg, cfg.seed)
+    got = _run(mla, cfg, x, out, lse, do, mla.MLA_ALGO_MFMA)
+    for k in GRADS:
+        _compare(got[k], g[k], f"{cfg.name} {k}", 1e-2, 5e-3)
+
+
 def test_backward_after_gpu_forward(mla):
     """The GPU forward's own output and LSE into the GPU backward: the
     forward's rounding (bf16 inputs, fp16 attention operands) enters the
