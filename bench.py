@@ -214,6 +214,65 @@ def explicit_case(mla, torch, cfg, args):
             "timing": "hip_graph_replay", "kernels": kernels}
 
 
+def backward_case(mla, torch, cfg, args):
+    """The explicit-form backward at the explicit workload: time per call
+    (HIP events, eager, after one untimed call) and per-kernel averages.
+    Algorithmic FLOPs: the up-projection recomputed for K and V, the five
+    attention products per visible pair and head (S = Q K^T 192, dP = dO V^T
+    128, dV = P^T dO 128, dK = dS^T Q 192, dQ = dS K 192), and the two
+    latent-space GEMMs dc_kv = dKV W and dW = dKV^T c_kv."""
+    log(f"backward of {cfg.name}: inputs, forward, {args.steps} timed calls")
+    x = I_mod().make_explicit_inputs(cfg)
+    t = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    del x
+    kw = dict(q_pos0=cfg.q_pos0, kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale)
+    out, lse, _ = mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], **kw)
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed)
+    d_out = torch.randn(out.shape, device="cuda", generator=g)
+    grads, ws = mla.mla_bwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], out, lse, d_out, **kw)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ms = []
+    for _ in range(args.steps):
+        ev[0].record()
+        mla.mla_bwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], out, lse, d_out, grads=grads,
+                             workspace=ws, **kw)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms.append(ev[0].elapsed_time(ev[1]))
+    mla.mla_timing_reset()
+    mla.mla_timing_begin()
+    for _ in range(args.steps):
+        mla.mla_bwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], out, lse, d_out, grads=grads,
+                             workspace=ws, **kw)
+    torch.cuda.synchronize()
+    mla.mla_timing_end()
+    kt = mla.mla_timing_get()
+    mla.mla_timing_reset()
+    pairs, vk, H = cfg.visible_pairs() * cfg.batch, cfg.visible_keys() * cfg.batch, cfg.n_heads
+    gemm = 2 * vk * H * (cfg.d_nope + cfg.d_v) * cfg.d_kv
+    attn = 2 * H * pairs * (3 * (cfg.d_nope + cfg.d_rope) + 2 * cfg.d_v)
+    work = {"mfma_up_projection": gemm, "bwd_kv": 2 * H * pairs * (2 * (cfg.d_nope + cfg.d_rope) + 2 * cfg.d_v),
+            "bwd_dq": 2 * H * pairs * (cfg.d_nope + cfg.d_rope), "bwd_gemms": 2 * gemm}
+    kernels = {}
+    for name, (tot, n) in kt.items():
+        ent = {"avg_ms": tot / max(n, 1), "launches_per_call": n / args.steps}
+        if name in work:
+            ach = work[name] / (ent["avg_ms"] * 1e-3) / 1e12
+            ent.update({"algorithmic_flop": work[name], "achieved": ach, "unit": "TFLOP/s",
+                        "frac": ach / PEAK_MFMA_TFLOPS})
+        kernels[name] = ent
+    total = gemm + attn + 2 * gemm
+    avg = float(np.mean(ms))
+    del t, out, lse, d_out, grads, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{cfg.name} explicit-form backward (B={cfg.batch}, S={cfg.s_q}, n_h={cfg.n_heads}, causal)",
+            "ms": avg, "algorithmic_flop": total, "tflops": total / (avg * 1e-3) / 1e12,
+            "frac_mfma_peak": total / (avg * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, "timing": "eager, HIP events",
+            "kernels": kernels,
+            "note": "bwd_kv recomputes S and dP, bwd_dq recomputes them again; counted once in algorithmic_flop"}
+
+
 def I_mod():
     from head_latent_attention_02_amd import inputs as I
     return I
@@ -326,6 +385,7 @@ def parse():
                    help="skip the timing of the V2-Lite and SP=8-rank explicit configurations")
     p.add_argument("--no-forms", action="store_true",
                    help="skip the explicit-vs-absorbed memory and time comparison at 4K/8K/16K tokens")
+    p.add_argument("--no-backward", action="store_true", help="skip the explicit-form backward")
     p.add_argument("--form-calls", type=int, default=3,
                    help="timed calls per form and length in the explicit-vs-absorbed comparison")
     p.add_argument("--copy-calibration", action="store_true",
@@ -631,6 +691,9 @@ def main():
     if not args.no_configs:
         res["configs"] = {name: explicit_case(mla, torch, I.EXPLICIT_CONFIGS[name], args)
                           for name in ("v3_sp8_rank3", "v2lite_bf16")}
+
+    if not args.no_backward:
+        res["backward"] = backward_case(mla, torch, ecfg, args)
 
     if not args.no_cpu_baseline:
         log("oracle CPU baseline on a bounded sample")

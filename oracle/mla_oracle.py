@@ -325,7 +325,8 @@ def _softmax_bwd(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
 
 
 def explicit_bwd(q_nope, q_pe, c_kv, k_pe, w_kv_b, d_out, *, q_pos0=0, kv_pos0=0, causal=True,
-                 softmax_scale: Optional[float] = None, rope_base=10000.0):
+                 softmax_scale: Optional[float] = None, rope_base=10000.0,
+                 heads: Optional[Sequence[int]] = None):
     """Gradients of sum(d_out * O) through explicit_fwd, with respect to every
     input.  [LAGA] is about training: its "If this is right" section states
     that LAGA's parameter gradients equal the explicit form's, and the Fig. 5
@@ -346,6 +347,9 @@ def explicit_bwd(q_nope, q_pe, c_kv, k_pe, w_kv_b, d_out, *, q_pos0=0, kv_pos0=0
                                       dk_pe = R(sum_h dk_r, -p')
     Returns a dict with dq_nope [B,S_q,H,d_n], dq_pe [B,S_q,H,d_r],
     dc_kv [B,S_kv,d_c], dk_pe [B,S_kv,d_r] and dw_kv_b [H*(d_n+d_v), d_c].
+    With ``heads`` only those heads are differentiated: their dq and W_kv_b
+    rows are exact, other heads' entries are zero, and dc_kv / dk_pe hold
+    only the selected heads' terms of their sums over heads.
     """
     q_nope = np.asarray(q_nope, dtype=np.float64)
     q_pe = np.asarray(q_pe, dtype=np.float64)
@@ -367,10 +371,11 @@ def explicit_bwd(q_nope, q_pe, c_kv, k_pe, w_kv_b, d_out, *, q_pos0=0, kv_pos0=0
          "dk_pe": np.zeros_like(k_pe)}
     dw_uk = np.zeros_like(w_uk)
     dw_uv = np.zeros_like(w_uv)
+    heads = list(range(H)) if heads is None else list(heads)
     for b in range(B):
         k_rot = rope_rotate(k_pe[b], kpos, rope_base)
         dk_rot = np.zeros_like(k_rot)
-        for h in range(H):
+        for h in heads:
             k_n = c_kv[b] @ w_uk[h].T
             v = c_kv[b] @ w_uv[h].T
             q_rot = rope_rotate(q_pe[b, :, h], qpos, rope_base)

@@ -152,3 +152,64 @@ def test_backward_after_gpu_forward(mla):
     g = O.explicit_bwd(**x, d_out=do.astype(np.float64), **_args(cfg))
     for k in GRADS:
         _compare(grads[k].cpu().numpy(), g[k], f"chained {k}", 1e-2, 5e-3)
+
+
+def _oracle_bwd_pooled(x, do, cfg, heads):
+    """explicit_bwd over `heads`, one head per task on a thread pool (BLAS
+    single-threaded inside), the per-head results summed: the head-subset
+    results partition the full gradient (pinned in the oracle tests)."""
+    import concurrent.futures as cf
+    import os
+
+    from threadpoolctl import threadpool_limits
+    workers = max(1, min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
+    d64 = do.astype(np.float64)
+    with threadpool_limits(limits=1, user_api="blas"), cf.ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(lambda h: O.explicit_bwd(**x, d_out=d64, **_args(cfg), heads=[h]), heads))
+    out = {k: sum(p[k] for p in parts) for k in GRADS}
+    return out
+
+
+def test_backward_v3_heads_full_compare(mla):
+    """All 128 heads at 1024 tokens (several key and query tiles per head),
+    every gradient compared whole."""
+    cfg = I.small_explicit("mbwd_h128", s_q=1024, s_kv=1024, n_heads=128, d_kv=512, d_nope=128, d_rope=64,
+                           d_v=128, dtype="bf16", seed=941)
+    x = I.make_explicit_inputs(cfg)
+    do = np.random.default_rng(942).standard_normal((1, 1024, 128, 128)).astype(np.float32)
+    ro, rl = O.explicit_fwd(**x, **_args(cfg))
+    got = _run(mla, cfg, x, ro.astype(np.float32), rl.astype(np.float32), do, mla.MLA_ALGO_MFMA)
+    g = _oracle_bwd_pooled(x, do, cfg, list(range(128)))
+    for k in GRADS:
+        _compare(got[k], g[k], f"h128 {k}", 1e-2, 5e-3)
+
+
+def test_backward_v3_full_size_sampled_heads(mla):
+    """The timed V3 shape (4096 tokens, 128 heads): the query gradients and the
+    W_kv_b rows of heads 0 and 127, whose oracle terms need only those heads;
+    the other gradients must be finite.  The forward output and LSE fed to the
+    backward are the oracle's on those heads and the GPU forward's elsewhere
+    (they enter only their own heads' terms)."""
+    cfg = I.EXPLICIT_CONFIGS["v3_bf16"]
+    x = I.make_explicit_inputs(cfg)
+    do = np.random.default_rng(943).standard_normal((1, 4096, 128, 128)).astype(np.float32)
+    heads = [0, 127]
+    t = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    out, lse, _ = mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], **_args(cfg))
+    ro, rl = O.explicit_fwd(**x, **_args(cfg), heads=heads)
+    out[:, :, heads] = torch.from_numpy(ro.astype(np.float32)).cuda()
+    lse[:, heads] = torch.from_numpy(rl.astype(np.float32)).cuda()
+    _say("backward v3_bf16 full size: B=1 Sq=4096 H=128")
+    grads, _ = mla.mla_bwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], out.contiguous(),
+                                    lse.contiguous(), torch.from_numpy(do).cuda(), **_args(cfg))
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in grads.items()}
+    for k in GRADS:
+        assert np.isfinite(got[k]).all(), k
+    g = _oracle_bwd_pooled(x, do, cfg, heads)
+    hd = cfg.d_nope + cfg.d_v
+    for h in heads:
+        _compare(got["dq_nope"][:, :, h], g["dq_nope"][:, :, h], f"v3 dq_nope head {h}", 1e-2, 5e-3)
+        _compare(got["dq_pe"][:, :, h], g["dq_pe"][:, :, h], f"v3 dq_pe head {h}", 1e-2, 5e-3)
+        _compare(got["dw_kv_b"][h * hd:(h + 1) * hd], g["dw_kv_b"][h * hd:(h + 1) * hd], f"v3 dW rows head {h}",
+                 1e-2, 5e-3)

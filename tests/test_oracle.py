@@ -469,3 +469,22 @@ def test_backward_pins_catch_planted_mistakes(monkeypatch, mutation):
               - _loss(dict(x, **{name: x[name] - 1e-5 * v}), do, cfg)) / 2e-5
         worst = max(worst, abs(fd - float(np.sum(g[gname] * v))))
     assert worst > 1e-4
+
+
+def test_backward_head_subsets_partition_the_full_gradient():
+    """dq and W_kv_b rows of a head subset are the full gradient's entries;
+    dc_kv and dk_pe of disjoint subsets add up to the full sums."""
+    cfg = BWD_CASES[1]
+    x = _f64(I.make_explicit_inputs(cfg))
+    do = np.random.default_rng(4).standard_normal((cfg.batch, cfg.s_q, cfg.n_heads, cfg.d_v))
+    full = O.explicit_bwd(**x, d_out=do, **_args(cfg))
+    parts = [O.explicit_bwd(**x, d_out=do, **_args(cfg), heads=hs) for hs in ([0, 2], [1])]
+    hd = cfg.d_nope + cfg.d_v
+    for hs, g in zip(([0, 2], [1]), parts):
+        for h in hs:
+            np.testing.assert_allclose(g["dq_nope"][:, :, h], full["dq_nope"][:, :, h], atol=1e-14)
+            np.testing.assert_allclose(g["dq_pe"][:, :, h], full["dq_pe"][:, :, h], atol=1e-14)
+            np.testing.assert_allclose(g["dw_kv_b"][h * hd:(h + 1) * hd], full["dw_kv_b"][h * hd:(h + 1) * hd],
+                                       atol=1e-14)
+    for k in ("dc_kv", "dk_pe"):
+        np.testing.assert_allclose(parts[0][k] + parts[1][k], full[k], atol=1e-13)
