@@ -508,3 +508,40 @@ def test_absorbed_v3_sampled(mla):
     _compare(o[:, rows][:, :, heads], ro, True, "absorbed v3 sampled out")
     _compare_lse(l[:, heads][:, :, rows], rl, True, "absorbed v3")
     assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+# Both forms at the long causal prefill lengths of the memory comparison
+# (B = 1, 128 heads, S = 8192 and 16384): rows sampled over the whole sequence,
+# heads covering every residue mod 8; the rest of each tensor must be finite.
+_LONG_INPUTS = {}
+
+
+def _long_inputs(name):
+    # one configuration held at a time: the 16K inputs are 1.7 GB as float32
+    if name not in _LONG_INPUTS:
+        _LONG_INPUTS.clear()
+        _say(f"generating inputs of {name}")
+        _LONG_INPUTS[name] = I.make_explicit_inputs(I.EXPLICIT_CONFIGS[name])
+    return _LONG_INPUTS[name]
+
+
+@pytest.mark.parametrize("form", ["explicit", "absorbed"])
+@pytest.mark.parametrize("name", ["v3_s8k_bf16", "v3_s16k_bf16"])
+def test_long_sequence_sampled(mla, name, form):
+    cfg = I.EXPLICIT_CONFIGS[name]
+    x = _long_inputs(name)
+    if form == "explicit":
+        o, l, _, _ = _run_explicit(mla, cfg, x)
+    else:
+        o, l = _run_absorbed(mla, cfg, x)
+    rng = np.random.default_rng(11)
+    heads = V3_SAMPLE_HEADS
+    rows = _sample_rows(cfg.s_q, rng, k=64)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    o_s, l_s = o[:, rows][:, :, heads], l[:, heads][:, :, rows]
+    del o, l
+    ro, rl = _oracle_explicit(cfg, x, heads=heads, rows=rows)
+    _compare(o_s, ro, True, f"{form} {name} sampled out")
+    _compare_lse(l_s, rl, True, f"{form} {name}")
+    if form == "absorbed":
+        _LONG_INPUTS.clear()
