@@ -75,6 +75,9 @@ hipError_t launch_krot_f16(const ExplicitArgs& a, const float2* ktab, uint16_t* 
                            hipStream_t stream);
 hipError_t launch_mfma_attention(const ExplicitArgs& a, const uint16_t* kn, const uint16_t* vt,
                                  const uint16_t* krot, const float2* qtab, hipStream_t stream);
+// Attention with the up-projection fused in: reads c_kv and w directly.
+hipError_t launch_fused_attention(const ExplicitArgs& a, const uint16_t* krot, const float2* qtab,
+                                  hipStream_t stream);
 
 // ---- explicit-form backward ----------------------------------------------
 // SIMT path.  Workspace (fp32): Kn [B,H,s_vis,dn], V [B,H,s_vis,dv], krot

@@ -22,7 +22,9 @@ constexpr int kUpTile = 256;        // latent-row tile of the MFMA up-projection
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_dtype(mla_dtype d) { return d == MLA_BF16 || d == MLA_FP32; }
-bool valid_algo(mla_algo a) { return a == MLA_ALGO_AUTO || a == MLA_ALGO_SIMT || a == MLA_ALGO_MFMA; }
+bool valid_algo(mla_algo a) {
+  return a == MLA_ALGO_AUTO || a == MLA_ALGO_SIMT || a == MLA_ALGO_MFMA || a == MLA_ALGO_FUSED;
+}
 
 mla_status hip_fail(hipError_t e, const char* where) {
   g_last_error = std::string(where) + ": " + hipGetErrorString(e);
@@ -83,6 +85,7 @@ class TimedLaunch {
 // ---------------------------------------------------------------- explicit --
 struct ExplicitPlan {
   bool mfma = false;
+  bool fused = false;     // MFMA attention with the up-projection fused in
   int s_vis = 0, s_pad = 0;
   size_t off_qtab = 0, off_ktab = 0, off_kn = 0, off_v = 0, off_krot = 0, total = 0;
 };
@@ -132,7 +135,7 @@ mla_status make_explicit_plan(const mla_explicit_desc* d, ExplicitPlan* plan) {
   // byte offsets: s_pad * 256 bytes must stay below 2^31
   const bool mfma_ok = explicit_mfma_eligible(d) && p.s_pad <= kMaxMfmaKeys;
   bool mfma;
-  if (d->algo == MLA_ALGO_MFMA) {
+  if (d->algo == MLA_ALGO_MFMA || d->algo == MLA_ALGO_FUSED) {
     if (!mfma_ok) return MLA_ERR_UNSUPPORTED;
     mfma = true;
   } else if (d->algo == MLA_ALGO_SIMT) {
@@ -141,12 +144,16 @@ mla_status make_explicit_plan(const mla_explicit_desc* d, ExplicitPlan* plan) {
     mfma = mfma_ok;
   }
   if (!mfma && !explicit_simt_supported(d)) return MLA_ERR_UNSUPPORTED;
-  p.mfma = mfma;
+  const bool fused = d->algo == MLA_ALGO_FUSED;
+  p.mfma = mfma && !fused;
+  p.fused = fused;
   const size_t B = d->batch, H = d->n_heads, half = d->d_rope / 2;
   size_t off = 0;
   p.off_qtab = off; off = align_up(off + sizeof(float2) * (size_t)d->s_q * half);
   p.off_ktab = off; off = align_up(off + sizeof(float2) * (size_t)p.s_vis * half);
-  if (mfma) {
+  if (fused) {
+    p.off_krot = off; off = align_up(off + 2 * B * (size_t)p.s_pad * 64);
+  } else if (mfma) {
     p.off_kn = off;   off = align_up(off + 2 * B * H * (size_t)p.s_pad * 128);
     p.off_v = off;    off = align_up(off + 2 * B * H * 128 * (size_t)p.s_pad);
     p.off_krot = off; off = align_up(off + 2 * B * (size_t)p.s_pad * 64);
@@ -192,7 +199,7 @@ bool decode_simt_supported(const mla_decode_desc* d) { return d->d_kv <= 1024 &&
 
 mla_status make_decode_plan(const mla_decode_desc* d, DecodePlan* plan) {
   if (!decode_shape_ok(d)) return MLA_ERR_INVALID_ARGUMENT;
-  if (d->n_splits > 64) return MLA_ERR_UNSUPPORTED;
+  if (d->n_splits > 64 || d->algo == MLA_ALGO_FUSED) return MLA_ERR_UNSUPPORTED;
   // the combine keeps 8 merged rows in LDS and reads rows 8 elements at a time
   if (d->d_kv > 1024 || d->d_kv % 8 != 0) return MLA_ERR_UNSUPPORTED;
   bool mfma;
@@ -294,6 +301,10 @@ ExplicitArgs explicit_args(const mla_explicit_desc* desc, const ExplicitPlan& p)
 }
 
 mla_status make_backward_plan(const mla_explicit_desc* d, BackwardPlan* plan) {
+  if (d != nullptr && d->algo == MLA_ALGO_FUSED) {
+    if (!explicit_shape_ok(d)) return MLA_ERR_INVALID_ARGUMENT;
+    return MLA_ERR_UNSUPPORTED;
+  }
   BackwardPlan p;
   mla_explicit_desc fd = *d;
   // the MFMA backward takes the forward's MFMA shapes, with its GEMM
@@ -447,7 +458,7 @@ mla_status mla_fwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
   if (has_kv && (c_kv == nullptr || k_pe == nullptr)) return MLA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < p.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (p.total > 0 && workspace == nullptr) return MLA_ERR_INVALID_ARGUMENT;
-  if (p.mfma) {
+  if (p.mfma || p.fused) {
     const void* ptrs[] = {q_nope, q_pe, c_kv, k_pe, w_kv_b, out, workspace};
     for (const void* q : ptrs)
       if (q != nullptr && !aligned16(q)) return MLA_ERR_INVALID_ARGUMENT;
@@ -475,7 +486,19 @@ mla_status mla_fwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
     if (e == hipSuccess) e = launch_rope_table(ktab, a.kv_pos0, a.s_vis, a.dr, a.rope_base, s);
   }
   if (e != hipSuccess) return hip_fail(e, "rope tables");
-  if (p.mfma) {
+  if (p.fused) {
+    uint16_t* kr = reinterpret_cast<uint16_t*>(ws + p.off_krot);
+    {
+      TimedLaunch t("key_rope_band", s);
+      e = launch_krot_f16(a, ktab, kr, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "key rope band");
+    {
+      TimedLaunch t("fused_attention", s);
+      e = launch_fused_attention(a, kr, qtab, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "fused attention");
+  } else if (p.mfma) {
     uint16_t* kn = reinterpret_cast<uint16_t*>(ws + p.off_kn);
     uint16_t* vt = reinterpret_cast<uint16_t*>(ws + p.off_v);
     uint16_t* kr = reinterpret_cast<uint16_t*>(ws + p.off_krot);

@@ -136,6 +136,10 @@ EXPLICIT_CONFIGS = {
         # time comparison (the LAGA page's 4K / 8K / 16K range)
         ExplicitConfig("v3_s8k_bf16", 1, 8192, 8192, 128, 512, 128, 64, 128, 0, 0, True, "bf16", 1006),
         ExplicitConfig("v3_s16k_bf16", 1, 16384, 16384, 128, 512, 128, 64, 128, 0, 0, True, "bf16", 1007),
+        # one rank's share after LAGA's all-to-all at S = 16384 over 8 ranks:
+        # H/8 = 16 heads over the whole causal sequence (the head-shard shape
+        # of the fused up-projection comparison)
+        ExplicitConfig("v3_headshard_sp8", 1, 16384, 16384, 16, 512, 128, 64, 128, 0, 0, True, "bf16", 1008),
     ]
 }
 

@@ -30,6 +30,7 @@ DECODE_NOALLOC_MAX_BYTES = 64 << 20
 MLA_ALGO_AUTO = 0
 MLA_ALGO_SIMT = 1
 MLA_ALGO_MFMA = 2
+MLA_ALGO_FUSED = 3     # explicit forward with the up-projection inside the attention kernel
 
 EXPORTED_SYMBOLS = (
     "mla_fwd_explicit_workspace_size", "mla_fwd_explicit", "mla_fwd_explicit_workspace_layout",
@@ -257,7 +258,7 @@ def _fwd(explicit: bool, q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.T
     name = "mla_fwd_explicit" if explicit else "mla_fwd_absorbed"
     ws_bytes = (mla_fwd_explicit_workspace_size if explicit else mla_fwd_absorbed_workspace_size)(desc)
     if ws_bytes == 0 and S_q > 0:
-        _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,
+        _check(MLA_ERR_INVALID_ARGUMENT if algo not in (MLA_ALGO_MFMA, MLA_ALGO_FUSED) else MLA_ERR_UNSUPPORTED,
                name + "_workspace_size")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -321,7 +322,7 @@ def mla_bwd_explicit(q_nope: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tenso
                          algo=algo)
     ws_bytes = mla_bwd_explicit_workspace_size(desc)
     if ws_bytes == 0:
-        _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,
+        _check(MLA_ERR_INVALID_ARGUMENT if algo not in (MLA_ALGO_MFMA, MLA_ALGO_FUSED) else MLA_ERR_UNSUPPORTED,
                "mla_bwd_explicit_workspace_size")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -379,7 +380,7 @@ def mla_decode_absorbed(q_nope: torch.Tensor, q_pe: torch.Tensor, kv_cache: torc
     dev = q_nope.device
     ws_bytes = mla_decode_absorbed_workspace_size(desc)
     if ws_bytes == 0:
-        _check(MLA_ERR_INVALID_ARGUMENT if algo != MLA_ALGO_MFMA else MLA_ERR_UNSUPPORTED,
+        _check(MLA_ERR_INVALID_ARGUMENT if algo not in (MLA_ALGO_MFMA, MLA_ALGO_FUSED) else MLA_ERR_UNSUPPORTED,
                "mla_decode_absorbed_workspace_size")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

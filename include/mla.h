@@ -80,7 +80,11 @@ typedef enum { MLA_BF16 = 0, MLA_FP32 = 1 } mla_dtype;
 typedef enum {
   MLA_ALGO_AUTO = 0,     /* MFMA kernels when the shape allows, else SIMT      */
   MLA_ALGO_SIMT = 1,     /* fp32 SIMT kernels, any supported shape or dtype     */
-  MLA_ALGO_MFMA = 2      /* MFMA kernels; MLA_ERR_UNSUPPORTED if not eligible   */
+  MLA_ALGO_MFMA = 2,     /* MFMA kernels; MLA_ERR_UNSUPPORTED if not eligible   */
+  MLA_ALGO_FUSED = 3     /* explicit forward only: the MFMA attention with the
+                            latent up-projection fused in, so K_nope and V
+                            never reach device memory (MFMA eligibility; the
+                            other entry points return MLA_ERR_UNSUPPORTED)    */
 } mla_algo;
 
 /* ------------------------------------------------------------------------ */
@@ -103,9 +107,9 @@ typedef struct {
   float rope_base;      /* RoPE base, > 1 (10000)                              */
   mla_dtype in_dtype;   /* dtype of q_nope, q_pe, c_kv, k_pe, w_kv_b            */
   mla_dtype out_dtype;  /* dtype of out (lse is always fp32)                   */
-  mla_algo algo;        /* kernel family.  MFMA needs bf16 inputs, d_kv 512,
-                           d_nope 128, d_rope 64, d_v 128, and at most 2^22
-                           visible latent rows per sequence                  */
+  mla_algo algo;        /* kernel family.  MFMA and FUSED need bf16 inputs,
+                           d_kv 512, d_nope 128, d_rope 64, d_v 128, and at
+                           most 2^22 visible latent rows per sequence        */
 } mla_explicit_desc;
 
 /* Bytes of device workspace mla_fwd_explicit needs for `desc`; 0 if the
@@ -127,7 +131,14 @@ size_t mla_fwd_explicit_workspace_size(const mla_explicit_desc* desc);
  *   workspace: device buffer of at least mla_fwd_explicit_workspace_size()
  *   bytes; its contents on entry are ignored and on exit are unspecified
  *   (see mla_fwd_explicit_workspace_layout for the MFMA path's intermediates).
- * Latent rows no query can see (causal) are neither up-projected nor read. */
+ * Latent rows no query can see (causal) are neither up-projected nor read.
+ * With algo MLA_ALGO_FUSED the up-projection runs inside the attention
+ * kernel, once per 256-query block that reads a key tile ([LAGA] "Where Pith
+ * is reading between the lines": the fused kernel as future work; Fig. 3
+ * caption: the repeated up-projection is its cost), and the workspace holds
+ * only the RoPE tables and the rotated key band (2 * B * s_vis' * 64 bytes,
+ * s_vis' the visible rows rounded up to 256) instead of the
+ * B * H * s_vis' * 512 bytes of fp16 K_nope and V^T. */
 mla_status mla_fwd_explicit(const mla_explicit_desc* desc,
                             const void* q_nope, const void* q_pe,
                             const void* c_kv, const void* k_pe,

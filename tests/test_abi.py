@@ -141,6 +141,29 @@ def test_explicit_unsupported():
                                 None) == mla.MLA_ERR_UNSUPPORTED
 
 
+def test_fused_algo_workspace_and_scope():
+    lib = mla.library()
+    d = _v3_desc(algo=mla.MLA_ALGO_FUSED)
+    ws = mla.mla_fwd_explicit_workspace_size(d)
+    # the two fp32 (cos, sin) RoPE tables and the fp16 key band only: no K_nope / V^T
+    assert 0 < ws <= 2 * (8 * 4096 * 32) + 2 * 4096 * 64 + 3 * 256
+    assert ws + 2 * 128 * 4096 * 256 <= mla.mla_fwd_explicit_workspace_size(_v3_desc(algo=mla.MLA_ALGO_MFMA))
+    with pytest.raises(mla.MlaError):
+        mla.mla_fwd_explicit_workspace_layout(d)
+    # shapes the MFMA kernels do not take are unsupported, not rerouted
+    d1 = _v3_desc(d_nope=96, algo=mla.MLA_ALGO_FUSED)
+    assert mla.mla_fwd_explicit_workspace_size(d1) == 0
+    assert lib.mla_fwd_explicit(ctypes.byref(d1), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                None) == mla.MLA_ERR_UNSUPPORTED
+    # misaligned operand on the fused path
+    assert lib.mla_fwd_explicit(ctypes.byref(d), FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws,
+                                None) == mla.MLA_ERR_INVALID_ARGUMENT
+    # the fused algorithm names an explicit-forward kernel only
+    assert mla.mla_fwd_absorbed_workspace_size(d) == 0
+    assert mla.mla_bwd_explicit_workspace_size(d) == 0
+    assert mla.mla_decode_absorbed_workspace_size(_dec_desc(algo=mla.MLA_ALGO_FUSED)) == 0
+
+
 def _dec_desc(**kw):
     base = dict(batch=64, n_heads=128, d_kv=512, d_nope=128, d_rope=64, d_v=128, max_cache_len=32768,
                 n_splits=16)

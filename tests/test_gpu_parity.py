@@ -152,6 +152,72 @@ def test_mfma_explicit_edges(mla, cfg):
     _compare_lse(l, rl, True, cfg.name)
 
 
+# The fused up-projection: every edge case above plus shapes that cross its
+# 128-key tiles and 256-query blocks raggedly, several heads per XCD, and a
+# bf16 output.
+FUSED_EXTRA = [
+    I.small_explicit("fused_ragged_heads", batch=2, s_q=530, s_kv=530, n_heads=19, d_kv=512, d_nope=128,
+                     d_rope=64, d_v=128, dtype="bf16", seed=111),
+    I.small_explicit("fused_long_kv", s_q=257, s_kv=1100, n_heads=4, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                     q_pos0=843, dtype="bf16", seed=112),
+    I.small_explicit("fused_noncausal_tail", s_q=33, s_kv=385, n_heads=9, d_kv=512, d_nope=128, d_rope=64,
+                     d_v=128, causal=False, dtype="bf16", seed=113),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE + FUSED_EXTRA, ids=lambda c: c.name)
+def test_fused_explicit_edges(mla, cfg):
+    x = I.make_explicit_inputs(cfg)
+    o, l, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_FUSED)
+    ro, rl = _oracle_explicit(cfg, x)
+    _compare(o, ro, True, f"fused {cfg.name} out")
+    _compare_lse(l, rl, True, f"fused {cfg.name}")
+
+
+def test_fused_bf16_out_matches_fp32_out(mla):
+    cfg = FUSED_EXTRA[0]
+    x = I.make_explicit_inputs(cfg)
+    o32, l32_, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_FUSED)
+    o16, l16, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_FUSED, out_dtype=torch.bfloat16)
+    # the same fp32 values rounded once to bf16 (round-to-nearest-even)
+    ref = torch.from_numpy(o32).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(o16, ref)
+    assert np.array_equal(l16, l32_)
+
+
+def test_fused_workspace_is_small(mla):
+    cfg = I.EXPLICIT_CONFIGS["v3_headshard_sp8"]
+    kw = dict(batch=cfg.batch, s_q=cfg.s_q, s_kv=cfg.s_kv, n_heads=cfg.n_heads, d_kv=cfg.d_kv,
+              d_nope=cfg.d_nope, d_rope=cfg.d_rope, d_v=cfg.d_v, causal=cfg.causal,
+              softmax_scale=cfg.softmax_scale, in_dtype=mla.MLA_BF16)
+    fused = mla.mla_fwd_explicit_workspace_size(mla.explicit_desc(algo=mla.MLA_ALGO_FUSED, **kw))
+    mat = mla.mla_fwd_explicit_workspace_size(mla.explicit_desc(algo=mla.MLA_ALGO_MFMA, **kw))
+    # the materialised path's fp16 K_nope and V^T: H * 256 * 2 bytes per latent row
+    assert mat - fused >= cfg.n_heads * 256 * 2 * cfg.s_kv
+    # what remains: the fp32 (cos, sin) tables of queries and keys, the fp16 key band
+    assert fused <= 2 * 8 * 32 * cfg.s_q + 2 * 64 * cfg.s_kv + 3 * 256
+
+
+# One rank's share after LAGA's all-to-all at S = 16384 over 8 ranks: all 16
+# heads, rows sampled over the whole sequence; the fused and materialised
+# paths also agree with each other on the whole tensor.
+def test_fused_headshard_share(mla):
+    cfg = I.EXPLICIT_CONFIGS["v3_headshard_sp8"]
+    x = I.make_explicit_inputs(cfg)
+    of, lf, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_FUSED)
+    om, lm, _, _ = _run_explicit(mla, cfg, x, algo=mla.MLA_ALGO_MFMA)
+    assert np.isfinite(of).all() and np.isfinite(lf).all()
+    d = float(np.abs(of - om).max())
+    _say(f"fused vs materialised: max|d| out {d:.3e}, lse {float(np.abs(lf - lm).max()):.3e}")
+    assert d <= BF16_MAX_ABS
+    del om, lm
+    rng = np.random.default_rng(13)
+    rows = _sample_rows(cfg.s_q, rng, k=64)
+    ro, rl = _oracle_explicit(cfg, x, rows=rows)
+    _compare(of[:, rows], ro, True, "fused head-shard sampled out")
+    _compare_lse(lf[:, :, rows], rl, True, "fused head-shard")
+
+
 @pytest.mark.parametrize("cfg", EDGE[:4], ids=lambda c: c.name)
 def test_simt_explicit_bf16(mla, cfg):
     x = I.make_explicit_inputs(cfg)
