@@ -278,9 +278,87 @@ def I_mod():
     return I
 
 
+def fused_upproj_flop(cfg, qb=256, kt=128):
+    """MFMA FLOPs of the up-projection as the fused kernel executes it: every
+    256-query block up-projects each 128-key tile it reads (keys up to the
+    causal limit of its last row), for every head."""
+    total_tiles = 0
+    for q0 in range(0, cfg.s_q, qb):
+        last = min(q0 + qb, cfg.s_q) - 1
+        kend = cfg.s_kv if not cfg.causal else min(max(cfg.q_pos0 + last - cfg.kv_pos0 + 1, 0), cfg.s_kv)
+        total_tiles += -(-kend // kt)
+    return 2 * cfg.batch * cfg.n_heads * total_tiles * kt * cfg.d_kv * (cfg.d_nope + cfg.d_v)
+
+
+def fused_case(mla, torch, cfg, args):
+    """The explicit forward with K_nope/V materialised in HBM (up-projection
+    GEMM, then attention) against the fused kernel that recomputes them per
+    query block, on one configuration: time per call (HIP events, eager, after
+    one untimed call), per-kernel averages, and the device memory each call
+    allocates (rise of torch.cuda.max_memory_allocated over the resident
+    inputs)."""
+    log(f"materialised vs fused up-projection at {cfg.name}: {args.form_calls + 2} calls of each")
+    x = I_mod().make_explicit_inputs(cfg)
+    t = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    del x
+    fl = cfg.flops()
+    res = {"workload": f"{cfg.name} explicit fwd (B={cfg.batch}, S={cfg.s_q}, n_h={cfg.n_heads}, causal): "
+                       "one rank's heads after the all-to-all of S=16384 over 8 ranks",
+           "algorithmic_flop": fl["total"]}
+    outs = {}
+    for name, algo in (("materialised", mla.MLA_ALGO_MFMA), ("fused", mla.MLA_ALGO_FUSED)):
+        kw = dict(q_pos0=cfg.q_pos0, kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale,
+                  algo=algo)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        out, lse, ws = mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], **kw)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ms = []
+        for _ in range(args.form_calls):
+            ev[0].record()
+            mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], out=out, lse=lse,
+                                 workspace=ws, **kw)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]))
+        mla.mla_timing_reset()
+        mla.mla_timing_begin()
+        for _ in range(2):
+            mla.mla_fwd_explicit(t["q_nope"], t["q_pe"], t["c_kv"], t["k_pe"], t["w_kv_b"], out=out, lse=lse,
+                                 workspace=ws, **kw)
+        torch.cuda.synchronize()
+        mla.mla_timing_end()
+        kt = mla.mla_timing_get()
+        mla.mla_timing_reset()
+        kernels = {k: {"avg_ms": tot / max(n, 1)} for k, (tot, n) in kt.items()}
+        avg = float(np.mean(ms))
+        res[name] = {"ms": avg, "tflops_algorithmic": fl["total"] / (avg * 1e-3) / 1e12,
+                     "device_bytes": int(peak), "workspace_bytes": int(ws.numel()), "kernels": kernels}
+        outs[name] = out
+        del lse, ws
+    f = res["fused"]
+    executed = fl["attention"] + fused_upproj_flop(cfg)
+    ka = f["kernels"].get("fused_attention")
+    if ka:
+        ach = executed / (ka["avg_ms"] * 1e-3) / 1e12
+        ka.update({"executed_flop": executed, "achieved": ach, "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_TFLOPS,
+                   "note": "executed = attention + the up-projection repeated per 256-query block"})
+    res["fused_over_materialised_time"] = f["ms"] / res["materialised"]["ms"]
+    res["memory_saved_bytes"] = res["materialised"]["device_bytes"] - f["device_bytes"]
+    res["max_abs_diff_fused_vs_materialised"] = float((outs["fused"] - outs["materialised"]).abs().max())
+    del t, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def forms_memory_and_time(mla, torch, names, args):
-    """Explicit and absorbed forms of the same V3 causal forward at several
-    sequence lengths: time per call (HIP events, eager, after one untimed call)
+    """Explicit (K_nope/V materialised, and fused into the attention) and
+    absorbed forms of the same V3 causal forward at several sequence lengths:
+    time per call (HIP events, eager, after one untimed call)
     and the device memory each call allocates, measured as the rise of
     torch.cuda.max_memory_allocated over the resident inputs while the binding
     allocates the outputs and the workspace and the call runs."""
@@ -293,8 +371,12 @@ def forms_memory_and_time(mla, torch, names, args):
         t = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
         del x
         row = {"tokens": cfg.s_q, "n_heads": cfg.n_heads}
-        for form, fn in (("explicit", mla.mla_fwd_explicit), ("absorbed", mla.mla_fwd_absorbed)):
-            kw = dict(q_pos0=cfg.q_pos0, kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale)
+        forms = (("explicit", mla.mla_fwd_explicit, mla.MLA_ALGO_AUTO),
+                 ("explicit_fused", mla.mla_fwd_explicit, mla.MLA_ALGO_FUSED),
+                 ("absorbed", mla.mla_fwd_absorbed, mla.MLA_ALGO_AUTO))
+        for form, fn, algo in forms:
+            kw = dict(q_pos0=cfg.q_pos0, kv_pos0=cfg.kv_pos0, causal=cfg.causal, softmax_scale=cfg.softmax_scale,
+                      algo=algo)
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
             base = torch.cuda.memory_allocated()
@@ -386,6 +468,8 @@ def parse():
     p.add_argument("--no-forms", action="store_true",
                    help="skip the explicit-vs-absorbed memory and time comparison at 4K/8K/16K tokens")
     p.add_argument("--no-backward", action="store_true", help="skip the explicit-form backward")
+    p.add_argument("--no-fused", action="store_true",
+                   help="skip the materialised-vs-fused up-projection comparison at the head-shard share")
     p.add_argument("--form-calls", type=int, default=3,
                    help="timed calls per form and length in the explicit-vs-absorbed comparison")
     p.add_argument("--copy-calibration", action="store_true",
@@ -694,6 +778,9 @@ def main():
 
     if not args.no_backward:
         res["backward"] = backward_case(mla, torch, ecfg, args)
+
+    if not args.no_fused:
+        res["fused_headshard"] = fused_case(mla, torch, I.EXPLICIT_CONFIGS["v3_headshard_sp8"], args)
 
     if not args.no_cpu_baseline:
         log("oracle CPU baseline on a bounded sample")
