@@ -64,13 +64,13 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "2bf9eca3de581d72", "fetch_kib": 351118.4, "write_kib": 292863.7,
+    "mfma_attention": {"digest": "aabadcfac918c61e", "fetch_kib": 343000.0, "write_kib": 264192.0,
                      "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "68ab45b86f5ca350", "fetch_kib": 100828.7, "write_kib": 273802.5,
+    "mfma_up_projection": {"digest": "176270ca02d70782", "fetch_kib": 100788.1, "write_kib": 274679.0,
                          "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "9b6b211f54df7297", "fetch_kib": 1216723.1, "write_kib": 131584.0,
+    "mfma_split_kv": {"digest": "33decc937d93c9dc", "fetch_kib": 1216712.5, "write_kib": 131584.0,
                     "fetch_factor": 0.50002, "write_factor": 1.0},
-    "lse_combine": {"digest": "d55fbd5cb131989a", "fetch_kib": 84068.6, "write_kib": 4352.1,
+    "lse_combine": {"digest": "ced3d374da039612", "fetch_kib": 84068.6, "write_kib": 4352.0,
                   "fetch_factor": 0.50002, "write_factor": 1.0},
 }
 
