@@ -67,12 +67,14 @@ fused_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ krot, const 
   __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * VT_LD];
   __shared__ __attribute__((aligned(16))) uint16_t Cr[2 * C_ELEMS];
 
-  // heads on XCDs (blockIdx.x % 8), longest query blocks first
+  // heads on XCDs (blockIdx.x % 8), two at a time, longest query blocks
+  // first alternating between the two
   const int P = a.B * a.H;
   const int n = blockIdx.x;
   const int xcd = n & 7, slot = n >> 3;
-  const int p = xcd + 8 * (slot / nqt);
-  const int qt = nqt - 1 - (slot % nqt);
+  const int grp = slot / (2 * nqt), r = slot % (2 * nqt);
+  const int p = xcd + 8 * (2 * grp + (r & 1));
+  const int qt = nqt - 1 - (r >> 1);
   if (p >= P) return;
   const int b = p / a.H, h = p % a.H;
   const int64_t bh = (int64_t)b * a.H + h;
@@ -337,7 +339,7 @@ hipError_t launch_fused_attention(const ExplicitArgs& a, const uint16_t* krot, c
   if (a.Sq == 0) return hipSuccess;
   const int nqt = (a.Sq + QB - 1) / QB;
   const int P = a.B * a.H;
-  const dim3 grid(8 * ((P + 7) / 8) * nqt);
+  const dim3 grid(16 * ((P + 15) / 16) * nqt);         // whole pairs of heads on every XCD
   if (a.out_dt == MLA_BF16)
     hipLaunchKernelGGL(fused_attention_kernel<MLA_BF16>, grid, dim3(NT), 0, stream, a, krot, qtab, nqt);
   else

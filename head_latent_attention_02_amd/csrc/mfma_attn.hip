@@ -48,7 +48,7 @@
 // pass), so the accumulators are only ever touched by MFMAs.
 //
 // Workgroups are dealt so that all query tiles of one head run on the same
-// XCD (its L2 holds that head's K/V), longest first.
+// XCD (its L2 holds that head's K/V), two heads at a time, longest first.
 #include "common.h"
 #include "kernels.h"
 
@@ -141,11 +141,16 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
                       const uint16_t* __restrict__ krot, const float2* __restrict__ qtab, int nqt) {
   __shared__ __attribute__((aligned(16))) uint16_t Ls[NSTAGE * STAGE];
 
+  // XCD x (= blockIdx.x % 8, the order the dispatcher deals workgroups)
+  // takes the (batch, head) pairs p = x, x + 8, ... two at a time; within a
+  // pair the query tiles go longest first, alternating between the two
+  // heads, so the long tiles of the last pair do not start last.
   const int P = a.B * a.H;
   const int n = blockIdx.x;
   const int xcd = n & 7, slot = n >> 3;
-  const int p = xcd + 8 * (slot / nqt);
-  const int qt = nqt - 1 - (slot % nqt);
+  const int grp = slot / (2 * nqt), r = slot % (2 * nqt);
+  const int p = xcd + 8 * (2 * grp + (r & 1));
+  const int qt = nqt - 1 - (r >> 1);
   if (p >= P) return;
   const int b = p / a.H, h = p % a.H;
   const int64_t bh = (int64_t)b * a.H + h;
@@ -523,8 +528,8 @@ hipError_t launch_mfma_attention(const ExplicitArgs& a, const uint16_t* kn, cons
   if (a.Sq == 0) return hipSuccess;
   const int P = a.B * a.H;
   const int nqt = (a.Sq + QT - 1) / QT;
-  const int P8 = (P + 7) & ~7;
-  dim3 grid((unsigned)(P8 * nqt));
+  const int P16 = (P + 15) & ~15;                    // whole pairs of heads on every XCD
+  dim3 grid((unsigned)(P16 * nqt));
   if (a.out_dt == MLA_BF16)
     hipLaunchKernelGGL(mfma_attention_kernel<MLA_BF16>, grid, dim3(NTHREADS), 0, stream, a, kn, vt, krot,
                        qtab, nqt);
