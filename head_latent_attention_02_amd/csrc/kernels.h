@@ -101,6 +101,7 @@ struct MfmaBwdWorkspace {
   float2 *qtab, *ktab;
   uint16_t *kn, *vt, *krot, *qf, *qft, *dof, *doft, *vrow, *knt, *krt, *dkv, *dkvt, *wt, *ct;
   float *dvec, *dkr;
+  float* lsdt;        // per 32-query tile: LSE then D, 32 each, in the permuted row order
   int sq_pad;
 };
 // Bytes of workspace (base == nullptr) or the carving of `base` into `w`.

@@ -59,7 +59,8 @@ __device__ __forceinline__ uint16_t h_bits(float x) { return float_to_f16_bits(x
 template <mla_dtype OT>
 __global__ void __launch_bounds__(256)
 prep_q_kernel(BackwardArgs a, const float2* __restrict__ qtab, uint16_t* __restrict__ qf, uint16_t* __restrict__ qft,
-              uint16_t* __restrict__ dof, uint16_t* __restrict__ doft, float* __restrict__ dvec, int sq_pad) {
+              uint16_t* __restrict__ dof, uint16_t* __restrict__ doft, float* __restrict__ dvec,
+              float* __restrict__ lsdt, int sq_pad) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[32][DQK + 8];
   __shared__ __attribute__((aligned(16))) uint16_t Ds[32][DV + 8];
   __shared__ float red[32][9];
@@ -109,6 +110,11 @@ prep_q_kernel(BackwardArgs a, const float2* __restrict__ qtab, uint16_t* __restr
     float s = 0.f;
     for (int k = 0; k < 8; ++k) s += red[r][k];
     dvec[bh * sq_pad + i] = live ? s : 0.f;
+    // the key-parallel kernel's copy of this tile: LSE then D at the LDS row
+    // of query r (rows past S_q get an infinite LSE, so P = 0 there)
+    float* t64 = lsdt + (bh * (sq_pad / 32) + blockIdx.x) * 64;
+    t64[perm32(r)] = live ? a.lse[bh * f.Sq + i] : INFINITY;
+    t64[32 + perm32(r)] = live ? s : 0.f;
   }
   // row layouts: 192 / 128 fp16 per row, 16-byte pieces
   for (int c = tid; c < 32 * (DQK / 8); c += 256) {
@@ -164,24 +170,34 @@ transpose_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out, in
 }
 
 // -------------------------------------------------------------------- kv --
-// LDS stage of one 32-query tile (fp16 elements; rows padded by 8 elements):
-//   Qp  [32][192+8]  rows in permuted order      QT  [192][32+8]
-//   dOp [32][128+8]  rows in permuted order      dOT [128][32+8]
-//   lse, D [32] in permuted order (fp32)
+// LDS stage of one 32-query tile, in 16-byte chunks.  Rows are padded so that
+// 16-byte fragment reads of 16 consecutive rows fall in distinct banks; each
+// part starts at a multiple of 64 chunks, so one buffer->LDS copy instruction
+// (64 lanes x 16 bytes) never spans two parts:
+//   Qp  [32][192+8] fp16, rows in permuted order   chunks    0 ..  799 (832)
+//   dOp [32][128+8] fp16, rows in permuted order   chunks  832 .. 1375 (1408)
+//   QT  [192][32+8] fp16                            chunks 1408 .. 2367
+//   dOT [128][32+8] fp16                            chunks 2368 .. 3007
+//   LSE, D [32] each, fp32, permuted order          chunks 3008 .. 3023 (3072)
+// Padding chunks are filled with a copy of some chunk of the same part.
 constexpr int QP_LD = DQK + 8, DOP_LD = DV + 8, QT_LD = 40;
-constexpr int KV_STAGE_H = 32 * QP_LD + 32 * DOP_LD + DQK * QT_LD + DV * QT_LD;   // fp16 elements
-constexpr int KV_STAGE_B = KV_STAGE_H * 2 + 2 * 32 * 4;                           // + lse, D
-constexpr int KV_CHUNKS = 32 * (DQK / 8) + 32 * (DV / 8) + DQK * 4 + DV * 4;      // 16-byte pieces (2560)
-constexpr int KV_PER_THREAD = KV_CHUNKS / 256;                                     // 10
-static_assert(KV_CHUNKS % 256 == 0, "tile pieces must split evenly");
+constexpr int KV_QP0 = 0, KV_DOP0 = 832, KV_QT0 = 1408, KV_DOT0 = 2368, KV_LSD0 = 3008, KV_CH = 3072;
+constexpr int KV_STAGE_B = KV_CH * 16;
+constexpr int KV_INSTR = KV_CH / 64;          // copy instructions per stage (48)
+constexpr int KV_IPW = KV_INSTR / 4;          // per wave (12)
+constexpr int KV_NST = 3;                     // stages
+static_assert(KV_QP0 + 32 * QP_LD / 8 <= KV_DOP0 && KV_DOP0 + 32 * DOP_LD / 8 <= KV_QT0 &&
+              KV_QT0 + DQK * QT_LD / 8 <= KV_DOT0 && KV_DOT0 + DV * QT_LD / 8 <= KV_LSD0 && KV_LSD0 + 16 <= KV_CH,
+              "stage parts");
+static_assert(KV_DOP0 % 64 == 0 && KV_QT0 % 64 == 0 && KV_DOT0 % 64 == 0 && KV_LSD0 % 64 == 0, "part alignment");
 
 __global__ void __launch_bounds__(256)
 kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __restrict__ qft,
-          const uint16_t* __restrict__ dof, const uint16_t* __restrict__ doft, const float* __restrict__ dvec,
+          const uint16_t* __restrict__ dof, const uint16_t* __restrict__ doft, const float* __restrict__ lsdt,
           const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vt, const uint16_t* __restrict__ krot,
           uint16_t* __restrict__ dkv, uint16_t* __restrict__ dkvt, float* __restrict__ dkr, int sq_pad,
           int n_kb) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem_kv[2 * KV_STAGE_B];
+  __shared__ __attribute__((aligned(16))) uint8_t smem_kv[KV_NST * KV_STAGE_B];
   const ExplicitArgs& f = a.f;
   // longest first: key block 0 sees the most queries
   const int kbi = blockIdx.x % n_kb, bhi = blockIdx.x / n_kb;
@@ -192,6 +208,75 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
   const int l32 = lane & 31, hb = lane >> 5;
   const int key = kb + wave * 32 + l32;            // this lane's key (accumulator column)
   const float c2 = f.scale * MLA_LOG2E;
+
+  // query tiles: from the first one that can see key kb to the last
+  int qt0 = 0;
+  if (f.causal) {
+    const int64_t first = (int64_t)kb + f.kv_pos0 - f.q_pos0;     // first query that sees key kb
+    qt0 = (int)max((int64_t)0, min(first, (int64_t)sq_pad) / 32);
+  }
+  const int nqt = sq_pad / 32;
+
+  // ---- tile copies: instruction n = KV_IPW * wave + i fills chunks 64n .. 64n+63
+  // of a stage; the lane's source offset within its part is fixed, the tile
+  // moves it by a uniform amount.
+  const uint32_t q_bytes = (uint32_t)sq_pad * DQK * 2, o_bytes = (uint32_t)sq_pad * DV * 2;
+  const i32x4_t rs_qp = make_rsrc_uniform(qf + bh * sq_pad * DQK, q_bytes);
+  const i32x4_t rs_dop = make_rsrc_uniform(dof + bh * sq_pad * DV, o_bytes);
+  const i32x4_t rs_qt = make_rsrc_uniform(qft + bh * DQK * sq_pad, q_bytes);
+  const i32x4_t rs_dot = make_rsrc_uniform(doft + bh * DV * sq_pad, o_bytes);
+  const i32x4_t rs_lsd = make_rsrc_uniform(lsdt + bh * (sq_pad / 32) * 64, (uint32_t)(sq_pad / 32) * 256);
+  int voff[KV_IPW];
+#pragma unroll
+  for (int i = 0; i < KV_IPW; ++i) {
+    const int pch = 64 * (KV_IPW * wave + i) + lane;
+    int o;
+    if (pch < KV_DOP0) {
+      int rho = pch / (QP_LD / 8), c = pch % (QP_LD / 8);
+      if (rho >= 32 || c >= DQK / 8) rho = c = 0;
+      o = (perm32(rho) * DQK + 8 * c) * 2;
+    } else if (pch < KV_QT0) {
+      const int p2 = pch - KV_DOP0;
+      int rho = p2 / (DOP_LD / 8), c = p2 % (DOP_LD / 8);
+      if (rho >= 32 || c >= DV / 8) rho = c = 0;
+      o = (perm32(rho) * DV + 8 * c) * 2;
+    } else if (pch < KV_DOT0) {
+      const int p2 = pch - KV_QT0;
+      int d = p2 / (QT_LD / 8), c = p2 % (QT_LD / 8);
+      if (c >= 4) c = 0;
+      o = (d * sq_pad + 8 * c) * 2;
+    } else if (pch < KV_LSD0) {
+      const int p2 = pch - KV_DOT0;
+      int d = p2 / (QT_LD / 8), c = p2 % (QT_LD / 8);
+      if (c >= 4) c = 0;
+      o = (d * sq_pad + 8 * c) * 2;
+    } else {
+      const int p2 = pch - KV_LSD0;
+      o = (p2 < 16 ? p2 : 0) * 16;
+    }
+    voff[i] = o;
+  }
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&smem_kv[0];
+  // instruction n's part is known at compile time once the wave is: each wave
+  // runs its own unrolled copy of the issue code
+  auto issue_w = [&](auto wc, int qt) __attribute__((always_inline)) {
+    constexpr int W = decltype(wc)::value;
+    const uint32_t st = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(((qt - qt0) % KV_NST) * KV_STAGE_B));
+    static_for<KV_IPW>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value, n = KV_IPW * W + i, c0 = 64 * n;
+      constexpr int part = c0 < KV_DOP0 ? 0 : c0 < KV_QT0 ? 1 : c0 < KV_DOT0 ? 2 : c0 < KV_LSD0 ? 3 : 4;
+      const i32x4_t& rs = part == 0 ? rs_qp : part == 1 ? rs_dop : part == 2 ? rs_qt : part == 3 ? rs_dot : rs_lsd;
+      const int so = part == 0 ? qt * 32 * DQK * 2 : part == 1 ? qt * 32 * DV * 2 : part <= 3 ? qt * 64 : qt * 256;
+      lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[i], __builtin_amdgcn_readfirstlane(so));
+    });
+  };
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue_tile = [&](int qt) __attribute__((always_inline)) {
+    if (wave_u == 0) issue_w(std::integral_constant<int, 0>{}, qt);
+    else if (wave_u == 1) issue_w(std::integral_constant<int, 1>{}, qt);
+    else if (wave_u == 2) issue_w(std::integral_constant<int, 2>{}, qt);
+    else issue_w(std::integral_constant<int, 3>{}, qt);
+  };
 
   // K (B operand of S = Q K^T: lane = key, k-slots 16 ks + 8 hb ..) and V
   // (B operand of dP = dO V^T) of the lane's key, loaded once
@@ -213,14 +298,9 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
       for (int e = 0; e < 8; ++e)
         vb_[ks][e] = __builtin_bit_cast(f16, vc[(int64_t)(16 * ks + 8 * hb + e) * f.s_pad]);
   }
-
-  // query tiles: from the first one that can see key kb to the last
-  int qt0 = 0;
-  if (f.causal) {
-    const int64_t first = (int64_t)kb + f.kv_pos0 - f.q_pos0;     // first query that sees key kb
-    qt0 = (int)max((int64_t)0, min(first, (int64_t)sq_pad) / 32);
-  }
-  const int nqt = sq_pad / 32;
+  // these loads are done before the first copies go out, so the copy waits
+  // below count copies only
+  wait_vmcnt<0>();
 
   f32x16_t dvt[DV / 32], dkt[DQK / 32];
 #pragma unroll
@@ -228,101 +308,52 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
 #pragma unroll
   for (int d = 0; d < DQK / 32; ++d) dkt[d] = f32x16_t{};
 
-  // tile loader: piece c of the tile into registers, then into a stage
-  u32x4_t stg[KV_PER_THREAD];
-  float sl = 0.f, sd = 0.f;                       // lse / D of one query (threads 0..31)
-  auto load_tile = [&](int qt) __attribute__((always_inline)) {
-    const int q0 = qt * 32;
-#pragma unroll
-    for (int k = 0; k < KV_PER_THREAD; ++k) {
-      const int c = tid + 256 * k;
-      const uint16_t* src;
-      if (c < 768) {                                     // Qp: row rho <- query perm(rho)
-        const int rho = c / 24, cc = c % 24;
-        src = qf + (bh * sq_pad + q0 + perm32(rho)) * DQK + cc * 8;
-      } else if (c < 1280) {                             // dOp
-        const int c2_ = c - 768, rho = c2_ / 16, cc = c2_ % 16;
-        src = dof + (bh * sq_pad + q0 + perm32(rho)) * DV + cc * 8;
-      } else if (c < 2048) {                             // QT: row d, 8 queries
-        const int c2_ = c - 1280, d = c2_ >> 2, q8 = (c2_ & 3) * 8;
-        src = qft + (bh * DQK + d) * sq_pad + q0 + q8;
-      } else {                                           // dOT
-        const int c2_ = c - 2048, d = c2_ >> 2, q8 = (c2_ & 3) * 8;
-        src = doft + (bh * DV + d) * sq_pad + q0 + q8;
-      }
-      stg[k] = *reinterpret_cast<const u32x4_t*>(src);
-    }
-    if (tid < 32) {
-      const int i = q0 + perm32(tid);                    // stored at rho = tid
-      sl = (i < f.Sq) ? a.lse[bh * f.Sq + i] : INFINITY;
-      sd = dvec[bh * sq_pad + i];
-    }
+  // Tile qt sits in stage (qt - qt0) % 3.  Iteration qt computes P and dS of
+  // tile qt (its S and dP were computed at the end of the previous
+  // iteration), dV^T and dK^T, then S and dP of tile qt + 1; tile qt + 2 is
+  // copied at the top of iteration qt into the stage last read in iteration
+  // qt - 1, so the copies of a tile have a whole iteration to land.
+  auto stage = [&](int qt) __attribute__((always_inline)) {
+    return reinterpret_cast<const uint16_t*>(smem_kv + ((qt - qt0) % KV_NST) * KV_STAGE_B);
   };
-  auto store_tile = [&](int s) __attribute__((always_inline)) {
-    uint16_t* st = reinterpret_cast<uint16_t*>(smem_kv + s * KV_STAGE_B);
+  auto sdp = [&](int qt, f32x16_t& sacc, f32x16_t& pacc) __attribute__((always_inline)) {
+    const uint16_t* Qp = stage(qt) + KV_QP0 * 8;
+    const uint16_t* dOp = stage(qt) + KV_DOP0 * 8;
+    sacc = f32x16_t{};
+    pacc = f32x16_t{};
 #pragma unroll
-    for (int k = 0; k < KV_PER_THREAD; ++k) {
-      const int c = tid + 256 * k;
-      uint16_t* dst;
-      if (c < 768) {
-        const int rho = c / 24, cc = c % 24;
-        dst = st + rho * QP_LD + cc * 8;
-      } else if (c < 1280) {
-        const int c2_ = c - 768, rho = c2_ / 16, cc = c2_ % 16;
-        dst = st + 32 * QP_LD + rho * DOP_LD + cc * 8;
-      } else if (c < 2048) {
-        const int c2_ = c - 1280, d = c2_ >> 2, q8 = (c2_ & 3) * 8;
-        dst = st + 32 * QP_LD + 32 * DOP_LD + d * QT_LD + q8;
-      } else {
-        const int c2_ = c - 2048, d = c2_ >> 2, q8 = (c2_ & 3) * 8;
-        dst = st + 32 * QP_LD + 32 * DOP_LD + DQK * QT_LD + d * QT_LD + q8;
-      }
-      *reinterpret_cast<u32x4_t*>(dst) = stg[k];
-    }
-    if (tid < 32) {
-      float* lsd = reinterpret_cast<float*>(smem_kv + s * KV_STAGE_B + KV_STAGE_H * 2);
-      lsd[tid] = sl;
-      lsd[32 + tid] = sd;
-    }
-  };
-
-  if (qt0 < nqt) {
-    load_tile(qt0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int s = (qt - qt0) & 1;
-    if (qt + 1 < nqt) load_tile(qt + 1);
-    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem_kv + s * KV_STAGE_B);
-    const uint16_t* Qp = st;
-    const uint16_t* dOp = st + 32 * QP_LD;
-    const uint16_t* QT = dOp + 32 * DOP_LD;
-    const uint16_t* dOT = QT + DQK * QT_LD;
-    const float* lsd = reinterpret_cast<const float*>(smem_kv + s * KV_STAGE_B + KV_STAGE_H * 2);
-    // S = Qp K^T, dP = dOp V^T  (rows: permuted queries, columns: keys)
-    f32x16_t sacc = {}, pacc = {};
-#pragma unroll
-    for (int ks = 0; ks < DQK / 16; ++ks)
+    for (int ks = 0; ks < DQK / 16; ++ks) {
       sacc = mfma(*reinterpret_cast<const f16x8_t*>(Qp + l32 * QP_LD + 16 * ks + 8 * hb), kb_[ks], sacc);
-#pragma unroll
-    for (int ks = 0; ks < DV / 16; ++ks)
-      pacc = mfma(*reinterpret_cast<const f16x8_t*>(dOp + l32 * DOP_LD + 16 * ks + 8 * hb), vb_[ks], pacc);
-    // P and dS; element e is query row rho = 8 (e/4) + 4 hb + e%4
-    f16x8_t pb[2], sb[2];
+      if (ks < DV / 16)
+        pacc = mfma(*reinterpret_cast<const f16x8_t*>(dOp + l32 * DOP_LD + 16 * ks + 8 * hb), vb_[ks], pacc);
+    }
+  };
+  // every (query, key) pair of the tile is visible to this wave's 32 keys
+  const int key_last = kb + wave * 32 + 31;
+  // P and dS; element e is query row rho = 8 (e/4) + 4 hb + e%4
+  auto pds = [&](int qt, const f32x16_t& sacc, const f32x16_t& pacc, f16x8_t* pb, f16x8_t* sb)
+      __attribute__((always_inline)) {
+    const float* lsd = reinterpret_cast<const float*>(stage(qt) + KV_LSD0 * 8);
+    const int q0 = qt * 32;
+    const bool full =
+        key_last < f.s_vis && q0 + 31 < f.Sq && (!f.causal || f.kv_pos0 + key_last <= f.q_pos0 + q0);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
-      const int i = qt * 32 + perm32(rho);
+      const int i = q0 + perm32(rho);
       const float lse = lsd[rho], dd = lsd[32 + rho];
-      const bool vis = key < f.s_vis && i < f.Sq && lse != -INFINITY &&
-                       (!f.causal || f.kv_pos0 + key <= f.q_pos0 + i);
+      const bool vis = full || (key < f.s_vis && i < f.Sq && lse != -INFINITY &&
+                                (!f.causal || f.kv_pos0 + key <= f.q_pos0 + i));
       const float p = vis ? fast_exp2(sacc[e] * c2 - lse * MLA_LOG2E) : 0.f;
       const float ds = p * (pacc[e] - dd);
       pb[e >> 3][e & 7] = (f16)p;
       sb[e >> 3][e & 7] = (f16)ds;
     }
-    // dV^T += dO^T P,  dK^T += Q^T dS  (k-slots: queries 16u + 8hb .. in natural order)
+  };
+  // dV^T += dO^T P,  dK^T += Q^T dS  (k-slots: queries 16u + 8hb .. in natural order)
+  auto dvdk = [&](int qt, const f16x8_t* pb, const f16x8_t* sb) __attribute__((always_inline)) {
+    const uint16_t* QT = stage(qt) + KV_QT0 * 8;
+    const uint16_t* dOT = stage(qt) + KV_DOT0 * 8;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -334,9 +365,23 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
         dkt[db] = mfma(*reinterpret_cast<const f16x8_t*>(QT + (db * 32 + l32) * QT_LD + 16 * u + 8 * hb), sb[u],
                        dkt[db]);
     }
-    __syncthreads();                                     // stage s is no longer read
-    if (qt + 1 < nqt) store_tile(s ^ 1);
-    __syncthreads();
+  };
+
+  f32x16_t sacc, pacc;
+  if (qt0 < nqt) issue_tile(qt0);
+  if (qt0 + 1 < nqt) issue_tile(qt0 + 1);
+  if (qt0 + 1 < nqt) wait_vmcnt<KV_IPW>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  if (qt0 < nqt) sdp(qt0, sacc, pacc);
+  for (int qt = qt0; qt < nqt; ++qt) {
+    wait_vmcnt<0>();                                     // this wave's copies of tile qt + 1 have landed
+    __syncthreads();                                     // ... everyone's; the stage of tile qt - 1 is free
+    if (qt + 2 < nqt) issue_tile(qt + 2);
+    f16x8_t pb[2], sb[2];
+    pds(qt, sacc, pacc, pb, sb);
+    dvdk(qt, pb, sb);
+    if (qt + 1 < nqt) sdp(qt + 1, sacc, pacc);
   }
 
   // ---- epilogue: dKV (fp16, both layouts) and the key-band gradient -------
@@ -674,6 +719,7 @@ size_t mfma_backward_workspace(const ExplicitArgs& f, MfmaBwdWorkspace* w, char*
   p = take(2 * B * H * sq_pad * DV);           if (w) w->dof = reinterpret_cast<uint16_t*>(p);
   p = take(2 * B * H * DV * sq_pad);           if (w) w->doft = reinterpret_cast<uint16_t*>(p);
   p = take(4 * B * H * sq_pad);                if (w) w->dvec = reinterpret_cast<float*>(p);
+  p = take(4 * B * H * sq_pad * 2);            if (w) w->lsdt = reinterpret_cast<float*>(p);
   p = take(2 * B * H * sp * DV);               if (w) w->vrow = reinterpret_cast<uint16_t*>(p);
   p = take(2 * B * H * DN * sp);               if (w) w->knt = reinterpret_cast<uint16_t*>(p);
   p = take(2 * B * DR * sp);                   if (w) w->krt = reinterpret_cast<uint16_t*>(p);
@@ -715,10 +761,10 @@ hipError_t launch_bwd_prep(const BackwardArgs& a, const MfmaBwdWorkspace& w, hip
   if (w.sq_pad > 0) {
     if (f.out_dt == MLA_BF16)
       hipLaunchKernelGGL(prep_q_kernel<MLA_BF16>, dim3(w.sq_pad / 32, H, B), dim3(256), 0, s, a, w.qtab, w.qf, w.qft,
-                         w.dof, w.doft, w.dvec, w.sq_pad);
+                         w.dof, w.doft, w.dvec, w.lsdt, w.sq_pad);
     else
       hipLaunchKernelGGL(prep_q_kernel<MLA_FP32>, dim3(w.sq_pad / 32, H, B), dim3(256), 0, s, a, w.qtab, w.qf, w.qft,
-                         w.dof, w.doft, w.dvec, w.sq_pad);
+                         w.dof, w.doft, w.dvec, w.lsdt, w.sq_pad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // V rows: vt[bh][d][key] -> vrow[bh][key][d]
@@ -743,7 +789,7 @@ hipError_t launch_bwd_kv(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipSt
   const ExplicitArgs& f = a.f;
   if (f.s_pad == 0) return hipSuccess;
   const int n_kb = f.s_pad / 128;
-  hipLaunchKernelGGL(kv_kernel, dim3(f.B * f.H * n_kb), dim3(256), 0, s, a, w.qf, w.qft, w.dof, w.doft, w.dvec, w.kn,
+  hipLaunchKernelGGL(kv_kernel, dim3(f.B * f.H * n_kb), dim3(256), 0, s, a, w.qf, w.qft, w.dof, w.doft, w.lsdt, w.kn,
                      w.vt, w.krot, w.dkv, w.dkvt, w.dkr, w.sq_pad, n_kb);
   return hipGetLastError();
 }
