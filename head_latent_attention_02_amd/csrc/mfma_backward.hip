@@ -426,20 +426,32 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
 }
 
 // -------------------------------------------------------------------- dq --
-// LDS stage of one 32-key tile: Kp [32][192+8] and Vp [32][128+8] in permuted
-// key order, KT [192][32+8] in natural key order.
-constexpr int KP_LD = DQK + 8, VP_LD = DV + 8, KT_LD = 40;
-constexpr int DQ_STAGE_H = 32 * KP_LD + 32 * VP_LD + DQK * KT_LD;
-constexpr int DQ_CHUNKS = 32 * (DQK / 8) + 32 * (DV / 8) + DQK * 4;                 // 2048
-constexpr int DQ_PER_THREAD = DQ_CHUNKS / 256;                                      // 8
-static_assert(DQ_CHUNKS % 256 == 0, "tile pieces must split evenly");
+// LDS stage of one 32-key tile, in 16-byte chunks (rows padded against bank
+// conflicts; each part starts at a multiple of 64 chunks and comes from one
+// buffer, so one buffer->LDS copy instruction never spans two parts):
+//   Kn  [32][128+8] fp16, rows in permuted key order   chunks    0 ..  543 (576)
+//   Kr  [32][64+8]  fp16 (rotated band), permuted       chunks  576 ..  863 (896)
+//   Vp  [32][128+8] fp16, permuted                       chunks  896 .. 1439 (1472)
+//   KTn [128][32+8] fp16 (K_nope^T, natural key order)   chunks 1472 .. 2111
+//   KTr [64][32+8]  fp16 (band^T)                        chunks 2112 .. 2431 (2560)
+// Padding chunks are filled with a copy of some chunk of the same part.
+constexpr int KN_LD = DN + 8, KR_LD = DR + 8, VP_LD = DV + 8, KT_LD = 40;
+constexpr int DQ_KN0 = 0, DQ_KR0 = 576, DQ_VP0 = 896, DQ_KTN0 = 1472, DQ_KTR0 = 2112, DQ_END = 2432, DQ_CH = 2560;
+constexpr int DQ_STAGE_B = DQ_CH * 16;
+constexpr int DQ_IPW = DQ_CH / 64 / 4;        // copy instructions per wave (10)
+constexpr int DQ_NST = 3;
+static_assert(DQ_KN0 + 32 * KN_LD / 8 <= DQ_KR0 && DQ_KR0 + 32 * KR_LD / 8 <= DQ_VP0 &&
+              DQ_VP0 + 32 * VP_LD / 8 <= DQ_KTN0 && DQ_KTN0 + DN * KT_LD / 8 <= DQ_KTR0 &&
+              DQ_KTR0 + DR * KT_LD / 8 <= DQ_END && DQ_END <= DQ_CH, "stage parts");
+static_assert(DQ_KR0 % 64 == 0 && DQ_VP0 % 64 == 0 && DQ_KTN0 % 64 == 0 && DQ_KTR0 % 64 == 0 && DQ_END % 64 == 0,
+              "part alignment");
 
 __global__ void __launch_bounds__(256)
 dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __restrict__ dof,
           const float* __restrict__ dvec, const uint16_t* __restrict__ kn, const uint16_t* __restrict__ krot,
           const uint16_t* __restrict__ vrow, const uint16_t* __restrict__ knt, const uint16_t* __restrict__ krt,
           const float2* __restrict__ qtab, int sq_pad, int n_qb) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem_dq[2 * DQ_STAGE_H * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t smem_dq[DQ_NST * DQ_STAGE_B];
   const ExplicitArgs& f = a.f;
   // longest first: the last query block sees the most keys
   const int qbi = n_qb - 1 - (int)(blockIdx.x % n_qb), bhi = blockIdx.x / n_qb;
@@ -459,6 +471,9 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
     ob_[ks] = *reinterpret_cast<const f16x8_t*>(dof + (bh * sq_pad + i) * DV + 16 * ks + 8 * hb);
   const float lse = (i < f.Sq) ? a.lse[bh * f.Sq + i] : -INFINITY;
   const float dd = dvec[bh * sq_pad + i];
+  // these loads are done before the first copies go out, so the copy waits
+  // below count copies only
+  wait_vmcnt<0>();
 
   // key tiles visible to the block's last query
   int kend = f.s_vis;
@@ -468,77 +483,110 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
     kend = (int)max((int64_t)0, min(lim, (int64_t)f.s_vis));
   }
   const int nkt = (kend + 31) / 32;
+  // keys [0, kfull) are visible to every query of this wave
+  int kfull = f.s_vis;
+  if (f.causal) {
+    const int64_t lim = f.q_pos0 + (qbi * 128 + wave * 32) - f.kv_pos0 + 1;
+    kfull = (int)max((int64_t)0, min(lim, (int64_t)f.s_vis));
+  }
+  const bool wave_rows_live = qbi * 128 + wave * 32 + 31 < f.Sq;
+
+  // ---- tile copies: instruction n = DQ_IPW * wave + i fills chunks 64n .. 64n+63
+  const uint32_t sp = (uint32_t)f.s_pad;
+  const i32x4_t rs_kn = make_rsrc_uniform(kn + bh * f.s_pad * DN, sp * DN * 2);
+  const i32x4_t rs_kr = make_rsrc_uniform(krot + (int64_t)b * f.s_pad * DR, sp * DR * 2);
+  const i32x4_t rs_vp = make_rsrc_uniform(vrow + bh * f.s_pad * DV, sp * DV * 2);
+  const i32x4_t rs_ktn = make_rsrc_uniform(knt + bh * DN * f.s_pad, sp * DN * 2);
+  const i32x4_t rs_ktr = make_rsrc_uniform(krt + (int64_t)b * DR * f.s_pad, sp * DR * 2);
+  int voff[DQ_IPW];
+#pragma unroll
+  for (int k = 0; k < DQ_IPW; ++k) {
+    const int pch = 64 * (DQ_IPW * wave + k) + lane;
+    int o;
+    if (pch < DQ_KR0) {
+      int rho = pch / (KN_LD / 8), c = pch % (KN_LD / 8);
+      if (rho >= 32 || c >= DN / 8) rho = c = 0;
+      o = (perm32(rho) * DN + 8 * c) * 2;
+    } else if (pch < DQ_VP0) {
+      const int p2 = pch - DQ_KR0;
+      int rho = p2 / (KR_LD / 8), c = p2 % (KR_LD / 8);
+      if (rho >= 32 || c >= DR / 8) rho = c = 0;
+      o = (perm32(rho) * DR + 8 * c) * 2;
+    } else if (pch < DQ_KTN0) {
+      const int p2 = pch - DQ_VP0;
+      int rho = p2 / (VP_LD / 8), c = p2 % (VP_LD / 8);
+      if (rho >= 32 || c >= DV / 8) rho = c = 0;
+      o = (perm32(rho) * DV + 8 * c) * 2;
+    } else if (pch < DQ_END) {
+      const int p2 = pch - (pch < DQ_KTR0 ? DQ_KTN0 : DQ_KTR0);
+      int d = p2 / (KT_LD / 8), c = p2 % (KT_LD / 8);
+      if (c >= 4) c = 0;
+      o = (d * f.s_pad + 8 * c) * 2;
+    } else {
+      o = 0;                                             // past the last part: a dummy copy
+    }
+    voff[k] = o;
+  }
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&smem_dq[0];
+  auto issue_w = [&](auto wc, int kt) __attribute__((always_inline)) {
+    constexpr int W = decltype(wc)::value;
+    const uint32_t st = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)((kt % DQ_NST) * DQ_STAGE_B));
+    static_for<DQ_IPW>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value, c0 = 64 * (DQ_IPW * W + k);
+      constexpr int part = c0 < DQ_KR0 ? 0 : c0 < DQ_VP0 ? 1 : c0 < DQ_KTN0 ? 2 : c0 < DQ_KTR0 ? 3 : 4;
+      // rows of the first three parts are keys (row bytes 256 / 128 / 256);
+      // rows of the transposed parts are features, 32 keys = 64 bytes along
+      const i32x4_t& rs = part == 0 ? rs_kn : part == 1 ? rs_kr : part == 2 ? rs_vp : part == 3 ? rs_ktn : rs_ktr;
+      const int so = part == 0 ? kt * 32 * DN * 2 : part == 1 ? kt * 32 * DR * 2 : part == 2 ? kt * 32 * DV * 2
+                                                                                              : kt * 64;
+      lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[k], __builtin_amdgcn_readfirstlane(so));
+    });
+  };
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue_tile = [&](int kt) __attribute__((always_inline)) {
+    if (wave_u == 0) issue_w(std::integral_constant<int, 0>{}, kt);
+    else if (wave_u == 1) issue_w(std::integral_constant<int, 1>{}, kt);
+    else if (wave_u == 2) issue_w(std::integral_constant<int, 2>{}, kt);
+    else issue_w(std::integral_constant<int, 3>{}, kt);
+  };
 
   f32x16_t dqt[DQK / 32];
 #pragma unroll
   for (int d = 0; d < DQK / 32; ++d) dqt[d] = f32x16_t{};
 
-  u32x4_t stg[DQ_PER_THREAD];
-  auto load_tile = [&](int kt) __attribute__((always_inline)) {
-    const int k0 = kt * 32;
-#pragma unroll
-    for (int k = 0; k < DQ_PER_THREAD; ++k) {
-      const int c = tid + 256 * k;
-      const uint16_t* src;
-      if (c < 768) {                                     // Kp: row rho <- key perm(rho)
-        const int rho = c / 24, cc = c % 24, j = k0 + perm32(rho);
-        src = cc < 16 ? kn + (bh * f.s_pad + j) * DN + cc * 8 : krot + ((int64_t)b * f.s_pad + j) * DR + (cc - 16) * 8;
-      } else if (c < 1280) {                             // Vp
-        const int c2_ = c - 768, rho = c2_ / 16, cc = c2_ % 16;
-        src = vrow + (bh * f.s_pad + k0 + perm32(rho)) * DV + cc * 8;
-      } else {                                           // KT: row d, 8 keys
-        const int c2_ = c - 1280, d = c2_ >> 2, k8 = (c2_ & 3) * 8;
-        src = d < DN ? knt + (bh * DN + d) * f.s_pad + k0 + k8 : krt + ((int64_t)b * DR + d - DN) * f.s_pad + k0 + k8;
-      }
-      stg[k] = *reinterpret_cast<const u32x4_t*>(src);
-    }
-  };
-  auto store_tile = [&](int s) __attribute__((always_inline)) {
-    uint16_t* st = reinterpret_cast<uint16_t*>(smem_dq) + s * DQ_STAGE_H;
-#pragma unroll
-    for (int k = 0; k < DQ_PER_THREAD; ++k) {
-      const int c = tid + 256 * k;
-      uint16_t* dst;
-      if (c < 768) {
-        const int rho = c / 24, cc = c % 24;
-        dst = st + rho * KP_LD + cc * 8;
-      } else if (c < 1280) {
-        const int c2_ = c - 768, rho = c2_ / 16, cc = c2_ % 16;
-        dst = st + 32 * KP_LD + rho * VP_LD + cc * 8;
-      } else {
-        const int c2_ = c - 1280, d = c2_ >> 2, k8 = (c2_ & 3) * 8;
-        dst = st + 32 * KP_LD + 32 * VP_LD + d * KT_LD + k8;
-      }
-      *reinterpret_cast<u32x4_t*>(dst) = stg[k];
-    }
-  };
-
-  if (nkt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  // Tile kt sits in stage kt % 3; tile kt + 2 is copied at the top of
+  // iteration kt into the stage last read in iteration kt - 1.
+  if (nkt > 0) issue_tile(0);
+  if (nkt > 1) issue_tile(1);
   for (int kt = 0; kt < nkt; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nkt) load_tile(kt + 1);
-    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem_dq) + s * DQ_STAGE_H;
-    const uint16_t* Kp = st;
-    const uint16_t* Vp = st + 32 * KP_LD;
-    const uint16_t* KT = Vp + 32 * VP_LD;
-    // S^T = Kp Q^T, dP^T = Vp dO^T  (rows: permuted keys, columns: queries)
+    if (kt + 1 < nkt) wait_vmcnt<DQ_IPW>();             // this wave's copies of tile kt have landed
+    else wait_vmcnt<0>();
+    __syncthreads();                                     // ... everyone's; the stage of tile kt - 1 is free
+    if (kt + 2 < nkt) issue_tile(kt + 2);
+    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem_dq + (kt % DQ_NST) * DQ_STAGE_B);
+    const uint16_t* Kn = st + DQ_KN0 * 8;
+    const uint16_t* Kr = st + DQ_KR0 * 8;
+    const uint16_t* Vp = st + DQ_VP0 * 8;
+    const uint16_t* KTn = st + DQ_KTN0 * 8;
+    const uint16_t* KTr = st + DQ_KTR0 * 8;
+    // S^T = K Q^T, dP^T = V dO^T  (rows: permuted keys, columns: queries)
     f32x16_t sacc = {}, pacc = {};
 #pragma unroll
-    for (int ks = 0; ks < DQK / 16; ++ks)
-      sacc = mfma(*reinterpret_cast<const f16x8_t*>(Kp + l32 * KP_LD + 16 * ks + 8 * hb), qb_[ks], sacc);
+    for (int ks = 0; ks < DQK / 16; ++ks) {
+      const uint16_t* ap = ks < DN / 16 ? Kn + l32 * KN_LD + 16 * ks : Kr + l32 * KR_LD + 16 * (ks - DN / 16);
+      sacc = mfma(*reinterpret_cast<const f16x8_t*>(ap + 8 * hb), qb_[ks], sacc);
+    }
 #pragma unroll
     for (int ks = 0; ks < DV / 16; ++ks)
       pacc = mfma(*reinterpret_cast<const f16x8_t*>(Vp + l32 * VP_LD + 16 * ks + 8 * hb), ob_[ks], pacc);
+    const bool full = wave_rows_live && kt * 32 + 32 <= kfull;
     f16x8_t sb[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
       const int j = kt * 32 + perm32(rho);
-      const bool vis = j < f.s_vis && i < f.Sq && lse != -INFINITY && (!f.causal || f.kv_pos0 + j <= f.q_pos0 + i);
+      const bool vis =
+          full || (j < f.s_vis && i < f.Sq && lse != -INFINITY && (!f.causal || f.kv_pos0 + j <= f.q_pos0 + i));
       const float p = vis ? fast_exp2(sacc[e] * c2 - lse * MLA_LOG2E) : 0.f;
       sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - dd));
     }
@@ -546,12 +594,10 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int db = 0; db < DQK / 32; ++db)
-        dqt[db] = mfma(*reinterpret_cast<const f16x8_t*>(KT + (db * 32 + l32) * KT_LD + 16 * u + 8 * hb), sb[u],
-                       dqt[db]);
-    __syncthreads();
-    if (kt + 1 < nkt) store_tile(s ^ 1);
-    __syncthreads();
+      for (int db = 0; db < DQK / 32; ++db) {
+        const uint16_t* ap = db < DN / 32 ? KTn + (db * 32 + l32) * KT_LD : KTr + ((db - DN / 32) * 32 + l32) * KT_LD;
+        dqt[db] = mfma(*reinterpret_cast<const f16x8_t*>(ap + 16 * u + 8 * hb), sb[u], dqt[db]);
+      }
   }
 
   // ---- epilogue: dq_nope, and dq_pe rotated back by the negative angle ----
