@@ -554,31 +554,45 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
 #pragma unroll
   for (int d = 0; d < DQK / 32; ++d) dqt[d] = f32x16_t{};
 
-  // Tile kt sits in stage kt % 3; tile kt + 2 is copied at the top of
+  // Tile kt sits in stage kt % 3.  Iteration kt computes dS of tile kt (its
+  // S^T and dP^T were computed at the end of the previous iteration) and
+  // dQ^T, then S^T and dP^T of tile kt + 1, so that the two MFMA runs follow
+  // each other without a dependency; tile kt + 2 is copied at the top of
   // iteration kt into the stage last read in iteration kt - 1.
-  if (nkt > 0) issue_tile(0);
-  if (nkt > 1) issue_tile(1);
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) wait_vmcnt<DQ_IPW>();             // this wave's copies of tile kt have landed
-    else wait_vmcnt<0>();
-    __syncthreads();                                     // ... everyone's; the stage of tile kt - 1 is free
-    if (kt + 2 < nkt) issue_tile(kt + 2);
-    const uint16_t* st = reinterpret_cast<const uint16_t*>(smem_dq + (kt % DQ_NST) * DQ_STAGE_B);
+  auto stage_p = [&](int kt) __attribute__((always_inline)) {
+    return reinterpret_cast<const uint16_t*>(smem_dq + (kt % DQ_NST) * DQ_STAGE_B);
+  };
+  // S^T = K Q^T, dP^T = V dO^T  (rows: permuted keys, columns: queries)
+  auto sdp = [&](int kt, f32x16_t& sacc, f32x16_t& pacc) __attribute__((always_inline)) {
+    const uint16_t* st = stage_p(kt);
     const uint16_t* Kn = st + DQ_KN0 * 8;
     const uint16_t* Kr = st + DQ_KR0 * 8;
     const uint16_t* Vp = st + DQ_VP0 * 8;
-    const uint16_t* KTn = st + DQ_KTN0 * 8;
-    const uint16_t* KTr = st + DQ_KTR0 * 8;
-    // S^T = K Q^T, dP^T = V dO^T  (rows: permuted keys, columns: queries)
-    f32x16_t sacc = {}, pacc = {};
+    sacc = f32x16_t{};
+    pacc = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks) {
       const uint16_t* ap = ks < DN / 16 ? Kn + l32 * KN_LD + 16 * ks : Kr + l32 * KR_LD + 16 * (ks - DN / 16);
       sacc = mfma(*reinterpret_cast<const f16x8_t*>(ap + 8 * hb), qb_[ks], sacc);
+      if (ks < DV / 16)
+        pacc = mfma(*reinterpret_cast<const f16x8_t*>(Vp + l32 * VP_LD + 16 * ks + 8 * hb), ob_[ks], pacc);
     }
-#pragma unroll
-    for (int ks = 0; ks < DV / 16; ++ks)
-      pacc = mfma(*reinterpret_cast<const f16x8_t*>(Vp + l32 * VP_LD + 16 * ks + 8 * hb), ob_[ks], pacc);
+  };
+
+  f32x16_t sacc, pacc;
+  if (nkt > 0) issue_tile(0);
+  if (nkt > 1) issue_tile(1);
+  if (nkt > 1) wait_vmcnt<DQ_IPW>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  if (nkt > 0) sdp(0, sacc, pacc);
+  for (int kt = 0; kt < nkt; ++kt) {
+    wait_vmcnt<0>();                                     // this wave's copies of tile kt + 1 have landed
+    __syncthreads();                                     // ... everyone's; the stage of tile kt - 1 is free
+    if (kt + 2 < nkt) issue_tile(kt + 2);
+    const uint16_t* st = stage_p(kt);
+    const uint16_t* KTn = st + DQ_KTN0 * 8;
+    const uint16_t* KTr = st + DQ_KTR0 * 8;
     const bool full = wave_rows_live && kt * 32 + 32 <= kfull;
     f16x8_t sb[2];
 #pragma unroll
@@ -598,6 +612,7 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
         const uint16_t* ap = db < DN / 32 ? KTn + (db * 32 + l32) * KT_LD : KTr + ((db - DN / 32) * 32 + l32) * KT_LD;
         dqt[db] = mfma(*reinterpret_cast<const f16x8_t*>(ap + 16 * u + 8 * hb), sb[u], dqt[db]);
       }
+    if (kt + 1 < nkt) sdp(kt + 1, sacc, pacc);
   }
 
   // ---- epilogue: dq_nope, and dq_pe rotated back by the negative angle ----
