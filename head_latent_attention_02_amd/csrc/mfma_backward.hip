@@ -73,36 +73,100 @@ prep_q_kernel(BackwardArgs a, const float2* __restrict__ qtab, uint16_t* __restr
   const int i = i0 + r;
   const bool live = i < f.Sq;
   const int64_t row = ((int64_t)b * f.Sq + (live ? i : 0)) * f.H + h;
-  // q_nope: 16 columns per thread
-  for (int k = 0; k < DN / 8; ++k) {
-    const int d = c8 * (DN / 8) + k;
-    const float v = live ? bf16_bits_to_float(static_cast<const uint16_t*>(f.q_nope)[row * DN + d]) : 0.f;
-    Qs[r][d] = h_bits(v);
-  }
-  // rope pairs (m, m + 32): 4 pairs per thread
-  for (int k = 0; k < 4; ++k) {
-    const int m = c8 * 4 + k;
-    float lo = 0.f, hi = 0.f;
+  // q_nope: 16 columns per thread (two 16-byte loads, two 16-byte LDS stores)
+  {
+    u32x4_t v[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
     if (live) {
-      const uint16_t* qp = static_cast<const uint16_t*>(f.q_pe) + row * DR;
-      const float x0 = bf16_bits_to_float(qp[m]), x1 = bf16_bits_to_float(qp[m + 32]);
-      const float2 cs = qtab[(int64_t)i * 32 + m];
-      lo = x0 * cs.x - x1 * cs.y;
-      hi = x1 * cs.x + x0 * cs.y;
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(f.q_nope) + row * DN + c8 * 16);
+      v[0] = src[0];
+      v[1] = src[1];
     }
-    Qs[r][DN + m] = h_bits(lo);
-    Qs[r][DN + m + 32] = h_bits(hi);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      u32x4_t o;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const uint32_t x = v[hh][w2];
+        o[w2] = (uint32_t)h_bits(bf16_bits_to_float((uint16_t)(x & 0xffff))) |
+                ((uint32_t)h_bits(bf16_bits_to_float((uint16_t)(x >> 16))) << 16);
+      }
+      *reinterpret_cast<u32x4_t*>(&Qs[r][c8 * 16 + 8 * hh]) = o;
+    }
   }
-  // dO and D = dO . out
+  // rope pairs (m, m + 32), m = 4 c8 .. 4 c8 + 3: 8-byte loads of both halves
+  {
+    u32x2_t xl = {0u, 0u}, xh = {0u, 0u};
+    f32x4_t cs[2] = {f32x4_t{1.f, 0.f, 1.f, 0.f}, f32x4_t{1.f, 0.f, 1.f, 0.f}};
+    if (live) {
+      const uint16_t* qp = static_cast<const uint16_t*>(f.q_pe) + row * DR + 4 * c8;
+      xl = *reinterpret_cast<const u32x2_t*>(qp);
+      xh = *reinterpret_cast<const u32x2_t*>(qp + 32);
+      const f32x4_t* ct = reinterpret_cast<const f32x4_t*>(qtab + (int64_t)i * 32 + 4 * c8);
+      cs[0] = ct[0];
+      cs[1] = ct[1];
+    }
+    u32x2_t lo2, hi2;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float x0 = bf16_bits_to_float((uint16_t)((xl[k >> 1] >> (16 * (k & 1))) & 0xffff));
+      const float x1 = bf16_bits_to_float((uint16_t)((xh[k >> 1] >> (16 * (k & 1))) & 0xffff));
+      const float c = cs[k >> 1][2 * (k & 1)], sn = cs[k >> 1][2 * (k & 1) + 1];
+      const uint32_t lo = h_bits(live ? x0 * c - x1 * sn : 0.f), hi = h_bits(live ? x1 * c + x0 * sn : 0.f);
+      if (k & 1) {
+        lo2[k >> 1] |= lo << 16;
+        hi2[k >> 1] |= hi << 16;
+      } else {
+        lo2[k >> 1] = lo;
+        hi2[k >> 1] = hi;
+      }
+    }
+    *reinterpret_cast<u32x2_t*>(&Qs[r][DN + 4 * c8]) = lo2;
+    *reinterpret_cast<u32x2_t*>(&Qs[r][DN + 32 + 4 * c8]) = hi2;
+  }
+  // dO and D = dO . out (16 columns per thread, summed in column order)
   float dsum = 0.f;
-  for (int k = 0; k < DV / 8; ++k) {
-    const int d = c8 * (DV / 8) + k;
-    float g = 0.f;
-    if (live) {
-      g = load_elem<OT>(a.d_out, row * DV + d);
-      dsum += g * load_elem<OT>(a.out, row * DV + d);
+  {
+    float g[16], o[16];
+    if constexpr (OT == MLA_BF16) {
+      u32x4_t gv[2] = {}, ov[2] = {};
+      if (live) {
+        const u32x4_t* gs = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.d_out) + row * DV + c8 * 16);
+        const u32x4_t* os = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.out) + row * DV + c8 * 16);
+        gv[0] = gs[0]; gv[1] = gs[1];
+        ov[0] = os[0]; ov[1] = os[1];
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        g[k] = bf16_bits_to_float((uint16_t)((gv[k >> 3][(k & 7) >> 1] >> (16 * (k & 1))) & 0xffff));
+        o[k] = bf16_bits_to_float((uint16_t)((ov[k >> 3][(k & 7) >> 1] >> (16 * (k & 1))) & 0xffff));
+      }
+    } else {
+      f32x4_t gv[4] = {}, ov[4] = {};
+      if (live) {
+        const f32x4_t* gs = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.d_out) + row * DV + c8 * 16);
+        const f32x4_t* os = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.out) + row * DV + c8 * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          gv[q] = gs[q];
+          ov[q] = os[q];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        g[k] = gv[k >> 2][k & 3];
+        o[k] = ov[k >> 2][k & 3];
+      }
     }
-    Ds[r][d] = h_bits(g);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dsum += g[k] * o[k];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      u32x4_t pk;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2)
+        pk[w2] = (uint32_t)h_bits(g[8 * hh + 2 * w2]) | ((uint32_t)h_bits(g[8 * hh + 2 * w2 + 1]) << 16);
+      *reinterpret_cast<u32x4_t*>(&Ds[r][c8 * 16 + 8 * hh]) = pk;
+    }
   }
   red[r][c8] = dsum;
   __syncthreads();
