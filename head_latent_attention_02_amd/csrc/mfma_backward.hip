@@ -233,6 +233,45 @@ transpose_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out, in
   }
 }
 
+// The same with 64 x 64 tiles moved in 16-byte pieces; rows and cols must be
+// multiples of 8 (row r reads as 0 for rows_valid <= r < rows).
+template <bool IN_BF16>
+__global__ void __launch_bounds__(256)
+transpose64_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out, int rows, int rows_valid, int cols,
+                   int64_t in_ld, int64_t in_bs, int64_t out_ld, int64_t out_bs) {
+  __shared__ __attribute__((aligned(16))) uint16_t T[64][64 + 8];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64, z = blockIdx.z;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + 256 * k, rr = q >> 3, cc = (q & 7) * 8;     // row rr, columns cc .. cc+7 of the tile
+    const int r = r0 + rr, c = c0 + cc;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < rows_valid && c < cols) {
+      v = *reinterpret_cast<const u32x4_t*>(in + z * in_bs + (int64_t)r * in_ld + c);
+      if (IN_BF16) {
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2)
+          v[w2] = (uint32_t)h_bits(bf16_bits_to_float((uint16_t)(v[w2] & 0xffff))) |
+                  ((uint32_t)h_bits(bf16_bits_to_float((uint16_t)(v[w2] >> 16))) << 16);
+      }
+    }
+    *reinterpret_cast<u32x4_t*>(&T[rr][cc]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + 256 * k, cc = q >> 3, rr = (q & 7) * 8;     // column cc, rows rr .. rr+7 of the tile
+    const int c = c0 + cc, r = r0 + rr;
+    if (c < cols && r < rows) {
+      u32x4_t v;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) v[w2] = (uint32_t)T[rr + 2 * w2][cc] | ((uint32_t)T[rr + 2 * w2 + 1][cc] << 16);
+      *reinterpret_cast<u32x4_t*>(out + z * out_bs + (int64_t)c * out_ld + r) = v;
+    }
+  }
+}
+
 // -------------------------------------------------------------------- kv --
 // LDS stage of one 32-query tile, in 16-byte chunks.  Rows are padded so that
 // 16-byte fragment reads of 16 consecutive rows fall in distinct banks; each
@@ -863,8 +902,16 @@ template <bool IN_BF16>
 hipError_t transpose(const uint16_t* in, uint16_t* out, int rows, int rows_valid, int cols, int64_t in_ld,
                      int64_t in_bs, int64_t out_ld, int64_t out_bs, int nbatch, hipStream_t s) {
   if (rows == 0 || cols == 0 || nbatch == 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_kernel<IN_BF16>, dim3((cols + 31) / 32, (rows + 31) / 32, nbatch), dim3(256), 0, s,
-                     in, out, rows, rows_valid, cols, in_ld, in_bs, out_ld, out_bs);
+  // 16-byte pieces need 8-element multiples and 16-byte aligned rows
+  const bool wide = rows % 8 == 0 && cols % 8 == 0 && in_ld % 8 == 0 && in_bs % 8 == 0 && out_ld % 8 == 0 &&
+                    out_bs % 8 == 0 && reinterpret_cast<uintptr_t>(in) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(out) % 16 == 0;
+  if (wide)
+    hipLaunchKernelGGL(transpose64_kernel<IN_BF16>, dim3((cols + 63) / 64, (rows + 63) / 64, nbatch), dim3(256), 0, s,
+                       in, out, rows, rows_valid, cols, in_ld, in_bs, out_ld, out_bs);
+  else
+    hipLaunchKernelGGL(transpose_kernel<IN_BF16>, dim3((cols + 31) / 32, (rows + 31) / 32, nbatch), dim3(256), 0, s,
+                       in, out, rows, rows_valid, cols, in_ld, in_bs, out_ld, out_bs);
   return hipGetLastError();
 }
 
