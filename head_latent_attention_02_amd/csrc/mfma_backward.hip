@@ -433,24 +433,40 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
   };
   // every (query, key) pair of the tile is visible to this wave's 32 keys
   const int key_last = kb + wave * 32 + 31;
-  // P and dS; element e is query row rho = 8 (e/4) + 4 hb + e%4
+  // P and dS; element e is query row rho = 8 (e/4) + 4 hb + e%4.  Branch free:
+  // a masked pair gets the exponent -inf, so exp2 gives 0.  Key j is visible to
+  // query i iff j - i <= q_pos0 - kv_pos0 (clamped: |j - i| < 2^30).
+  const int dpos = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), f.q_pos0 - f.kv_pos0));
   auto pds = [&](int qt, const f32x16_t& sacc, const f32x16_t& pacc, f16x8_t* pb, f16x8_t* sb)
       __attribute__((always_inline)) {
     const float* lsd = reinterpret_cast<const float*>(stage(qt) + KV_LSD0 * 8);
     const int q0 = qt * 32;
-    const bool full =
-        key_last < f.s_vis && q0 + 31 < f.Sq && (!f.causal || f.kv_pos0 + key_last <= f.q_pos0 + q0);
+    const bool full = key_last < f.s_vis && q0 + 31 < f.Sq && (!f.causal || key_last - q0 <= dpos);
+    f32x4_t l4[4], d4[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
-      const int i = q0 + perm32(rho);
-      const float lse = lsd[rho], dd = lsd[32 + rho];
-      const bool vis = full || (key < f.s_vis && i < f.Sq && lse != -INFINITY &&
-                                (!f.causal || f.kv_pos0 + key <= f.q_pos0 + i));
-      const float p = vis ? fast_exp2(sacc[e] * c2 - lse * MLA_LOG2E) : 0.f;
-      const float ds = p * (pacc[e] - dd);
-      pb[e >> 3][e & 7] = (f16)p;
-      sb[e >> 3][e & 7] = (f16)ds;
+    for (int g = 0; g < 4; ++g) {
+      l4[g] = *reinterpret_cast<const f32x4_t*>(lsd + 8 * g + 4 * hb);
+      d4[g] = *reinterpret_cast<const f32x4_t*>(lsd + 32 + 8 * g + 4 * hb);
+    }
+    if (__builtin_amdgcn_readfirstlane((int)full)) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(sacc[e] * c2 - l4[e >> 2][e & 3] * MLA_LOG2E);
+        pb[e >> 3][e & 7] = (f16)p;
+        sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - d4[e >> 2][e & 3]));
+      }
+    } else {
+      const bool key_ok = key < f.s_vis;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
+        const int i = q0 + perm32(rho);
+        const bool vis = key_ok & (i < f.Sq) & (!f.causal | (key - i <= dpos));
+        const float x = sacc[e] * c2 - l4[e >> 2][e & 3] * MLA_LOG2E;
+        const float p = fast_exp2(vis ? x : -INFINITY);
+        pb[e >> 3][e & 7] = (f16)p;
+        sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - d4[e >> 2][e & 3]));
+      }
     }
   };
   // dV^T += dO^T P,  dK^T += Q^T dS  (k-slots: queries 16u + 8hb .. in natural order)
@@ -574,6 +590,11 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
     ob_[ks] = *reinterpret_cast<const f16x8_t*>(dof + (bh * sq_pad + i) * DV + 16 * ks + 8 * hb);
   const float lse = (i < f.Sq) ? a.lse[bh * f.Sq + i] : -INFINITY;
   const float dd = dvec[bh * sq_pad + i];
+  // a row with an infinite LSE sees no key; its P is 0 through row_ok
+  const bool row_ok = i < f.Sq && lse != -INFINITY;
+  const float lse_l2 = row_ok ? lse * MLA_LOG2E : 0.f;
+  // key j is visible to query i iff j - i <= q_pos0 - kv_pos0 (clamped: |j - i| < 2^30)
+  const int dpos = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), f.q_pos0 - f.kv_pos0));
   // these loads are done before the first copies go out, so the copy waits
   // below count copies only
   wait_vmcnt<0>();
@@ -698,14 +719,22 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
     const uint16_t* KTr = st + DQ_KTR0 * 8;
     const bool full = wave_rows_live && kt * 32 + 32 <= kfull;
     f16x8_t sb[2];
+    if (__builtin_amdgcn_readfirstlane((int)full)) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
-      const int j = kt * 32 + perm32(rho);
-      const bool vis =
-          full || (j < f.s_vis && i < f.Sq && lse != -INFINITY && (!f.causal || f.kv_pos0 + j <= f.q_pos0 + i));
-      const float p = vis ? fast_exp2(sacc[e] * c2 - lse * MLA_LOG2E) : 0.f;
-      sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - dd));
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(sacc[e] * c2 - lse_l2);
+        sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - dd));
+      }
+    } else {
+      // branch free: a masked pair gets the exponent -inf, so exp2 gives 0
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
+        const int j = kt * 32 + perm32(rho);
+        const bool vis = row_ok & (j < f.s_vis) & (!f.causal | (j - i <= dpos));
+        const float p = fast_exp2(vis ? sacc[e] * c2 - lse_l2 : -INFINITY);
+        sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - dd));
+      }
     }
     // dQ^T += K^T dS^T  (k-slots: keys 16u + 8hb .. in natural order)
 #pragma unroll
