@@ -808,42 +808,51 @@ template <int BM>
 __global__ void __launch_bounds__(256)
 gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ C, int M,
                int M_store, int N, int K, int64_t ldc, int64_t c_row_map_div, int64_t c_row_map_stride) {
-  constexpr int BN = 128, BK = 32, LD = 40;
+  constexpr int BN = 128, BK = 32, LD = 40;          // LDS row: BK fp16 plus one padding chunk
   constexpr int WM = BM / 2, WN = 64;               // per-wave tile
   constexpr int FM = WM / 32, FN = WN / 32;         // 32x32 blocks per wave
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LD];
+  constexpr int NST = 4;                            // LDS stages
+  // stage: A rows then B rows, 16-byte chunks; whole copy instructions for 4 waves
+  constexpr int A_CH = BM * LD / 8, B_CH = BN * LD / 8;
+  constexpr int ST_CH = (A_CH + B_CH + 255) / 256 * 256;
+  constexpr int IPW = ST_CH / 64 / 4;               // copy instructions per wave per step
+  static_assert(A_CH % 64 == 0 && B_CH % 64 == 0, "parts on instruction boundaries");
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[NST * ST_CH * 8];
   const int n_tn = N / BN;
   const int tm = blockIdx.x / n_tn, tn = blockIdx.x % n_tn;
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hb = lane >> 5;
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
-  constexpr int A_PER = BM * BK / 8 / 256, B_PER = BN * BK / 8 / 256;   // 16-byte pieces per thread
-  u32x4_t ra[A_PER], rb[B_PER];
-  auto load = [&](int k0) __attribute__((always_inline)) {
+  // copies: chunk p of a stage is row p / 5 (A rows, then B rows), column
+  // chunk p % 5 (chunk 4 is padding: a second copy of chunk 0)
+  const i32x4_t rs_a = make_rsrc_uniform(A + (int64_t)m0 * K, (uint32_t)BM * K * 2);
+  const i32x4_t rs_b = make_rsrc_uniform(B + (int64_t)n0 * K, (uint32_t)BN * K * 2);
+  int voff[IPW];
 #pragma unroll
-    for (int p = 0; p < A_PER; ++p) {
-      const int c = tid + 256 * p, r = c >> 2, q = (c & 3) * 8;
-      ra[p] = *reinterpret_cast<const u32x4_t*>(A + (int64_t)(m0 + r) * K + k0 + q);
-    }
-#pragma unroll
-    for (int p = 0; p < B_PER; ++p) {
-      const int c = tid + 256 * p, r = c >> 2, q = (c & 3) * 8;
-      rb[p] = *reinterpret_cast<const u32x4_t*>(B + (int64_t)(n0 + r) * K + k0 + q);
-    }
+  for (int k = 0; k < IPW; ++k) {
+    int p = 64 * (IPW * wave + k) + lane;
+    if (p >= A_CH) p -= A_CH;                       // B rows (or a dummy copy past them)
+    int r = p / (LD / 8), c = p % (LD / 8);
+    if (c >= BK / 8 || r >= BN) r = c = 0;
+    voff[k] = (r * K + 8 * c) * 2;
+  }
+  const uint32_t ls_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&Ls[0];
+  auto issue_w = [&](auto wc, int g) __attribute__((always_inline)) {
+    constexpr int W = decltype(wc)::value;
+    const uint32_t st = __builtin_amdgcn_readfirstlane(ls_lds + (uint32_t)((g % NST) * ST_CH * 16));
+    static_for<IPW>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value, c0 = 64 * (IPW * W + k);
+      const i32x4_t& rs = c0 < A_CH ? rs_a : rs_b;
+      lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[k], __builtin_amdgcn_readfirstlane(g * BK * 2));
+    });
   };
-  auto store = [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-    for (int p = 0; p < A_PER; ++p) {
-      const int c = tid + 256 * p, r = c >> 2, q = (c & 3) * 8;
-      *reinterpret_cast<u32x4_t*>(&As[s][r * LD + q]) = ra[p];
-    }
-#pragma unroll
-    for (int p = 0; p < B_PER; ++p) {
-      const int c = tid + 256 * p, r = c >> 2, q = (c & 3) * 8;
-      *reinterpret_cast<u32x4_t*>(&Bs[s][r * LD + q]) = rb[p];
-    }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int g) __attribute__((always_inline)) {
+    if (wave_u == 0) issue_w(std::integral_constant<int, 0>{}, g);
+    else if (wave_u == 1) issue_w(std::integral_constant<int, 1>{}, g);
+    else if (wave_u == 2) issue_w(std::integral_constant<int, 2>{}, g);
+    else issue_w(std::integral_constant<int, 3>{}, g);
   };
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -851,29 +860,31 @@ gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, f
 #pragma unroll
     for (int y = 0; y < FN; ++y) acc[x][y] = f32x16_t{};
   const int nk = K / BK;
-  load(0);
-  store(0);
-  __syncthreads();
+  for (int g = 0; g < NST - 1 && g < nk; ++g) issue(g);
   for (int kk = 0; kk < nk; ++kk) {
-    const int s = kk & 1;
-    if (kk + 1 < nk) load((kk + 1) * BK);
+    // copies of step kk have landed (up to two later steps may be in flight)
+    const int newer = min(NST - 2, nk - 1 - kk);
+    if (newer == 2) wait_vmcnt<2 * IPW>();
+    else if (newer == 1) wait_vmcnt<IPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();                                 // ... for every wave; the stage of step kk - 1 is free
+    if (kk + NST - 1 < nk) issue(kk + NST - 1);
+    const uint16_t* As = Ls + (kk % NST) * ST_CH * 8;
+    const uint16_t* Bs = As + A_CH * 8;
 #pragma unroll
     for (int u = 0; u < BK / 16; ++u) {
       f16x8_t af[FM], bf[FN];
 #pragma unroll
       for (int x = 0; x < FM; ++x)
-        af[x] = *reinterpret_cast<const f16x8_t*>(&As[s][(wm + 32 * x + l32) * LD + 16 * u + 8 * hb]);
+        af[x] = *reinterpret_cast<const f16x8_t*>(&As[(wm + 32 * x + l32) * LD + 16 * u + 8 * hb]);
 #pragma unroll
       for (int y = 0; y < FN; ++y)
-        bf[y] = *reinterpret_cast<const f16x8_t*>(&Bs[s][(wn + 32 * y + l32) * LD + 16 * u + 8 * hb]);
+        bf[y] = *reinterpret_cast<const f16x8_t*>(&Bs[(wn + 32 * y + l32) * LD + 16 * u + 8 * hb]);
 #pragma unroll
       for (int x = 0; x < FM; ++x)
 #pragma unroll
         for (int y = 0; y < FN; ++y) acc[x][y] = mfma(af[x], bf[y], acc[x][y]);
     }
-    __syncthreads();
-    if (kk + 1 < nk) store(s ^ 1);
-    __syncthreads();
   }
   // D element e of block (x, y): row wm + 32x + 8(e/4) + 4hb + e%4, column wn + 32y + l32.
   // Row m of C sits at (m / div) * stride + m % div (a batch of row blocks
