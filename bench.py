@@ -703,7 +703,8 @@ def main():
         "mfma_attention": ("TFLOP/s", fl["attention"]),
         "mfma_up_projection": ("TFLOP/s", fl["up_proj"]),
         "mfma_split_kv": ("GB/s", dbytes["cache"]),
-        "lse_combine": ("GB/s", B * dcfg.n_splits * H * (dcfg.d_kv + 1) * 4 + H * dcfg.d_v * dcfg.d_kv * 2),
+        # the fp16 partials and fp32 chunk LSEs it reads, and W_UV (bf16)
+        "lse_combine": ("GB/s", B * dcfg.n_splits * H * (dcfg.d_kv * 2 + 4) + H * dcfg.d_v * dcfg.d_kv * 2),
         "absorb": ("GB/s", H * dcfg.d_nope * dcfg.d_kv * 2 + B * H * (dcfg.d_kv + dcfg.d_rope) * 2),
     }
     kernels = {}
