@@ -19,7 +19,7 @@
 
 namespace {
 
-constexpr int CB = 8;          // sequences per block
+constexpr int CB = 16;         // sequences per block (the un-absorb MFMA's 16 columns)
 constexpr int CTHREADS = 256;
 constexpr int MAXNS = 64;      // chunk limit (checked on the host)
 constexpr int KBATCH = 16;     // chunk loads in flight per column
@@ -133,7 +133,7 @@ combine_kernel(DecodeArgs a, const float* __restrict__ lse_part, const void* __r
   if constexpr (WT == MLA_BF16) {
     if (mfma_unabsorb) {
       // On 16x16x32 bf16 MFMA: out^T[v][s] = W_UV[h][v][:] . o_lat[s][:], 16 rows
-      // v x 16 sequence columns (8 used) per product; wave w owns v-blocks 2w
+      // v x 16 sequence columns per product; wave w owns v-blocks 2w
       // and 2w+1.  A lane holds 8 consecutive latent columns of one W row (the
       // 16 lanes of a k-group read 16 rows, 64 contiguous bytes each), and the
       // fp32 o_lat enters as two bf16 terms, hi = bf16(x) and lo = bf16(x - hi),
