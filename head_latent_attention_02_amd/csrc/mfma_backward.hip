@@ -18,15 +18,21 @@
 //               zeros), and D = dO . out in fp32.
 //   transpose   V [bh][key][128] from the up-projection's V^T, K_nope^T, the
 //               rotated key band transposed, W^T and c_kv^T (fp16).
-//   kv          per (b, h, 128 keys): 4 waves of 32 keys hold K and V as MFMA
-//               B operands and stream 32-query tiles of Q, dO, Q^T, dO^T
-//               through LDS; S = Q K^T, dP = dO V^T, dV^T += dO^T P,
-//               dK^T += Q^T dS.  Writes dKV in both row and column layouts
-//               (fp16, for the two GEMMs) and the per-head key-band gradient.
+//   kv          per (b, h, 128 keys): 8 waves, two per 32-key block sharing a
+//               SIMD: one holds K and computes S = Q K^T, P and dV^T += dO^T P,
+//               the other holds V and computes dP = dO V^T, dS and
+//               dK^T += Q^T dS, P passing between them through LDS; the two
+//               alternate MFMA and vector phases in opposite order.  32-query
+//               tiles of Q, dO, Q^T, dO^T stream through LDS.  Writes dKV in
+//               both row and column layouts (fp16, for the two GEMMs) and the
+//               per-head key-band gradient.
 //   dq          per (b, h, 128 queries): 4 waves of 32 queries hold Q^T and
 //               dO^T and stream 32-key tiles of K, V and K^T; S^T = K Q^T,
 //               dP^T = V dO^T, dQ^T += K^T dS^T; writes dq_nope and the
 //               rotated-back dq_pe.
+//   Both attention kernels deal the heads over the XCDs (all blocks of a
+//   head on one XCD at once, walking the streamed tiles in the same order),
+//   so each streamed tile is fetched into that XCD's L2 once for all of them.
 //   dk_pe       the head sum of the key-band gradient, rotated back.
 //   gemm_nt     C = A B^T with A, B fp16 row-major and fp32 C: dc_kv and dW.
 //
@@ -273,274 +279,386 @@ transpose64_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out, 
 }
 
 // -------------------------------------------------------------------- kv --
-// LDS stage of one 32-query tile, in 16-byte chunks.  Rows are padded so that
-// 16-byte fragment reads of 16 consecutive rows fall in distinct banks; each
-// part starts at a multiple of 64 chunks, so one buffer->LDS copy instruction
-// (64 lanes x 16 bytes) never spans two parts:
-//   Qp  [32][192+8] fp16, rows in permuted order   chunks    0 ..  799 (832)
-//   dOp [32][128+8] fp16, rows in permuted order   chunks  832 .. 1375 (1408)
-//   QT  [192][32+8] fp16                            chunks 1408 .. 2367
-//   dOT [128][32+8] fp16                            chunks 2368 .. 3007
-//   LSE, D [32] each, fp32, permuted order          chunks 3008 .. 3023 (3072)
+// Key-parallel kernel: per (b, h, 128 keys), 8 waves; the work of each
+// 32-key block is split between two waves that share a SIMD:
+//   wave A (waves 0-3) holds K and dV^T:  S = Q K^T, P, dV^T += dO^T P
+//   wave B (waves 4-7) holds V and dK^T:  dP = dO V^T, dS = P (dP - D),
+//                                         dK^T += Q^T dS
+// P goes from A to B through LDS (fp32, lane to the same lane, since dP and S
+// share the accumulator layout).  Each wave alternates an MFMA phase and a
+// vector phase, one barrier apart, and the B waves run one phase behind the A
+// waves, so on every SIMD one wave issues MFMAs while the other does its
+// exponentials, LDS exchange and tile copies:
+//   M_A(t): dV(t) and S(t+1)       V_A(t): P(t), its copy to LDS
+//   M_B(t): dK(t) and dP(t+1)      V_B(t): P(t) from LDS, dS(t)
+// Query tiles stream through two rings of 3 stages: the early part (Q and dO
+// rows, LSE and D), copied by the A waves two tiles ahead, and the late part
+// (Q^T, dO^T), copied by the B waves two tiles ahead (the late part of a
+// tile is read one tile later than its early part).
+// Stage parts in 16-byte chunks; rows padded so that 16-byte fragment reads of
+// 16 consecutive rows fall in distinct banks, each part starting at a multiple
+// of 64 chunks so that one copy instruction reads one buffer:
+//   early: Qp [32][192+8] and dOp [32][128+8] fp16 (rows in permuted order),
+//          LSE and D [32] fp32 (permuted order)
+//   late:  QT [192][32+8] and dOT [128][32+8] fp16
 // Padding chunks are filled with a copy of some chunk of the same part.
 constexpr int QP_LD = DQK + 8, DOP_LD = DV + 8, QT_LD = 40;
-constexpr int KV_QP0 = 0, KV_DOP0 = 832, KV_QT0 = 1408, KV_DOT0 = 2368, KV_LSD0 = 3008, KV_CH = 3072;
-constexpr int KV_STAGE_B = KV_CH * 16;
-constexpr int KV_INSTR = KV_CH / 64;          // copy instructions per stage (48)
-constexpr int KV_IPW = KV_INSTR / 4;          // per wave (12)
-constexpr int KV_NST = 3;                     // stages
-static_assert(KV_QP0 + 32 * QP_LD / 8 <= KV_DOP0 && KV_DOP0 + 32 * DOP_LD / 8 <= KV_QT0 &&
-              KV_QT0 + DQK * QT_LD / 8 <= KV_DOT0 && KV_DOT0 + DV * QT_LD / 8 <= KV_LSD0 && KV_LSD0 + 16 <= KV_CH,
-              "stage parts");
-static_assert(KV_DOP0 % 64 == 0 && KV_QT0 % 64 == 0 && KV_DOT0 % 64 == 0 && KV_LSD0 % 64 == 0, "part alignment");
+constexpr int KE_QP0 = 0, KE_DOP0 = 832, KE_LSD0 = 1408, KE_CH = 1472;   // early stage (16-byte chunks)
+constexpr int KL_QT0 = 0, KL_DOT0 = 960, KL_CH = 1600;                   // late stage
+constexpr int KE_INSTR = KE_CH / 64, KL_INSTR = KL_CH / 64;               // copy instructions per stage (23, 25)
+constexpr int KE_STAGE_B = KE_CH * 16, KL_STAGE_B = KL_CH * 16;
+constexpr int KV_NST = 3;
+constexpr int KV_PEX0 = KV_NST * (KE_STAGE_B + KL_STAGE_B);             // P exchange: [key block][4][64 lanes] f32x4
+constexpr int KV_LDS = KV_PEX0 + 4 * 4 * 64 * 16;
+static_assert(KV_LDS <= 160 * 1024, "LDS");
+static_assert(KE_CH % 64 == 0 && KL_CH % 64 == 0 && KE_DOP0 % 64 == 0 && KE_LSD0 % 64 == 0 && KL_DOT0 % 64 == 0,
+              "part alignment");
+static_assert(KE_QP0 + 32 * QP_LD / 8 <= KE_DOP0 && KE_DOP0 + 32 * DOP_LD / 8 <= KE_LSD0 && KE_LSD0 + 16 <= KE_CH &&
+              KL_QT0 + DQK * QT_LD / 8 <= KL_DOT0 && KL_DOT0 + DV * QT_LD / 8 <= KL_CH, "stage parts");
+constexpr int KV_PRIO_M = 2;
 
-__global__ void __launch_bounds__(256)
+// LDS writes of this wave are complete, then the workgroup barrier; no memory
+// access moves across it
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// byte offset of the lane's chunk pch of an early (E) or late (L) stage in its
+// source tensor (tile 0); padding chunks copy chunk 0 of their row
+__device__ __forceinline__ int kv_src_early(int pch) {
+  if (pch < KE_DOP0) {
+    int rho = pch / (QP_LD / 8), c = pch % (QP_LD / 8);
+    if (rho >= 32 || c >= DQK / 8) rho = c = 0;
+    return (perm32(rho) * DQK + 8 * c) * 2;
+  }
+  if (pch < KE_LSD0) {
+    const int p2 = pch - KE_DOP0;
+    int rho = p2 / (DOP_LD / 8), c = p2 % (DOP_LD / 8);
+    if (rho >= 32 || c >= DV / 8) rho = c = 0;
+    return (perm32(rho) * DV + 8 * c) * 2;
+  }
+  const int p2 = pch - KE_LSD0;
+  return (p2 < 16 ? p2 : 0) * 16;
+}
+__device__ __forceinline__ int kv_src_late(int pch, int sq_pad) {
+  const int p2 = pch < KL_DOT0 ? pch : pch - KL_DOT0;
+  const int d = p2 / (QT_LD / 8);
+  int c = p2 % (QT_LD / 8);
+  if (c >= 4) c = 0;
+  return (d * sq_pad + 8 * c) * 2;
+}
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __restrict__ qft,
-          const uint16_t* __restrict__ dof, const uint16_t* __restrict__ doft, const float* __restrict__ lsdt,
-          const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vt, const uint16_t* __restrict__ krot,
-          uint16_t* __restrict__ dkv, uint16_t* __restrict__ dkvt, float* __restrict__ dkr, int sq_pad,
-          int n_kb) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem_kv[KV_NST * KV_STAGE_B];
+           const uint16_t* __restrict__ dof, const uint16_t* __restrict__ doft, const float* __restrict__ lsdt,
+           const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vrow, const uint16_t* __restrict__ krot,
+           uint16_t* __restrict__ dkv, uint16_t* __restrict__ dkvt, float* __restrict__ dkr, int sq_pad, int n_kb,
+           int xcd_deal) {
+  __shared__ __attribute__((aligned(16))) uint8_t sm[KV_LDS];
   const ExplicitArgs& f = a.f;
-  // longest first: key block 0 sees the most queries
-  const int kbi = blockIdx.x % n_kb, bhi = blockIdx.x / n_kb;
+  // XCD x (= blockIdx.x % 8) takes heads x, x + 8, ...: all key blocks of a
+  // head run on one XCD at the same time, key block 0 (the longest) first;
+  // they all walk the query tiles from the last one down, so a tile is
+  // fetched once into that XCD's L2 and read there by every key block
+  int kbi, bhi;
+  if (xcd_deal) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    bhi = xcd + 8 * (slot / n_kb);
+    kbi = slot % n_kb;
+  } else {
+    kbi = blockIdx.x % n_kb;
+    bhi = blockIdx.x / n_kb;
+  }
   const int b = bhi / f.H, h = bhi % f.H;
   const int64_t bh = (int64_t)b * f.H + h;
   const int kb = kbi * 128;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave >> 2, kw = wave & 3;          // role 0: A, 1: B; key block kw of 32 keys
   const int l32 = lane & 31, hb = lane >> 5;
-  const int key = kb + wave * 32 + l32;            // this lane's key (accumulator column)
+  const int key = kb + kw * 32 + l32;                 // this lane's key (accumulator column)
   const float c2 = f.scale * MLA_LOG2E;
 
-  // query tiles: from the first one that can see key kb to the last
   int qt0 = 0;
   if (f.causal) {
     const int64_t first = (int64_t)kb + f.kv_pos0 - f.q_pos0;     // first query that sees key kb
     qt0 = (int)max((int64_t)0, min(first, (int64_t)sq_pad) / 32);
   }
-  const int nqt = sq_pad / 32;
+  const int nt = sq_pad / 32 - qt0;                   // query tiles of this workgroup
+  const int qlast = sq_pad / 32 - 1;                  // step r handles query tile qlast - r
 
-  // ---- tile copies: instruction n = KV_IPW * wave + i fills chunks 64n .. 64n+63
-  // of a stage; the lane's source offset within its part is fixed, the tile
-  // moves it by a uniform amount.
-  const uint32_t q_bytes = (uint32_t)sq_pad * DQK * 2, o_bytes = (uint32_t)sq_pad * DV * 2;
-  const i32x4_t rs_qp = make_rsrc_uniform(qf + bh * sq_pad * DQK, q_bytes);
-  const i32x4_t rs_dop = make_rsrc_uniform(dof + bh * sq_pad * DV, o_bytes);
-  const i32x4_t rs_qt = make_rsrc_uniform(qft + bh * DQK * sq_pad, q_bytes);
-  const i32x4_t rs_dot = make_rsrc_uniform(doft + bh * DV * sq_pad, o_bytes);
-  const i32x4_t rs_lsd = make_rsrc_uniform(lsdt + bh * (sq_pad / 32) * 64, (uint32_t)(sq_pad / 32) * 256);
-  int voff[KV_IPW];
+  const uint32_t sm_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&sm[0];
+  auto est = [&](int r) __attribute__((always_inline)) { return sm + (r % KV_NST) * KE_STAGE_B; };
+  auto lst = [&](int r) __attribute__((always_inline)) {
+    return sm + KV_NST * KE_STAGE_B + (r % KV_NST) * KL_STAGE_B;
+  };
+  f32x4_t* pex = reinterpret_cast<f32x4_t*>(sm + KV_PEX0) + kw * 4 * 64;   // [4][64 lanes]
+
+  // the B operands of the two products of each role, loaded once; then every
+  // later vector-memory operation of the wave is a tile copy
+  const int kk = min(key, f.s_pad - 1);
+  if (role == 0) {
+    // ================================ A ==================================
+    f16x8_t kb_[DQK / 16];
+    {
+      const uint16_t* kr = kn + (bh * f.s_pad + kk) * DN;
 #pragma unroll
-  for (int i = 0; i < KV_IPW; ++i) {
-    const int pch = 64 * (KV_IPW * wave + i) + lane;
-    int o;
-    if (pch < KV_DOP0) {
-      int rho = pch / (QP_LD / 8), c = pch % (QP_LD / 8);
-      if (rho >= 32 || c >= DQK / 8) rho = c = 0;
-      o = (perm32(rho) * DQK + 8 * c) * 2;
-    } else if (pch < KV_QT0) {
-      const int p2 = pch - KV_DOP0;
-      int rho = p2 / (DOP_LD / 8), c = p2 % (DOP_LD / 8);
-      if (rho >= 32 || c >= DV / 8) rho = c = 0;
-      o = (perm32(rho) * DV + 8 * c) * 2;
-    } else if (pch < KV_DOT0) {
-      const int p2 = pch - KV_QT0;
-      int d = p2 / (QT_LD / 8), c = p2 % (QT_LD / 8);
-      if (c >= 4) c = 0;
-      o = (d * sq_pad + 8 * c) * 2;
-    } else if (pch < KV_LSD0) {
-      const int p2 = pch - KV_DOT0;
-      int d = p2 / (QT_LD / 8), c = p2 % (QT_LD / 8);
-      if (c >= 4) c = 0;
-      o = (d * sq_pad + 8 * c) * 2;
-    } else {
-      const int p2 = pch - KV_LSD0;
-      o = (p2 < 16 ? p2 : 0) * 16;
+      for (int ks = 0; ks < DN / 16; ++ks) kb_[ks] = *reinterpret_cast<const f16x8_t*>(kr + 16 * ks + 8 * hb);
+      const uint16_t* rr = krot + ((int64_t)b * f.s_pad + kk) * DR;
+#pragma unroll
+      for (int ks = 0; ks < DR / 16; ++ks)
+        kb_[DN / 16 + ks] = *reinterpret_cast<const f16x8_t*>(rr + 16 * ks + 8 * hb);
     }
-    voff[i] = o;
-  }
-  const uint32_t smem_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&smem_kv[0];
-  // instruction n's part is known at compile time once the wave is: each wave
-  // runs its own unrolled copy of the issue code
-  auto issue_w = [&](auto wc, int qt) __attribute__((always_inline)) {
-    constexpr int W = decltype(wc)::value;
-    const uint32_t st = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(((qt - qt0) % KV_NST) * KV_STAGE_B));
-    static_for<KV_IPW>([&](auto ic) __attribute__((always_inline)) {
-      constexpr int i = decltype(ic)::value, n = KV_IPW * W + i, c0 = 64 * n;
-      constexpr int part = c0 < KV_DOP0 ? 0 : c0 < KV_QT0 ? 1 : c0 < KV_DOT0 ? 2 : c0 < KV_LSD0 ? 3 : 4;
-      const i32x4_t& rs = part == 0 ? rs_qp : part == 1 ? rs_dop : part == 2 ? rs_qt : part == 3 ? rs_dot : rs_lsd;
-      const int so = part == 0 ? qt * 32 * DQK * 2 : part == 1 ? qt * 32 * DV * 2 : part <= 3 ? qt * 64 : qt * 256;
-      lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[i], __builtin_amdgcn_readfirstlane(so));
-    });
-  };
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue_tile = [&](int qt) __attribute__((always_inline)) {
-    if (wave_u == 0) issue_w(std::integral_constant<int, 0>{}, qt);
-    else if (wave_u == 1) issue_w(std::integral_constant<int, 1>{}, qt);
-    else if (wave_u == 2) issue_w(std::integral_constant<int, 2>{}, qt);
-    else issue_w(std::integral_constant<int, 3>{}, qt);
-  };
-
-  // K (B operand of S = Q K^T: lane = key, k-slots 16 ks + 8 hb ..) and V
-  // (B operand of dP = dO V^T) of the lane's key, loaded once
-  f16x8_t kb_[DQK / 16], vb_[DV / 16];
-  {
-    const int kk = min(key, f.s_pad - 1);
-    const uint16_t* kr = kn + (bh * f.s_pad + kk) * DN;
+    wait_vmcnt<0>();
+    int voff[6];
 #pragma unroll
-    for (int ks = 0; ks < DN / 16; ++ks)
-      kb_[ks] = *reinterpret_cast<const f16x8_t*>(kr + 16 * ks + 8 * hb);
-    const uint16_t* rr = krot + ((int64_t)b * f.s_pad + kk) * DR;
-#pragma unroll
-    for (int ks = 0; ks < DR / 16; ++ks)
-      kb_[DN / 16 + ks] = *reinterpret_cast<const f16x8_t*>(rr + 16 * ks + 8 * hb);
-    const uint16_t* vc = vt + bh * DV * f.s_pad + kk;
-#pragma unroll
-    for (int ks = 0; ks < DV / 16; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vb_[ks][e] = __builtin_bit_cast(f16, vc[(int64_t)(16 * ks + 8 * hb + e) * f.s_pad]);
-  }
-  // these loads are done before the first copies go out, so the copy waits
-  // below count copies only
-  wait_vmcnt<0>();
-
-  f32x16_t dvt[DV / 32], dkt[DQK / 32];
-#pragma unroll
-  for (int d = 0; d < DV / 32; ++d) dvt[d] = f32x16_t{};
-#pragma unroll
-  for (int d = 0; d < DQK / 32; ++d) dkt[d] = f32x16_t{};
-
-  // Tile qt sits in stage (qt - qt0) % 3.  Iteration qt computes P and dS of
-  // tile qt (its S and dP were computed at the end of the previous
-  // iteration), dV^T and dK^T, then S and dP of tile qt + 1; tile qt + 2 is
-  // copied at the top of iteration qt into the stage last read in iteration
-  // qt - 1, so the copies of a tile have a whole iteration to land.
-  auto stage = [&](int qt) __attribute__((always_inline)) {
-    return reinterpret_cast<const uint16_t*>(smem_kv + ((qt - qt0) % KV_NST) * KV_STAGE_B);
-  };
-  auto sdp = [&](int qt, f32x16_t& sacc, f32x16_t& pacc) __attribute__((always_inline)) {
-    const uint16_t* Qp = stage(qt) + KV_QP0 * 8;
-    const uint16_t* dOp = stage(qt) + KV_DOP0 * 8;
-    sacc = f32x16_t{};
-    pacc = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < DQK / 16; ++ks) {
-      sacc = mfma(*reinterpret_cast<const f16x8_t*>(Qp + l32 * QP_LD + 16 * ks + 8 * hb), kb_[ks], sacc);
-      if (ks < DV / 16)
-        pacc = mfma(*reinterpret_cast<const f16x8_t*>(dOp + l32 * DOP_LD + 16 * ks + 8 * hb), vb_[ks], pacc);
-    }
-  };
-  // every (query, key) pair of the tile is visible to this wave's 32 keys
-  const int key_last = kb + wave * 32 + 31;
-  // P and dS; element e is query row rho = 8 (e/4) + 4 hb + e%4.  Branch free:
-  // a masked pair gets the exponent -inf, so exp2 gives 0.  Key j is visible to
-  // query i iff j - i <= q_pos0 - kv_pos0 (clamped: |j - i| < 2^30).
-  const int dpos = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), f.q_pos0 - f.kv_pos0));
-  auto pds = [&](int qt, const f32x16_t& sacc, const f32x16_t& pacc, f16x8_t* pb, f16x8_t* sb)
-      __attribute__((always_inline)) {
-    const float* lsd = reinterpret_cast<const float*>(stage(qt) + KV_LSD0 * 8);
-    const int q0 = qt * 32;
-    const bool full = key_last < f.s_vis && q0 + 31 < f.Sq && (!f.causal || key_last - q0 <= dpos);
-    f32x4_t l4[4], d4[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      l4[g] = *reinterpret_cast<const f32x4_t*>(lsd + 8 * g + 4 * hb);
-      d4[g] = *reinterpret_cast<const f32x4_t*>(lsd + 32 + 8 * g + 4 * hb);
-    }
-    if (__builtin_amdgcn_readfirstlane((int)full)) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(sacc[e] * c2 - l4[e >> 2][e & 3] * MLA_LOG2E);
-        pb[e >> 3][e & 7] = (f16)p;
-        sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - d4[e >> 2][e & 3]));
+    for (int i = 0; i < 6; ++i) voff[i] = kv_src_early(64 * (4 * i + kw) + lane);
+    const i32x4_t rs_qp = make_rsrc_uniform(qf + bh * sq_pad * DQK, (uint32_t)sq_pad * DQK * 2);
+    const i32x4_t rs_dop = make_rsrc_uniform(dof + bh * sq_pad * DV, (uint32_t)sq_pad * DV * 2);
+    const i32x4_t rs_lsd = make_rsrc_uniform(lsdt + bh * (sq_pad / 32) * 64, (uint32_t)(sq_pad / 32) * 256);
+    const int n_mine = kw < 3 ? 6 : 5;                 // early copy instructions of this wave
+    auto issue_w = [&](auto wc, int r) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
+      const int qt = qlast - r;
+      const uint32_t st = __builtin_amdgcn_readfirstlane(sm_lds + (uint32_t)((r % KV_NST) * KE_STAGE_B));
+      static_for<6>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value, n = 4 * i + W, c0 = 64 * n;
+        if constexpr (n < KE_INSTR) {
+          constexpr int part = c0 < KE_DOP0 ? 0 : c0 < KE_LSD0 ? 1 : 2;
+          const i32x4_t& rs = part == 0 ? rs_qp : part == 1 ? rs_dop : rs_lsd;
+          const int so = part == 0 ? qt * 32 * DQK * 2 : part == 1 ? qt * 32 * DV * 2 : qt * 256;
+          lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[i], __builtin_amdgcn_readfirstlane(so));
+        }
+      });
+    };
+    auto issue = [&](int r) __attribute__((always_inline)) {
+      if (r >= nt) return;
+      if (kw == 0) issue_w(std::integral_constant<int, 0>{}, r);
+      else if (kw == 1) issue_w(std::integral_constant<int, 1>{}, r);
+      else if (kw == 2) issue_w(std::integral_constant<int, 2>{}, r);
+      else issue_w(std::integral_constant<int, 3>{}, r);
+    };
+    // copies of tile r have landed given that those of tile r + 1 may be in flight
+    auto wait_for = [&](int r) __attribute__((always_inline)) {
+      if (r + 1 < nt) {
+        if (n_mine == 6) wait_vmcnt<6>();
+        else wait_vmcnt<5>();
+      } else {
+        wait_vmcnt<0>();
       }
-    } else {
-      const bool key_ok = key < f.s_vis;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
-        const int i = q0 + perm32(rho);
-        const bool vis = key_ok & (i < f.Sq) & (!f.causal | (key - i <= dpos));
-        const float x = sacc[e] * c2 - l4[e >> 2][e & 3] * MLA_LOG2E;
-        const float p = fast_exp2(vis ? x : -INFINITY);
-        pb[e >> 3][e & 7] = (f16)p;
-        sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - d4[e >> 2][e & 3]));
-      }
-    }
-  };
-  // dV^T += dO^T P,  dK^T += Q^T dS  (k-slots: queries 16u + 8hb .. in natural order)
-  auto dvdk = [&](int qt, const f16x8_t* pb, const f16x8_t* sb) __attribute__((always_inline)) {
-    const uint16_t* QT = stage(qt) + KV_QT0 * 8;
-    const uint16_t* dOT = stage(qt) + KV_DOT0 * 8;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int db = 0; db < DV / 32; ++db)
-        dvt[db] = mfma(*reinterpret_cast<const f16x8_t*>(dOT + (db * 32 + l32) * QT_LD + 16 * u + 8 * hb), pb[u],
-                       dvt[db]);
-#pragma unroll
-      for (int db = 0; db < DQK / 32; ++db)
-        dkt[db] = mfma(*reinterpret_cast<const f16x8_t*>(QT + (db * 32 + l32) * QT_LD + 16 * u + 8 * hb), sb[u],
-                       dkt[db]);
-    }
-  };
+    };
 
-  f32x16_t sacc, pacc;
-  if (qt0 < nqt) issue_tile(qt0);
-  if (qt0 + 1 < nqt) issue_tile(qt0 + 1);
-  if (qt0 + 1 < nqt) wait_vmcnt<KV_IPW>();
-  else wait_vmcnt<0>();
-  __syncthreads();
-  if (qt0 < nqt) sdp(qt0, sacc, pacc);
-  for (int qt = qt0; qt < nqt; ++qt) {
-    wait_vmcnt<0>();                                     // this wave's copies of tile qt + 1 have landed
-    __syncthreads();                                     // ... everyone's; the stage of tile qt - 1 is free
-    if (qt + 2 < nqt) issue_tile(qt + 2);
-    f16x8_t pb[2], sb[2];
-    pds(qt, sacc, pacc, pb, sb);
-    dvdk(qt, pb, sb);
-    if (qt + 1 < nqt) sdp(qt + 1, sacc, pacc);
-  }
-
-  // ---- epilogue: dKV (fp16, both layouts) and the key-band gradient -------
-  // accumulator element e of d-block db is row d = 32 db + 8 (e/4) + 4 hb + e%4
-  if (key < f.s_pad) {
-    uint16_t* rowp = dkv + ((int64_t)b * f.s_pad + key) * ((int64_t)f.H * HD) + (int64_t)h * HD;
-    const int64_t ncol = (int64_t)f.B * f.s_pad;
+    f32x16_t dvt[DV / 32];
 #pragma unroll
-    for (int db = 0; db < DQK / 32; ++db)
+    for (int d = 0; d < DV / 32; ++d) dvt[d] = f32x16_t{};
+    f32x16_t sacc = f32x16_t{};
+    auto s_mfmas = [&](int r) __attribute__((always_inline)) {
+      const uint16_t* Qp = reinterpret_cast<const uint16_t*>(est(r) + KE_QP0 * 16);
+      sacc = f32x16_t{};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * hb;
-        float v[4];
+      for (int ks = 0; ks < DQK / 16; ++ks)
+        sacc = mfma(*reinterpret_cast<const f16x8_t*>(Qp + l32 * QP_LD + 16 * ks + 8 * hb), kb_[ks], sacc);
+    };
+    const int key_last = kb + kw * 32 + 31;
+    const int dpos = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), f.q_pos0 - f.kv_pos0));
+    f16x8_t pb[2];
+    // V_A(r): P = exp2(S c2 - LSE log2 e), branch free (a masked pair gets the
+    // exponent -inf); fp16 copy for dV, fp32 copy to LDS for B
+    auto v_phase = [&](int r) __attribute__((always_inline)) {
+      const float* lsd = reinterpret_cast<const float*>(est(r) + KE_LSD0 * 16);
+      const int q0 = (qlast - r) * 32;
+      const bool full = key_last < f.s_vis && q0 + 31 < f.Sq && (!f.causal || key_last - q0 <= dpos);
+      f32x4_t l4[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = f.scale * dkt[db][4 * g + r];
-        if (d < DN) {
-          u32x2_t pk;
-          pk[0] = pack_f16x2(v[0], v[1]);
-          pk[1] = pack_f16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2_t*>(rowp + d) = pk;
+      for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const f32x4_t*>(lsd + 8 * g + 4 * hb);
+      float p[16];
+      if (__builtin_amdgcn_readfirstlane((int)full)) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            dkvt[((int64_t)h * HD + d + r) * ncol + (int64_t)b * f.s_pad + key] = h_bits(v[r]);
-        } else {
-          *reinterpret_cast<f32x4_t*>(dkr + (bh * f.s_pad + key) * DR + (d - DN)) = f32x4_t{v[0], v[1], v[2], v[3]};
+        for (int e = 0; e < 16; ++e) p[e] = fast_exp2(sacc[e] * c2 - l4[e >> 2][e & 3] * MLA_LOG2E);
+      } else {
+        const bool key_ok = key < f.s_vis;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
+          const int i = q0 + perm32(rho);
+          const bool vis = key_ok & (i < f.Sq) & (!f.causal | (key - i <= dpos));
+          const float x = sacc[e] * c2 - l4[e >> 2][e & 3] * MLA_LOG2E;
+          p[e] = fast_exp2(vis ? x : -INFINITY);
         }
       }
 #pragma unroll
-    for (int db = 0; db < DV / 32; ++db)
+      for (int e = 0; e < 16; ++e) pb[e >> 3][e & 7] = (f16)p[e];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pex[q * 64 + lane] = f32x4_t{p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
+    };
+    // M_A(r): dV(r) += dO^T P, then S(r+1)
+    auto m_phase = [&](int r) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(KV_PRIO_M);
+      const uint16_t* dOT = reinterpret_cast<const uint16_t*>(lst(r) + KL_DOT0 * 16);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < DV / 32; ++db)
+          dvt[db] = mfma(*reinterpret_cast<const f16x8_t*>(dOT + (db * 32 + l32) * QT_LD + 16 * u + 8 * hb), pb[u],
+                         dvt[db]);
+      if (r + 1 < nt) s_mfmas(r + 1);
+      __builtin_amdgcn_s_setprio(0);
+    };
+
+    issue(0);
+    issue(1);
+    wait_for(0);
+    __syncthreads();
+    if (nt > 0) s_mfmas(0);
+    for (int r = 0; r < nt; ++r) {
+      barrier_only();
+      issue(r + 2);
+      v_phase(r);
+      wait_for(r + 1);
+      barrier_lds();
+      m_phase(r);
+    }
+    barrier_only();                                   // the B waves' last phase
+    // dV^T -> dKV columns DN .. DN+127 (row and column layouts)
+    if (key < f.s_pad) {
+      uint16_t* rowp = dkv + ((int64_t)b * f.s_pad + key) * ((int64_t)f.H * HD) + (int64_t)h * HD;
+      const int64_t ncol = (int64_t)f.B * f.s_pad;
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * hb;
+          u32x2_t pk;
+          pk[0] = pack_f16x2(dvt[db][4 * g], dvt[db][4 * g + 1]);
+          pk[1] = pack_f16x2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
+          *reinterpret_cast<u32x2_t*>(rowp + DN + d) = pk;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            dkvt[((int64_t)h * HD + DN + d + rr) * ncol + (int64_t)b * f.s_pad + key] = h_bits(dvt[db][4 * g + rr]);
+        }
+    }
+  } else {
+    // ================================ B ==================================
+    f16x8_t vb_[DV / 16];
+    {
+      const uint16_t* vr = vrow + (bh * f.s_pad + kk) * DV;
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks) vb_[ks] = *reinterpret_cast<const f16x8_t*>(vr + 16 * ks + 8 * hb);
+    }
+    wait_vmcnt<0>();
+    int voff[7];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) voff[i] = kv_src_late(64 * (4 * i + kw) + lane, sq_pad);
+    const uint32_t q_bytes = (uint32_t)sq_pad * DQK * 2, o_bytes = (uint32_t)sq_pad * DV * 2;
+    const i32x4_t rs_qt = make_rsrc_uniform(qft + bh * DQK * sq_pad, q_bytes);
+    const i32x4_t rs_dot = make_rsrc_uniform(doft + bh * DV * sq_pad, o_bytes);
+    const int n_mine = kw == 0 ? 7 : 6;                // late copy instructions of this wave
+    auto issue_w = [&](auto wc, int r) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
+      const int qt = qlast - r;
+      const uint32_t st =
+          __builtin_amdgcn_readfirstlane(sm_lds + (uint32_t)(KV_NST * KE_STAGE_B + (r % KV_NST) * KL_STAGE_B));
+      static_for<7>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value, n = 4 * i + W, c0 = 64 * n;
+        if constexpr (n < KL_INSTR) {
+          constexpr int part = c0 < KL_DOT0 ? 0 : 1;
+          const i32x4_t& rs = part == 0 ? rs_qt : rs_dot;
+          lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[i], __builtin_amdgcn_readfirstlane(qt * 64));
+        }
+      });
+    };
+    auto issue = [&](int r) __attribute__((always_inline)) {
+      if (r >= nt) return;
+      if (kw == 0) issue_w(std::integral_constant<int, 0>{}, r);
+      else if (kw == 1) issue_w(std::integral_constant<int, 1>{}, r);
+      else if (kw == 2) issue_w(std::integral_constant<int, 2>{}, r);
+      else issue_w(std::integral_constant<int, 3>{}, r);
+    };
+    auto wait_for = [&](int r) __attribute__((always_inline)) {
+      if (r + 1 < nt) {
+        if (n_mine == 7) wait_vmcnt<7>();
+        else wait_vmcnt<6>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    };
+
+    f32x16_t dkt[DQK / 32];
+#pragma unroll
+    for (int d = 0; d < DQK / 32; ++d) dkt[d] = f32x16_t{};
+    f32x16_t pacc = f32x16_t{};
+    auto dp_mfmas = [&](int r) __attribute__((always_inline)) {
+      const uint16_t* dOp = reinterpret_cast<const uint16_t*>(est(r) + KE_DOP0 * 16);
+      pacc = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks)
+        pacc = mfma(*reinterpret_cast<const f16x8_t*>(dOp + l32 * DOP_LD + 16 * ks + 8 * hb), vb_[ks], pacc);
+    };
+    f16x8_t sb[2];
+    // V_B(r): dS = P (dP - D) with P from the A wave of this key block
+    auto v_phase = [&](int r) __attribute__((always_inline)) {
+      const float* lsd = reinterpret_cast<const float*>(est(r) + KE_LSD0 * 16);
+      f32x4_t d4[4], p4[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * hb;
-        u32x2_t pk;
-        pk[0] = pack_f16x2(dvt[db][4 * g], dvt[db][4 * g + 1]);
-        pk[1] = pack_f16x2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
-        *reinterpret_cast<u32x2_t*>(rowp + DN + d) = pk;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          dkvt[((int64_t)h * HD + DN + d + r) * ncol + (int64_t)b * f.s_pad + key] = h_bits(dvt[db][4 * g + r]);
+        d4[g] = *reinterpret_cast<const f32x4_t*>(lsd + 32 + 8 * g + 4 * hb);
+        p4[g] = pex[g * 64 + lane];
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sb[e >> 3][e & 7] = (f16)(p4[e >> 2][e & 3] * (pacc[e] - d4[e >> 2][e & 3]));
+    };
+    // M_B(r): dK(r) += Q^T dS, then dP(r+1)
+    auto m_phase = [&](int r) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(KV_PRIO_M);
+      const uint16_t* QT = reinterpret_cast<const uint16_t*>(lst(r) + KL_QT0 * 16);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < DQK / 32; ++db)
+          dkt[db] = mfma(*reinterpret_cast<const f16x8_t*>(QT + (db * 32 + l32) * QT_LD + 16 * u + 8 * hb), sb[u],
+                         dkt[db]);
+      if (r + 1 < nt) dp_mfmas(r + 1);
+      __builtin_amdgcn_s_setprio(0);
+    };
+
+    issue(0);
+    issue(1);
+    wait_for(0);
+    __syncthreads();
+    barrier_only();                                   // one phase behind the A waves
+    if (nt > 0) dp_mfmas(0);
+    for (int r = 0; r < nt; ++r) {
+      barrier_only();
+      issue(r + 2);
+      v_phase(r);
+      wait_for(r + 1);
+      barrier_lds();                                  // P(r) read before the A wave writes P(r+1)
+      m_phase(r);
+    }
+    // dK^T -> dKV columns 0 .. DN-1 (both layouts) and the key-band gradient
+    if (key < f.s_pad) {
+      uint16_t* rowp = dkv + ((int64_t)b * f.s_pad + key) * ((int64_t)f.H * HD) + (int64_t)h * HD;
+      const int64_t ncol = (int64_t)f.B * f.s_pad;
+#pragma unroll
+      for (int db = 0; db < DQK / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * hb;
+          float v[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) v[rr] = f.scale * dkt[db][4 * g + rr];
+          if (d < DN) {
+            u32x2_t pk;
+            pk[0] = pack_f16x2(v[0], v[1]);
+            pk[1] = pack_f16x2(v[2], v[3]);
+            *reinterpret_cast<u32x2_t*>(rowp + d) = pk;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              dkvt[((int64_t)h * HD + d + rr) * ncol + (int64_t)b * f.s_pad + key] = h_bits(v[rr]);
+          } else {
+            *reinterpret_cast<f32x4_t*>(dkr + (bh * f.s_pad + key) * DR + (d - DN)) = f32x4_t{v[0], v[1], v[2], v[3]};
+          }
+        }
+    }
   }
 }
 
@@ -569,11 +687,22 @@ __global__ void __launch_bounds__(256)
 dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __restrict__ dof,
           const float* __restrict__ dvec, const uint16_t* __restrict__ kn, const uint16_t* __restrict__ krot,
           const uint16_t* __restrict__ vrow, const uint16_t* __restrict__ knt, const uint16_t* __restrict__ krt,
-          const float2* __restrict__ qtab, int sq_pad, int n_qb) {
+          const float2* __restrict__ qtab, int sq_pad, int n_qb, int xcd_deal) {
   __shared__ __attribute__((aligned(16))) uint8_t smem_dq[DQ_NST * DQ_STAGE_B];
   const ExplicitArgs& f = a.f;
-  // longest first: the last query block sees the most keys
-  const int qbi = n_qb - 1 - (int)(blockIdx.x % n_qb), bhi = blockIdx.x / n_qb;
+  // longest first: the last query block sees the most keys.  XCD x (=
+  // blockIdx.x % 8) takes heads x, x + 8, ...: all query blocks of a head run
+  // on one XCD at the same time and walk the key tiles in the same order, so
+  // a key tile is fetched once into that XCD's L2 for all of them
+  int qbi, bhi;
+  if (xcd_deal) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    bhi = xcd + 8 * (slot / n_qb);
+    qbi = n_qb - 1 - slot % n_qb;
+  } else {
+    qbi = n_qb - 1 - (int)(blockIdx.x % n_qb);
+    bhi = blockIdx.x / n_qb;
+  }
   const int b = bhi / f.H, h = bhi % f.H;
   const int64_t bh = (int64_t)b * f.H + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1001,8 +1130,9 @@ hipError_t launch_bwd_kv(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipSt
   const ExplicitArgs& f = a.f;
   if (f.s_pad == 0) return hipSuccess;
   const int n_kb = f.s_pad / 128;
-  hipLaunchKernelGGL(kv_kernel, dim3(f.B * f.H * n_kb), dim3(256), 0, s, a, w.qf, w.qft, w.dof, w.doft, w.lsdt, w.kn,
-                     w.vt, w.krot, w.dkv, w.dkvt, w.dkr, w.sq_pad, n_kb);
+  const int xcd_deal = (f.B * f.H) % 8 == 0 ? 1 : 0;
+  hipLaunchKernelGGL(kv_kernel, dim3(f.B * f.H * n_kb), dim3(512), 0, s, a, w.qf, w.qft, w.dof, w.doft, w.lsdt, w.kn,
+                     w.vrow, w.krot, w.dkv, w.dkvt, w.dkr, w.sq_pad, n_kb, xcd_deal);
   return hipGetLastError();
 }
 
@@ -1010,8 +1140,9 @@ hipError_t launch_bwd_dq(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipSt
   const ExplicitArgs& f = a.f;
   if (f.Sq == 0) return hipSuccess;
   const int n_qb = w.sq_pad / 128;
+  const int xcd_deal = (f.B * f.H) % 8 == 0 ? 1 : 0;
   hipLaunchKernelGGL(dq_kernel, dim3(f.B * f.H * n_qb), dim3(256), 0, s, a, w.qf, w.dof, w.dvec, w.kn, w.krot, w.vrow,
-                     w.knt, w.krt, w.qtab, w.sq_pad, n_qb);
+                     w.knt, w.krt, w.qtab, w.sq_pad, n_qb, xcd_deal);
   return hipGetLastError();
 }
 
