@@ -26,10 +26,13 @@
 //               tiles of Q, dO, Q^T, dO^T stream through LDS.  Writes dKV in
 //               both row and column layouts (fp16, for the two GEMMs) and the
 //               per-head key-band gradient.
-//   dq          per (b, h, 128 queries): 4 waves of 32 queries hold Q^T and
-//               dO^T and stream 32-key tiles of K, V and K^T; S^T = K Q^T,
-//               dP^T = V dO^T, dQ^T += K^T dS^T; writes dq_nope and the
-//               rotated-back dq_pe.
+//   dq          per (b, h, 128 queries): 8 waves, two per 32-query block
+//               sharing a SIMD: one holds Q^T and computes S^T = K Q^T, P and
+//               the RoPE band of dQ^T += K^T dS^T, the other holds dO^T and
+//               computes dP^T = V dO^T, dS and the nope part of dQ^T; P and
+//               dS pass between them through LDS.  32-key tiles of K, V and
+//               K^T stream through LDS.  Writes dq_nope and the rotated-back
+//               dq_pe.
 //   Both attention kernels deal the heads over the XCDs (all blocks of a
 //   head on one XCD at once, walking the streamed tiles in the same order),
 //   so each streamed tile is fetched into that XCD's L2 once for all of them.
@@ -663,32 +666,71 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
 }
 
 // -------------------------------------------------------------------- dq --
-// LDS stage of one 32-key tile, in 16-byte chunks (rows padded against bank
-// conflicts; each part starts at a multiple of 64 chunks and comes from one
-// buffer, so one buffer->LDS copy instruction never spans two parts):
-//   Kn  [32][128+8] fp16, rows in permuted key order   chunks    0 ..  543 (576)
-//   Kr  [32][64+8]  fp16 (rotated band), permuted       chunks  576 ..  863 (896)
-//   Vp  [32][128+8] fp16, permuted                       chunks  896 .. 1439 (1472)
-//   KTn [128][32+8] fp16 (K_nope^T, natural key order)   chunks 1472 .. 2111
-//   KTr [64][32+8]  fp16 (band^T)                        chunks 2112 .. 2431 (2560)
-// Padding chunks are filled with a copy of some chunk of the same part.
+// Query-parallel kernel: per (b, h, 128 queries), 8 waves; the work of each
+// 32-query block is split between two waves that share a SIMD:
+//   wave A (waves 0-3) holds Q^T:  S^T = K Q^T, P, and dQ^T of the RoPE band
+//                                  (+= K_rope^T dS^T, one tile late)
+//   wave B (waves 4-7) holds dO^T: dP^T = V dO^T, dS = P (dP - D), and dQ^T
+//                                  of the nope part (+= K_nope^T dS^T)
+// P goes from A to B and dS from B to A through LDS, lane to the same lane.
+// The waves alternate MFMA and vector phases, B one phase behind A:
+//   M_A(t): dQ_rope(t-1), S(t+1)      V_A(t): P(t), its copy to LDS
+//   M_B(t): dQ_nope(t), dP(t+1)       V_B(t): P(t) from LDS, dS(t) and its copy
+// Key tiles stream through two rings of 3 stages: the early part (K_nope,
+// rotated band and V rows), copied by the A waves two tiles ahead, and the
+// late part (K_nope^T, band^T), copied by the B waves one tile ahead.
+// Stage parts in 16-byte chunks (rows padded against bank conflicts, parts
+// on 64-chunk boundaries, padding chunks copies of a chunk of the same part):
+//   early: Kn [32][128+8], Kr [32][64+8], Vp [32][128+8] fp16, rows in
+//          permuted key order
+//   late:  KTn [128][32+8], KTr [64][32+8] fp16 (natural key order)
 constexpr int KN_LD = DN + 8, KR_LD = DR + 8, VP_LD = DV + 8, KT_LD = 40;
-constexpr int DQ_KN0 = 0, DQ_KR0 = 576, DQ_VP0 = 896, DQ_KTN0 = 1472, DQ_KTR0 = 2112, DQ_END = 2432, DQ_CH = 2560;
-constexpr int DQ_STAGE_B = DQ_CH * 16;
-constexpr int DQ_IPW = DQ_CH / 64 / 4;        // copy instructions per wave (10)
+constexpr int QE_KN0 = 0, QE_KR0 = 576, QE_VP0 = 896, QE_CH = 1472;
+constexpr int QL_KTN0 = 0, QL_KTR0 = 640, QL_CH = 960;
+constexpr int QE_INSTR = QE_CH / 64, QL_INSTR = QL_CH / 64;   // 23, 15
+constexpr int QE_STAGE_B = QE_CH * 16, QL_STAGE_B = QL_CH * 16;
 constexpr int DQ_NST = 3;
-static_assert(DQ_KN0 + 32 * KN_LD / 8 <= DQ_KR0 && DQ_KR0 + 32 * KR_LD / 8 <= DQ_VP0 &&
-              DQ_VP0 + 32 * VP_LD / 8 <= DQ_KTN0 && DQ_KTN0 + DN * KT_LD / 8 <= DQ_KTR0 &&
-              DQ_KTR0 + DR * KT_LD / 8 <= DQ_END && DQ_END <= DQ_CH, "stage parts");
-static_assert(DQ_KR0 % 64 == 0 && DQ_VP0 % 64 == 0 && DQ_KTN0 % 64 == 0 && DQ_KTR0 % 64 == 0 && DQ_END % 64 == 0,
+constexpr int DQ_PEX0 = DQ_NST * (QE_STAGE_B + QL_STAGE_B);    // P: [query block][4][64 lanes] f32x4
+constexpr int DQ_SEX0 = DQ_PEX0 + 4 * 4 * 64 * 16;             // dS: [2][query block][2][64 lanes] f16x8
+constexpr int DQ_LDS = DQ_SEX0 + 2 * 4 * 2 * 64 * 16;
+static_assert(DQ_LDS <= 160 * 1024, "LDS");
+static_assert(QE_KN0 + 32 * KN_LD / 8 <= QE_KR0 && QE_KR0 + 32 * KR_LD / 8 <= QE_VP0 &&
+              QE_VP0 + 32 * VP_LD / 8 <= QE_CH && QL_KTN0 + DN * KT_LD / 8 <= QL_KTR0 &&
+              QL_KTR0 + DR * KT_LD / 8 <= QL_CH, "stage parts");
+static_assert(QE_KR0 % 64 == 0 && QE_VP0 % 64 == 0 && QE_CH % 64 == 0 && QL_KTR0 % 64 == 0 && QL_CH % 64 == 0,
               "part alignment");
 
-__global__ void __launch_bounds__(256)
+__device__ __forceinline__ int dq_src_early(int pch) {
+  if (pch < QE_KR0) {
+    int rho = pch / (KN_LD / 8), c = pch % (KN_LD / 8);
+    if (rho >= 32 || c >= DN / 8) rho = c = 0;
+    return (perm32(rho) * DN + 8 * c) * 2;
+  }
+  if (pch < QE_VP0) {
+    const int p2 = pch - QE_KR0;
+    int rho = p2 / (KR_LD / 8), c = p2 % (KR_LD / 8);
+    if (rho >= 32 || c >= DR / 8) rho = c = 0;
+    return (perm32(rho) * DR + 8 * c) * 2;
+  }
+  const int p2 = pch - QE_VP0;
+  int rho = p2 / (VP_LD / 8), c = p2 % (VP_LD / 8);
+  if (rho >= 32 || c >= DV / 8) rho = c = 0;
+  return (perm32(rho) * DV + 8 * c) * 2;
+}
+__device__ __forceinline__ int dq_src_late(int pch, int s_pad) {
+  const int p2 = pch < QL_KTR0 ? pch : pch - QL_KTR0;
+  const int d = p2 / (KT_LD / 8);
+  int c = p2 % (KT_LD / 8);
+  if (c >= 4) c = 0;
+  return (d * s_pad + 8 * c) * 2;
+}
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __restrict__ dof,
           const float* __restrict__ dvec, const uint16_t* __restrict__ kn, const uint16_t* __restrict__ krot,
           const uint16_t* __restrict__ vrow, const uint16_t* __restrict__ knt, const uint16_t* __restrict__ krt,
           const float2* __restrict__ qtab, int sq_pad, int n_qb, int xcd_deal) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem_dq[DQ_NST * DQ_STAGE_B];
+  __shared__ __attribute__((aligned(16))) uint8_t sm[DQ_LDS];
   const ExplicitArgs& f = a.f;
   // longest first: the last query block sees the most keys.  XCD x (=
   // blockIdx.x % 8) takes heads x, x + 8, ...: all query blocks of a head run
@@ -705,28 +747,12 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
   }
   const int b = bhi / f.H, h = bhi % f.H;
   const int64_t bh = (int64_t)b * f.H + h;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave >> 2, qw = wave & 3;          // role 0: A, 1: B; query block qw of 32
   const int l32 = lane & 31, hb = lane >> 5;
-  const int i = qbi * 128 + wave * 32 + l32;        // this lane's query (accumulator column)
+  const int i = qbi * 128 + qw * 32 + l32;            // this lane's query (accumulator column)
   const float c2 = f.scale * MLA_LOG2E;
-
-  f16x8_t qb_[DQK / 16], ob_[DV / 16];               // B operands: lane = query, k-slots 16 ks + 8 hb ..
-#pragma unroll
-  for (int ks = 0; ks < DQK / 16; ++ks)
-    qb_[ks] = *reinterpret_cast<const f16x8_t*>(qf + (bh * sq_pad + i) * DQK + 16 * ks + 8 * hb);
-#pragma unroll
-  for (int ks = 0; ks < DV / 16; ++ks)
-    ob_[ks] = *reinterpret_cast<const f16x8_t*>(dof + (bh * sq_pad + i) * DV + 16 * ks + 8 * hb);
-  const float lse = (i < f.Sq) ? a.lse[bh * f.Sq + i] : -INFINITY;
-  const float dd = dvec[bh * sq_pad + i];
-  // a row with an infinite LSE sees no key; its P is 0 through row_ok
-  const bool row_ok = i < f.Sq && lse != -INFINITY;
-  const float lse_l2 = row_ok ? lse * MLA_LOG2E : 0.f;
-  // key j is visible to query i iff j - i <= q_pos0 - kv_pos0 (clamped: |j - i| < 2^30)
-  const int dpos = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), f.q_pos0 - f.kv_pos0));
-  // these loads are done before the first copies go out, so the copy waits
-  // below count copies only
-  wait_vmcnt<0>();
 
   // key tiles visible to the block's last query
   int kend = f.s_vis;
@@ -736,169 +762,271 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
     kend = (int)max((int64_t)0, min(lim, (int64_t)f.s_vis));
   }
   const int nkt = (kend + 31) / 32;
-  // keys [0, kfull) are visible to every query of this wave
-  int kfull = f.s_vis;
-  if (f.causal) {
-    const int64_t lim = f.q_pos0 + (qbi * 128 + wave * 32) - f.kv_pos0 + 1;
-    kfull = (int)max((int64_t)0, min(lim, (int64_t)f.s_vis));
-  }
-  const bool wave_rows_live = qbi * 128 + wave * 32 + 31 < f.Sq;
 
-  // ---- tile copies: instruction n = DQ_IPW * wave + i fills chunks 64n .. 64n+63
+  const uint32_t sm_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&sm[0];
+  auto est = [&](int kt) __attribute__((always_inline)) { return sm + (kt % DQ_NST) * QE_STAGE_B; };
+  auto lst = [&](int kt) __attribute__((always_inline)) {
+    return sm + DQ_NST * QE_STAGE_B + (kt % DQ_NST) * QL_STAGE_B;
+  };
+  f32x4_t* pex = reinterpret_cast<f32x4_t*>(sm + DQ_PEX0) + qw * 4 * 64;                 // [4][64 lanes]
+  auto sex = [&](int kt) __attribute__((always_inline)) {                                  // [2][64 lanes]
+    return reinterpret_cast<f16x8_t*>(sm + DQ_SEX0) + ((kt & 1) * 4 + qw) * 2 * 64;
+  };
   const uint32_t sp = (uint32_t)f.s_pad;
-  const i32x4_t rs_kn = make_rsrc_uniform(kn + bh * f.s_pad * DN, sp * DN * 2);
-  const i32x4_t rs_kr = make_rsrc_uniform(krot + (int64_t)b * f.s_pad * DR, sp * DR * 2);
-  const i32x4_t rs_vp = make_rsrc_uniform(vrow + bh * f.s_pad * DV, sp * DV * 2);
-  const i32x4_t rs_ktn = make_rsrc_uniform(knt + bh * DN * f.s_pad, sp * DN * 2);
-  const i32x4_t rs_ktr = make_rsrc_uniform(krt + (int64_t)b * DR * f.s_pad, sp * DR * 2);
-  int voff[DQ_IPW];
+
+  if (role == 0) {
+    // ================================ A ==================================
+    f16x8_t qb_[DQK / 16];                             // B operand: lane = query, k-slots 16 ks + 8 hb ..
 #pragma unroll
-  for (int k = 0; k < DQ_IPW; ++k) {
-    const int pch = 64 * (DQ_IPW * wave + k) + lane;
-    int o;
-    if (pch < DQ_KR0) {
-      int rho = pch / (KN_LD / 8), c = pch % (KN_LD / 8);
-      if (rho >= 32 || c >= DN / 8) rho = c = 0;
-      o = (perm32(rho) * DN + 8 * c) * 2;
-    } else if (pch < DQ_VP0) {
-      const int p2 = pch - DQ_KR0;
-      int rho = p2 / (KR_LD / 8), c = p2 % (KR_LD / 8);
-      if (rho >= 32 || c >= DR / 8) rho = c = 0;
-      o = (perm32(rho) * DR + 8 * c) * 2;
-    } else if (pch < DQ_KTN0) {
-      const int p2 = pch - DQ_VP0;
-      int rho = p2 / (VP_LD / 8), c = p2 % (VP_LD / 8);
-      if (rho >= 32 || c >= DV / 8) rho = c = 0;
-      o = (perm32(rho) * DV + 8 * c) * 2;
-    } else if (pch < DQ_END) {
-      const int p2 = pch - (pch < DQ_KTR0 ? DQ_KTN0 : DQ_KTR0);
-      int d = p2 / (KT_LD / 8), c = p2 % (KT_LD / 8);
-      if (c >= 4) c = 0;
-      o = (d * f.s_pad + 8 * c) * 2;
-    } else {
-      o = 0;                                             // past the last part: a dummy copy
+    for (int ks = 0; ks < DQK / 16; ++ks)
+      qb_[ks] = *reinterpret_cast<const f16x8_t*>(qf + (bh * sq_pad + i) * DQK + 16 * ks + 8 * hb);
+    const float lse = (i < f.Sq) ? a.lse[bh * f.Sq + i] : -INFINITY;
+    // a row with an infinite LSE sees no key; its P is 0 through row_ok
+    const bool row_ok = i < f.Sq && lse != -INFINITY;
+    const float lse_l2 = row_ok ? lse * MLA_LOG2E : 0.f;
+    const int dpos = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), f.q_pos0 - f.kv_pos0));
+    // keys [0, kfull) are visible to every query of this block
+    int kfull = f.s_vis;
+    if (f.causal) {
+      const int64_t lim = f.q_pos0 + (qbi * 128 + qw * 32) - f.kv_pos0 + 1;
+      kfull = (int)max((int64_t)0, min(lim, (int64_t)f.s_vis));
     }
-    voff[k] = o;
-  }
-  const uint32_t smem_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&smem_dq[0];
-  auto issue_w = [&](auto wc, int kt) __attribute__((always_inline)) {
-    constexpr int W = decltype(wc)::value;
-    const uint32_t st = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)((kt % DQ_NST) * DQ_STAGE_B));
-    static_for<DQ_IPW>([&](auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value, c0 = 64 * (DQ_IPW * W + k);
-      constexpr int part = c0 < DQ_KR0 ? 0 : c0 < DQ_VP0 ? 1 : c0 < DQ_KTN0 ? 2 : c0 < DQ_KTR0 ? 3 : 4;
-      // rows of the first three parts are keys (row bytes 256 / 128 / 256);
-      // rows of the transposed parts are features, 32 keys = 64 bytes along
-      const i32x4_t& rs = part == 0 ? rs_kn : part == 1 ? rs_kr : part == 2 ? rs_vp : part == 3 ? rs_ktn : rs_ktr;
-      const int so = part == 0 ? kt * 32 * DN * 2 : part == 1 ? kt * 32 * DR * 2 : part == 2 ? kt * 32 * DV * 2
-                                                                                              : kt * 64;
-      lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[k], __builtin_amdgcn_readfirstlane(so));
-    });
-  };
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue_tile = [&](int kt) __attribute__((always_inline)) {
-    if (wave_u == 0) issue_w(std::integral_constant<int, 0>{}, kt);
-    else if (wave_u == 1) issue_w(std::integral_constant<int, 1>{}, kt);
-    else if (wave_u == 2) issue_w(std::integral_constant<int, 2>{}, kt);
-    else issue_w(std::integral_constant<int, 3>{}, kt);
-  };
-
-  f32x16_t dqt[DQK / 32];
+    const bool rows_live = qbi * 128 + qw * 32 + 31 < f.Sq;
+    wait_vmcnt<0>();                                   // later vector-memory operations are tile copies
+    int voff[6];
 #pragma unroll
-  for (int d = 0; d < DQK / 32; ++d) dqt[d] = f32x16_t{};
-
-  // Tile kt sits in stage kt % 3.  Iteration kt computes dS of tile kt (its
-  // S^T and dP^T were computed at the end of the previous iteration) and
-  // dQ^T, then S^T and dP^T of tile kt + 1, so that the two MFMA runs follow
-  // each other without a dependency; tile kt + 2 is copied at the top of
-  // iteration kt into the stage last read in iteration kt - 1.
-  auto stage_p = [&](int kt) __attribute__((always_inline)) {
-    return reinterpret_cast<const uint16_t*>(smem_dq + (kt % DQ_NST) * DQ_STAGE_B);
-  };
-  // S^T = K Q^T, dP^T = V dO^T  (rows: permuted keys, columns: queries)
-  auto sdp = [&](int kt, f32x16_t& sacc, f32x16_t& pacc) __attribute__((always_inline)) {
-    const uint16_t* st = stage_p(kt);
-    const uint16_t* Kn = st + DQ_KN0 * 8;
-    const uint16_t* Kr = st + DQ_KR0 * 8;
-    const uint16_t* Vp = st + DQ_VP0 * 8;
-    sacc = f32x16_t{};
-    pacc = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < DQK / 16; ++ks) {
-      const uint16_t* ap = ks < DN / 16 ? Kn + l32 * KN_LD + 16 * ks : Kr + l32 * KR_LD + 16 * (ks - DN / 16);
-      sacc = mfma(*reinterpret_cast<const f16x8_t*>(ap + 8 * hb), qb_[ks], sacc);
-      if (ks < DV / 16)
-        pacc = mfma(*reinterpret_cast<const f16x8_t*>(Vp + l32 * VP_LD + 16 * ks + 8 * hb), ob_[ks], pacc);
-    }
-  };
-
-  f32x16_t sacc, pacc;
-  if (nkt > 0) issue_tile(0);
-  if (nkt > 1) issue_tile(1);
-  if (nkt > 1) wait_vmcnt<DQ_IPW>();
-  else wait_vmcnt<0>();
-  __syncthreads();
-  if (nkt > 0) sdp(0, sacc, pacc);
-  for (int kt = 0; kt < nkt; ++kt) {
-    wait_vmcnt<0>();                                     // this wave's copies of tile kt + 1 have landed
-    __syncthreads();                                     // ... everyone's; the stage of tile kt - 1 is free
-    if (kt + 2 < nkt) issue_tile(kt + 2);
-    const uint16_t* st = stage_p(kt);
-    const uint16_t* KTn = st + DQ_KTN0 * 8;
-    const uint16_t* KTr = st + DQ_KTR0 * 8;
-    const bool full = wave_rows_live && kt * 32 + 32 <= kfull;
-    f16x8_t sb[2];
-    if (__builtin_amdgcn_readfirstlane((int)full)) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(sacc[e] * c2 - lse_l2);
-        sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - dd));
+    for (int k = 0; k < 6; ++k) voff[k] = dq_src_early(64 * (4 * k + qw) + lane);
+    const i32x4_t rs_kn = make_rsrc_uniform(kn + bh * f.s_pad * DN, sp * DN * 2);
+    const i32x4_t rs_kr = make_rsrc_uniform(krot + (int64_t)b * f.s_pad * DR, sp * DR * 2);
+    const i32x4_t rs_vp = make_rsrc_uniform(vrow + bh * f.s_pad * DV, sp * DV * 2);
+    const int n_mine = qw < 3 ? 6 : 5;                 // early copy instructions of this wave
+    auto issue_w = [&](auto wc, int kt) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
+      const uint32_t st = __builtin_amdgcn_readfirstlane(sm_lds + (uint32_t)((kt % DQ_NST) * QE_STAGE_B));
+      static_for<6>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value, n = 4 * k + W, c0 = 64 * n;
+        if constexpr (n < QE_INSTR) {
+          constexpr int part = c0 < QE_KR0 ? 0 : c0 < QE_VP0 ? 1 : 2;
+          const i32x4_t& rs = part == 0 ? rs_kn : part == 1 ? rs_kr : rs_vp;
+          const int so = part == 0 ? kt * 32 * DN * 2 : part == 1 ? kt * 32 * DR * 2 : kt * 32 * DV * 2;
+          lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[k], __builtin_amdgcn_readfirstlane(so));
+        }
+      });
+    };
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+      if (kt >= nkt) return;
+      if (qw == 0) issue_w(std::integral_constant<int, 0>{}, kt);
+      else if (qw == 1) issue_w(std::integral_constant<int, 1>{}, kt);
+      else if (qw == 2) issue_w(std::integral_constant<int, 2>{}, kt);
+      else issue_w(std::integral_constant<int, 3>{}, kt);
+    };
+    // copies of tile kt have landed given that those of tile kt + 1 may be in flight
+    auto wait_for = [&](int kt) __attribute__((always_inline)) {
+      if (kt + 1 < nkt) {
+        if (n_mine == 6) wait_vmcnt<6>();
+        else wait_vmcnt<5>();
+      } else {
+        wait_vmcnt<0>();
       }
-    } else {
-      // branch free: a masked pair gets the exponent -inf, so exp2 gives 0
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rho = 8 * (e >> 2) + 4 * hb + (e & 3);
-        const int j = kt * 32 + perm32(rho);
-        const bool vis = row_ok & (j < f.s_vis) & (!f.causal | (j - i <= dpos));
-        const float p = fast_exp2(vis ? sacc[e] * c2 - lse_l2 : -INFINITY);
-        sb[e >> 3][e & 7] = (f16)(p * (pacc[e] - dd));
-      }
-    }
-    // dQ^T += K^T dS^T  (k-slots: keys 16u + 8hb .. in natural order)
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int db = 0; db < DQK / 32; ++db) {
-        const uint16_t* ap = db < DN / 32 ? KTn + (db * 32 + l32) * KT_LD : KTr + ((db - DN / 32) * 32 + l32) * KT_LD;
-        dqt[db] = mfma(*reinterpret_cast<const f16x8_t*>(ap + 16 * u + 8 * hb), sb[u], dqt[db]);
-      }
-    if (kt + 1 < nkt) sdp(kt + 1, sacc, pacc);
-  }
+    };
 
-  // ---- epilogue: dq_nope, and dq_pe rotated back by the negative angle ----
-  if (i < f.Sq) {
-    const int64_t row = ((int64_t)b * f.Sq + i) * f.H + h;
+    f32x16_t dqr[DR / 32];                             // dQ^T of the RoPE band
 #pragma unroll
-    for (int db = 0; db < DN / 32; ++db)
+    for (int d = 0; d < DR / 32; ++d) dqr[d] = f32x16_t{};
+    f32x16_t sacc = f32x16_t{};
+    auto s_mfmas = [&](int kt) __attribute__((always_inline)) {
+      const uint8_t* st = est(kt);
+      const uint16_t* Kn = reinterpret_cast<const uint16_t*>(st + QE_KN0 * 16);
+      const uint16_t* Kr = reinterpret_cast<const uint16_t*>(st + QE_KR0 * 16);
+      sacc = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < DQK / 16; ++ks) {
+        const uint16_t* ap = ks < DN / 16 ? Kn + l32 * KN_LD + 16 * ks : Kr + l32 * KR_LD + 16 * (ks - DN / 16);
+        sacc = mfma(*reinterpret_cast<const f16x8_t*>(ap + 8 * hb), qb_[ks], sacc);
+      }
+    };
+    // dQ^T_rope += K_rope^T dS^T of tile kt (k-slots: keys 16u + 8hb .. in natural order)
+    auto dqr_mfmas = [&](int kt) __attribute__((always_inline)) {
+      const uint16_t* KTr = reinterpret_cast<const uint16_t*>(lst(kt) + QL_KTR0 * 16);
+      const f16x8_t* ds = sex(kt);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f16x8_t sbu = ds[u * 64 + lane];
+#pragma unroll
+        for (int db = 0; db < DR / 32; ++db)
+          dqr[db] = mfma(*reinterpret_cast<const f16x8_t*>(KTr + (db * 32 + l32) * KT_LD + 16 * u + 8 * hb), sbu,
+                         dqr[db]);
+      }
+    };
+    // V_A(kt): P^T = exp2(S^T c2 - LSE log2 e), branch free (a masked pair
+    // gets the exponent -inf), to LDS for B
+    auto v_phase = [&](int kt) __attribute__((always_inline)) {
+      const bool fast = __builtin_amdgcn_readfirstlane((int)(rows_live && kt * 32 + 32 <= kfull));
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * hb;
-        *reinterpret_cast<f32x4_t*>(a.dq_nope + row * DN + d) =
-            f32x4_t{f.scale * dqt[db][4 * g], f.scale * dqt[db][4 * g + 1], f.scale * dqt[db][4 * g + 2],
-                    f.scale * dqt[db][4 * g + 3]};
-      }
-    // rope rows 128 + m (block 4) and 128 + m + 32 (block 5) sit in the same lane and element
+        float p[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 8 * g + 4 * hb + r;
-        const float lo = f.scale * dqt[4][4 * g + r], hi = f.scale * dqt[5][4 * g + r];
-        const float2 cs = qtab[(int64_t)i * 32 + m];
-        a.dq_pe[row * DR + m] = lo * cs.x + hi * cs.y;
-        a.dq_pe[row * DR + m + 32] = hi * cs.x - lo * cs.y;
+        for (int rr = 0; rr < 4; ++rr) {
+          const int e = 4 * g + rr;
+          const float x = sacc[e] * c2 - lse_l2;
+          if (fast) {
+            p[rr] = fast_exp2(x);
+          } else {
+            const int j = kt * 32 + perm32(8 * g + 4 * hb + rr);
+            const bool vis = row_ok & (j < f.s_vis) & (!f.causal | (j - i <= dpos));
+            p[rr] = fast_exp2(vis ? x : -INFINITY);
+          }
+        }
+        pex[g * 64 + lane] = f32x4_t{p[0], p[1], p[2], p[3]};
       }
+    };
+    auto iteration = [&](auto with_s, int kt) __attribute__((always_inline)) {
+      barrier_only();
+      issue(kt + 2);
+      v_phase(kt);
+      wait_for(kt + 1);
+      barrier_lds();
+      __builtin_amdgcn_s_setprio(KV_PRIO_M);
+      if (kt > 0) dqr_mfmas(kt - 1);
+      if constexpr (decltype(with_s)::value) s_mfmas(kt + 1);
+      __builtin_amdgcn_s_setprio(0);
+    };
+
+    issue(0);
+    issue(1);
+    wait_for(0);
+    __syncthreads();
+    if (nkt > 0) s_mfmas(0);
+    for (int kt = 0; kt + 1 < nkt; ++kt) iteration(std::true_type{}, kt);
+    if (nkt > 0) iteration(std::false_type{}, nkt - 1);
+    barrier_only();                                   // dS of the last tile is in LDS
+    if (nkt > 0) dqr_mfmas(nkt - 1);
+    // dq_pe: rows 128 + m (block 0) and 128 + m + 32 (block 1) sit in the same
+    // lane and element; rotated back by the negative angle
+    if (i < f.Sq) {
+      const int64_t row = ((int64_t)b * f.Sq + i) * f.H + h;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 8 * g + 4 * hb + r;
+          const float lo = f.scale * dqr[0][4 * g + r], hi = f.scale * dqr[1][4 * g + r];
+          const float2 cs = qtab[(int64_t)i * 32 + m];
+          a.dq_pe[row * DR + m] = lo * cs.x + hi * cs.y;
+          a.dq_pe[row * DR + m + 32] = hi * cs.x - lo * cs.y;
+        }
+    }
+  } else {
+    // ================================ B ==================================
+    f16x8_t ob_[DV / 16];                              // B operand: lane = query
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks)
+      ob_[ks] = *reinterpret_cast<const f16x8_t*>(dof + (bh * sq_pad + i) * DV + 16 * ks + 8 * hb);
+    const float dd = dvec[bh * sq_pad + i];
+    wait_vmcnt<0>();
+    int voff[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) voff[k] = dq_src_late(64 * (4 * k + qw) + lane, f.s_pad);
+    const i32x4_t rs_ktn = make_rsrc_uniform(knt + bh * DN * f.s_pad, sp * DN * 2);
+    const i32x4_t rs_ktr = make_rsrc_uniform(krt + (int64_t)b * DR * f.s_pad, sp * DR * 2);
+    const int n_mine = qw < 3 ? 4 : 3;                 // late copy instructions of this wave
+    auto issue_w = [&](auto wc, int kt) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
+      const uint32_t st =
+          __builtin_amdgcn_readfirstlane(sm_lds + (uint32_t)(DQ_NST * QE_STAGE_B + (kt % DQ_NST) * QL_STAGE_B));
+      static_for<4>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value, n = 4 * k + W, c0 = 64 * n;
+        if constexpr (n < QL_INSTR) {
+          constexpr int part = c0 < QL_KTR0 ? 0 : 1;
+          const i32x4_t& rs = part == 0 ? rs_ktn : rs_ktr;
+          lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[k], __builtin_amdgcn_readfirstlane(kt * 64));
+        }
+      });
+    };
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+      if (kt >= nkt) return;
+      if (qw == 0) issue_w(std::integral_constant<int, 0>{}, kt);
+      else if (qw == 1) issue_w(std::integral_constant<int, 1>{}, kt);
+      else if (qw == 2) issue_w(std::integral_constant<int, 2>{}, kt);
+      else issue_w(std::integral_constant<int, 3>{}, kt);
+    };
+    auto wait_for = [&](int kt) __attribute__((always_inline)) {
+      if (kt + 1 < nkt) {
+        if (n_mine == 4) wait_vmcnt<4>();
+        else wait_vmcnt<3>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    };
+
+    f32x16_t dqn[DN / 32];                             // dQ^T of the nope part
+#pragma unroll
+    for (int d = 0; d < DN / 32; ++d) dqn[d] = f32x16_t{};
+    f32x16_t pacc = f32x16_t{};
+    auto dp_mfmas = [&](int kt) __attribute__((always_inline)) {
+      const uint16_t* Vp = reinterpret_cast<const uint16_t*>(est(kt) + QE_VP0 * 16);
+      pacc = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks)
+        pacc = mfma(*reinterpret_cast<const f16x8_t*>(Vp + l32 * VP_LD + 16 * ks + 8 * hb), ob_[ks], pacc);
+    };
+    f16x8_t sb[2];
+    // V_B(kt): dS^T = P^T (dP^T - D) with P from the A wave of this block
+    auto v_phase = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t p4 = pex[g * 64 + lane];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int e = 4 * g + rr;
+          sb[e >> 3][e & 7] = (f16)(p4[rr] * (pacc[e] - dd));
+        }
+      }
+      f16x8_t* ds = sex(kt);
+      ds[lane] = sb[0];
+      ds[64 + lane] = sb[1];
+    };
+    // dQ^T_nope += K_nope^T dS^T of tile kt
+    auto dqn_mfmas = [&](int kt) __attribute__((always_inline)) {
+      const uint16_t* KTn = reinterpret_cast<const uint16_t*>(lst(kt) + QL_KTN0 * 16);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < DN / 32; ++db)
+          dqn[db] = mfma(*reinterpret_cast<const f16x8_t*>(KTn + (db * 32 + l32) * KT_LD + 16 * u + 8 * hb), sb[u],
+                         dqn[db]);
+    };
+    auto iteration = [&](auto with_p, int kt) __attribute__((always_inline)) {
+      barrier_only();
+      issue(kt + 1);
+      v_phase(kt);
+      wait_for(kt);
+      barrier_lds();                                  // P(kt) read and dS(kt) written before A goes on
+      __builtin_amdgcn_s_setprio(KV_PRIO_M);
+      dqn_mfmas(kt);
+      if constexpr (decltype(with_p)::value) dp_mfmas(kt + 1);
+      __builtin_amdgcn_s_setprio(0);
+    };
+
+    issue(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    barrier_only();                                   // one phase behind the A waves
+    if (nkt > 0) dp_mfmas(0);
+    for (int kt = 0; kt + 1 < nkt; ++kt) iteration(std::true_type{}, kt);
+    if (nkt > 0) iteration(std::false_type{}, nkt - 1);
+    if (i < f.Sq) {
+      const int64_t row = ((int64_t)b * f.Sq + i) * f.H + h;
+#pragma unroll
+      for (int db = 0; db < DN / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * hb;
+          *reinterpret_cast<f32x4_t*>(a.dq_nope + row * DN + d) =
+              f32x4_t{f.scale * dqn[db][4 * g], f.scale * dqn[db][4 * g + 1], f.scale * dqn[db][4 * g + 2],
+                      f.scale * dqn[db][4 * g + 3]};
+        }
+    }
   }
 }
 
@@ -1141,7 +1269,7 @@ hipError_t launch_bwd_dq(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipSt
   if (f.Sq == 0) return hipSuccess;
   const int n_qb = w.sq_pad / 128;
   const int xcd_deal = (f.B * f.H) % 8 == 0 ? 1 : 0;
-  hipLaunchKernelGGL(dq_kernel, dim3(f.B * f.H * n_qb), dim3(256), 0, s, a, w.qf, w.dof, w.dvec, w.kn, w.krot, w.vrow,
+  hipLaunchKernelGGL(dq_kernel, dim3(f.B * f.H * n_qb), dim3(512), 0, s, a, w.qf, w.dof, w.dvec, w.kn, w.krot, w.vrow,
                      w.knt, w.krt, w.qtab, w.sq_pad, n_qb, xcd_deal);
   return hipGetLastError();
 }
