@@ -1076,7 +1076,18 @@ gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, f
   static_assert(A_CH % 64 == 0 && B_CH % 64 == 0, "parts on instruction boundaries");
   __shared__ __attribute__((aligned(16))) uint16_t Ls[NST * ST_CH * 8];
   const int n_tn = N / BN;
-  const int tm = blockIdx.x / n_tn, tn = blockIdx.x % n_tn;
+  // XCD x (= blockIdx.x % 8) takes the row tiles x, x + 8, ..., each with all
+  // its column tiles at once: the A rows of a tile reach that XCD's L2 once
+  // for every column tile (when the row tiles split evenly over the XCDs)
+  int tm, tn;
+  if ((M / BM) % 8 == 0) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    tm = xcd + 8 * (slot / n_tn);
+    tn = slot % n_tn;
+  } else {
+    tm = blockIdx.x / n_tn;
+    tn = blockIdx.x % n_tn;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hb = lane >> 5;
