@@ -126,6 +126,12 @@ MFMA_CASES = [
                      dtype="bf16", seed=936),
     I.small_explicit("mbwd_multi_tile", s_q=700, s_kv=700, n_heads=1, d_kv=512, d_nope=128, d_rope=64, d_v=128,
                      dtype="bf16", seed=937),
+    # B*H a multiple of 8: the attention kernels deal the (batch, head) pairs
+    # over the XCDs, here across two batch entries, with ragged last tiles
+    I.small_explicit("mbwd_xcd_deal", batch=2, s_q=300, s_kv=300, n_heads=4, d_kv=512, d_nope=128, d_rope=64,
+                     d_v=128, dtype="bf16", seed=938),
+    I.small_explicit("mbwd_xcd_deal_offset", batch=2, s_q=150, s_kv=420, n_heads=8, d_kv=512, d_nope=128,
+                     d_rope=64, d_v=128, q_pos0=270, dtype="bf16", seed=939),
 ]
 
 
