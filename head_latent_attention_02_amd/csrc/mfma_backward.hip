@@ -319,6 +319,7 @@ static_assert(KE_CH % 64 == 0 && KL_CH % 64 == 0 && KE_DOP0 % 64 == 0 && KE_LSD0
 static_assert(KE_QP0 + 32 * QP_LD / 8 <= KE_DOP0 && KE_DOP0 + 32 * DOP_LD / 8 <= KE_LSD0 && KE_LSD0 + 16 <= KE_CH &&
               KL_QT0 + DQK * QT_LD / 8 <= KL_DOT0 && KL_DOT0 + DV * QT_LD / 8 <= KL_CH, "stage parts");
 constexpr int KV_PRIO_M = 2;
+constexpr int KV_MPF = 4;                     // operand fragments read ahead in an MFMA phase
 
 // LDS writes of this wave are complete, then the workgroup barrier; no memory
 // access moves across it
@@ -493,17 +494,45 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
 #pragma unroll
       for (int q = 0; q < 4; ++q) pex[q * 64 + lane] = f32x4_t{p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
     };
-    // M_A(r): dV(r) += dO^T P, then S(r+1)
-    auto m_phase = [&](int r) __attribute__((always_inline)) {
-      __builtin_amdgcn_s_setprio(KV_PRIO_M);
+    // M_A(r): dV(r) += dO^T P and S(r+1) as one MFMA stream (the S chain
+    // interleaved with the independent dV products), operand fragments read
+    // KV_MPF ahead
+    auto m_stream = [&](auto with_s, int r) __attribute__((always_inline)) {
+      constexpr bool WS = decltype(with_s)::value;
+      constexpr int NOPS = WS ? 20 : 8;
       const uint16_t* dOT = reinterpret_cast<const uint16_t*>(lst(r) + KL_DOT0 * 16);
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < DV / 32; ++db)
-          dvt[db] = mfma(*reinterpret_cast<const f16x8_t*>(dOT + (db * 32 + l32) * QT_LD + 16 * u + 8 * hb), pb[u],
-                         dvt[db]);
-      if (r + 1 < nt) s_mfmas(r + 1);
+      const uint16_t* Qp = reinterpret_cast<const uint16_t*>(est(r + 1) + KE_QP0 * 16);
+      auto s_of = [](int k) constexpr { return !WS ? -1 : k < 16 ? ((k & 1) ? -1 : k >> 1) : k - 8; };
+      auto v_of = [](int k) constexpr { return !WS ? k : k < 16 ? ((k & 1) ? k >> 1 : -1) : -1; };
+      auto frag = [&](auto kc) __attribute__((always_inline)) -> f16x8_t {
+        constexpr int k = decltype(kc)::value, js = s_of(k), jv = v_of(k);
+        if constexpr (js >= 0) return *reinterpret_cast<const f16x8_t*>(Qp + l32 * QP_LD + 16 * js + 8 * hb);
+        else return *reinterpret_cast<const f16x8_t*>(dOT + ((jv & 3) * 32 + l32) * QT_LD + 16 * (jv >> 2) + 8 * hb);
+      };
+      f16x8_t fr[KV_MPF + 1];
+      static_for<KV_MPF>([&](auto c) __attribute__((always_inline)) {
+        constexpr int k = decltype(c)::value;
+        if constexpr (k < NOPS) fr[k] = frag(std::integral_constant<int, k>{});
+      });
+      static_for<NOPS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value, js = s_of(k), jv = v_of(k);
+        if constexpr (k + KV_MPF < NOPS)
+          fr[(k + KV_MPF) % (KV_MPF + 1)] = frag(std::integral_constant<int, k + KV_MPF>{});
+        if constexpr (js >= 0)
+          sacc = mfma(fr[k % (KV_MPF + 1)], kb_[js], js == 0 ? f32x16_t{} : sacc);
+        else
+          dvt[jv & 3] = mfma(fr[k % (KV_MPF + 1)], pb[jv >> 2], dvt[jv & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    auto iteration = [&](auto with_s, int r) __attribute__((always_inline)) {
+      barrier_only();
+      issue(r + 2);
+      v_phase(r);
+      wait_for(r + 1);
+      barrier_lds();
+      __builtin_amdgcn_s_setprio(KV_PRIO_M);
+      m_stream(with_s, r);
       __builtin_amdgcn_s_setprio(0);
     };
 
@@ -512,14 +541,9 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
     wait_for(0);
     __syncthreads();
     if (nt > 0) s_mfmas(0);
-    for (int r = 0; r < nt; ++r) {
-      barrier_only();
-      issue(r + 2);
-      v_phase(r);
-      wait_for(r + 1);
-      barrier_lds();
-      m_phase(r);
-    }
+    // the last iteration is peeled so that the loop body holds one MFMA stream
+    for (int r = 0; r + 1 < nt; ++r) iteration(std::true_type{}, r);
+    if (nt > 0) iteration(std::false_type{}, nt - 1);
     barrier_only();                                   // the B waves' last phase
     // dV^T -> dKV columns DN .. DN+127 (row and column layouts)
     if (key < f.s_pad) {
@@ -609,17 +633,44 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
 #pragma unroll
       for (int e = 0; e < 16; ++e) sb[e >> 3][e & 7] = (f16)(p4[e >> 2][e & 3] * (pacc[e] - d4[e >> 2][e & 3]));
     };
-    // M_B(r): dK(r) += Q^T dS, then dP(r+1)
-    auto m_phase = [&](int r) __attribute__((always_inline)) {
-      __builtin_amdgcn_s_setprio(KV_PRIO_M);
+    // M_B(r): dK(r) += Q^T dS and dP(r+1) as one MFMA stream (the dP chain
+    // interleaved with the dK products), fragments read KV_MPF ahead
+    auto m_stream = [&](auto with_p, int r) __attribute__((always_inline)) {
+      constexpr bool WP = decltype(with_p)::value;
+      constexpr int NOPS = WP ? 20 : 12;
       const uint16_t* QT = reinterpret_cast<const uint16_t*>(lst(r) + KL_QT0 * 16);
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < DQK / 32; ++db)
-          dkt[db] = mfma(*reinterpret_cast<const f16x8_t*>(QT + (db * 32 + l32) * QT_LD + 16 * u + 8 * hb), sb[u],
-                         dkt[db]);
-      if (r + 1 < nt) dp_mfmas(r + 1);
+      const uint16_t* dOp = reinterpret_cast<const uint16_t*>(est(r + 1) + KE_DOP0 * 16);
+      auto p_of = [](int k) constexpr { return !WP ? -1 : k < 16 ? ((k & 1) ? k >> 1 : -1) : -1; };
+      auto k_of = [](int k) constexpr { return !WP ? k : k < 16 ? ((k & 1) ? -1 : k >> 1) : k - 8; };
+      auto frag = [&](auto kc) __attribute__((always_inline)) -> f16x8_t {
+        constexpr int k = decltype(kc)::value, jp = p_of(k), jk = k_of(k);
+        if constexpr (jp >= 0) return *reinterpret_cast<const f16x8_t*>(dOp + l32 * DOP_LD + 16 * jp + 8 * hb);
+        else return *reinterpret_cast<const f16x8_t*>(QT + ((jk % 6) * 32 + l32) * QT_LD + 16 * (jk / 6) + 8 * hb);
+      };
+      f16x8_t fr[KV_MPF + 1];
+      static_for<KV_MPF>([&](auto c) __attribute__((always_inline)) {
+        constexpr int k = decltype(c)::value;
+        if constexpr (k < NOPS) fr[k] = frag(std::integral_constant<int, k>{});
+      });
+      static_for<NOPS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value, jp = p_of(k), jk = k_of(k);
+        if constexpr (k + KV_MPF < NOPS)
+          fr[(k + KV_MPF) % (KV_MPF + 1)] = frag(std::integral_constant<int, k + KV_MPF>{});
+        if constexpr (jp >= 0)
+          pacc = mfma(fr[k % (KV_MPF + 1)], vb_[jp], jp == 0 ? f32x16_t{} : pacc);
+        else
+          dkt[jk % 6] = mfma(fr[k % (KV_MPF + 1)], sb[jk / 6], dkt[jk % 6]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    auto iteration = [&](auto with_p, int r) __attribute__((always_inline)) {
+      barrier_only();
+      issue(r + 2);
+      v_phase(r);
+      wait_for(r + 1);
+      barrier_lds();                                  // P(r) read before the A wave writes P(r+1)
+      __builtin_amdgcn_s_setprio(KV_PRIO_M);
+      m_stream(with_p, r);
       __builtin_amdgcn_s_setprio(0);
     };
 
@@ -629,14 +680,8 @@ kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
     __syncthreads();
     barrier_only();                                   // one phase behind the A waves
     if (nt > 0) dp_mfmas(0);
-    for (int r = 0; r < nt; ++r) {
-      barrier_only();
-      issue(r + 2);
-      v_phase(r);
-      wait_for(r + 1);
-      barrier_lds();                                  // P(r) read before the A wave writes P(r+1)
-      m_phase(r);
-    }
+    for (int r = 0; r + 1 < nt; ++r) iteration(std::true_type{}, r);
+    if (nt > 0) iteration(std::false_type{}, nt - 1);
     // dK^T -> dKV columns 0 .. DN-1 (both layouts) and the key-band gradient
     if (key < f.s_pad) {
       uint16_t* rowp = dkv + ((int64_t)b * f.s_pad + key) * ((int64_t)f.H * HD) + (int64_t)h * HD;
@@ -880,15 +925,61 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
         pex[g * 64 + lane] = f32x4_t{p[0], p[1], p[2], p[3]};
       }
     };
-    auto iteration = [&](auto with_s, int kt) __attribute__((always_inline)) {
+    // M_A(kt): dQ_rope(kt-1) (with_r) and S(kt+1) (with_s) as one MFMA
+    // stream, the S chain interleaved with the rope products, operand
+    // fragments read KV_MPF ahead
+    auto m_stream = [&](auto with_r, auto with_s, int kt) __attribute__((always_inline)) {
+      constexpr bool WR = decltype(with_r)::value, WS = decltype(with_s)::value;
+      constexpr int NR = WR ? 4 : 0, NS = WS ? 12 : 0, NOPS = NR + NS;
+      const uint8_t* st = est(WS ? kt + 1 : kt);
+      const uint16_t* Kn = reinterpret_cast<const uint16_t*>(st + QE_KN0 * 16);
+      const uint16_t* Kr = reinterpret_cast<const uint16_t*>(st + QE_KR0 * 16);
+      const uint16_t* KTr = reinterpret_cast<const uint16_t*>(lst(WR ? kt - 1 : kt) + QL_KTR0 * 16);
+      // op k: rope product k/2 for odd k < 2 NR when both run, else the S chain
+      auto r_of = [](int k) constexpr { return !WR ? -1 : !WS ? k : (k < 2 * NR && (k & 1)) ? k >> 1 : -1; };
+      auto s_of = [](int k) constexpr {
+        return !WS ? -1 : !WR ? k : k < 2 * NR ? ((k & 1) ? -1 : k >> 1) : k - NR;
+      };
+      auto frag = [&](auto kc) __attribute__((always_inline)) -> f16x8_t {
+        constexpr int k = decltype(kc)::value, jr = r_of(k), js = s_of(k);
+        if constexpr (jr >= 0) {
+          // rope product jr: u = jr / 2, d-block jr % 2
+          return *reinterpret_cast<const f16x8_t*>(KTr + ((jr & 1) * 32 + l32) * KT_LD + 16 * (jr >> 1) + 8 * hb);
+        } else {
+          const uint16_t* ap = js < DN / 16 ? Kn + l32 * KN_LD + 16 * js : Kr + l32 * KR_LD + 16 * (js - DN / 16);
+          return *reinterpret_cast<const f16x8_t*>(ap + 8 * hb);
+        }
+      };
+      f16x8_t dsu[2];
+      if constexpr (WR) {
+        const f16x8_t* ds = sex(kt - 1);
+        dsu[0] = ds[lane];
+        dsu[1] = ds[64 + lane];
+      }
+      f16x8_t fr[KV_MPF + 1];
+      static_for<KV_MPF>([&](auto c) __attribute__((always_inline)) {
+        constexpr int k = decltype(c)::value;
+        if constexpr (k < NOPS) fr[k] = frag(std::integral_constant<int, k>{});
+      });
+      static_for<NOPS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value, jr = r_of(k), js = s_of(k);
+        if constexpr (k + KV_MPF < NOPS)
+          fr[(k + KV_MPF) % (KV_MPF + 1)] = frag(std::integral_constant<int, k + KV_MPF>{});
+        if constexpr (jr >= 0)
+          dqr[jr & 1] = mfma(fr[k % (KV_MPF + 1)], dsu[jr >> 1], dqr[jr & 1]);
+        else
+          sacc = mfma(fr[k % (KV_MPF + 1)], qb_[js], js == 0 ? f32x16_t{} : sacc);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    auto iteration = [&](auto with_r, auto with_s, int kt) __attribute__((always_inline)) {
       barrier_only();
       issue(kt + 2);
       v_phase(kt);
       wait_for(kt + 1);
       barrier_lds();
       __builtin_amdgcn_s_setprio(KV_PRIO_M);
-      if (kt > 0) dqr_mfmas(kt - 1);
-      if constexpr (decltype(with_s)::value) s_mfmas(kt + 1);
+      m_stream(with_r, with_s, kt);
       __builtin_amdgcn_s_setprio(0);
     };
 
@@ -897,8 +988,12 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
     wait_for(0);
     __syncthreads();
     if (nkt > 0) s_mfmas(0);
-    for (int kt = 0; kt + 1 < nkt; ++kt) iteration(std::true_type{}, kt);
-    if (nkt > 0) iteration(std::false_type{}, nkt - 1);
+    // the first and the last iterations are peeled so that the loop body
+    // holds one MFMA stream
+    if (nkt == 1) iteration(std::false_type{}, std::false_type{}, 0);
+    if (nkt > 1) iteration(std::false_type{}, std::true_type{}, 0);
+    for (int kt = 1; kt + 1 < nkt; ++kt) iteration(std::true_type{}, std::true_type{}, kt);
+    if (nkt > 1) iteration(std::true_type{}, std::false_type{}, nkt - 1);
     barrier_only();                                   // dS of the last tile is in LDS
     if (nkt > 0) dqr_mfmas(nkt - 1);
     // dq_pe: rows 128 + m (block 0) and 128 + m + 32 (block 1) sit in the same
@@ -986,15 +1081,37 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
       ds[lane] = sb[0];
       ds[64 + lane] = sb[1];
     };
-    // dQ^T_nope += K_nope^T dS^T of tile kt
-    auto dqn_mfmas = [&](int kt) __attribute__((always_inline)) {
+    // M_B(kt): dQ_nope(kt) and dP(kt+1) as one MFMA stream (the dP chain
+    // interleaved with the nope products), fragments read KV_MPF ahead
+    auto m_stream = [&](auto with_p, int kt) __attribute__((always_inline)) {
+      constexpr bool WP = decltype(with_p)::value;
+      constexpr int NOPS = WP ? 16 : 8;
       const uint16_t* KTn = reinterpret_cast<const uint16_t*>(lst(kt) + QL_KTN0 * 16);
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < DN / 32; ++db)
-          dqn[db] = mfma(*reinterpret_cast<const f16x8_t*>(KTn + (db * 32 + l32) * KT_LD + 16 * u + 8 * hb), sb[u],
-                         dqn[db]);
+      const uint16_t* Vp = reinterpret_cast<const uint16_t*>(est(kt + 1) + QE_VP0 * 16);
+      auto n_of = [](int k) constexpr { return !WP ? k : (k & 1) ? -1 : k >> 1; };
+      auto p_of = [](int k) constexpr { return !WP ? -1 : (k & 1) ? k >> 1 : -1; };
+      auto frag = [&](auto kc) __attribute__((always_inline)) -> f16x8_t {
+        constexpr int k = decltype(kc)::value, jn = n_of(k), jp = p_of(k);
+        if constexpr (jn >= 0)   // nope product jn: u = jn / 4, d-block jn % 4
+          return *reinterpret_cast<const f16x8_t*>(KTn + ((jn & 3) * 32 + l32) * KT_LD + 16 * (jn >> 2) + 8 * hb);
+        else
+          return *reinterpret_cast<const f16x8_t*>(Vp + l32 * VP_LD + 16 * jp + 8 * hb);
+      };
+      f16x8_t fr[KV_MPF + 1];
+      static_for<KV_MPF>([&](auto c) __attribute__((always_inline)) {
+        constexpr int k = decltype(c)::value;
+        if constexpr (k < NOPS) fr[k] = frag(std::integral_constant<int, k>{});
+      });
+      static_for<NOPS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value, jn = n_of(k), jp = p_of(k);
+        if constexpr (k + KV_MPF < NOPS)
+          fr[(k + KV_MPF) % (KV_MPF + 1)] = frag(std::integral_constant<int, k + KV_MPF>{});
+        if constexpr (jn >= 0)
+          dqn[jn & 3] = mfma(fr[k % (KV_MPF + 1)], sb[jn >> 2], dqn[jn & 3]);
+        else
+          pacc = mfma(fr[k % (KV_MPF + 1)], ob_[jp], jp == 0 ? f32x16_t{} : pacc);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
     auto iteration = [&](auto with_p, int kt) __attribute__((always_inline)) {
       barrier_only();
@@ -1003,8 +1120,7 @@ dq_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __res
       wait_for(kt);
       barrier_lds();                                  // P(kt) read and dS(kt) written before A goes on
       __builtin_amdgcn_s_setprio(KV_PRIO_M);
-      dqn_mfmas(kt);
-      if constexpr (decltype(with_p)::value) dp_mfmas(kt + 1);
+      m_stream(with_p, kt);
       __builtin_amdgcn_s_setprio(0);
     };
 
