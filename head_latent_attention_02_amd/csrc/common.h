@@ -162,6 +162,13 @@ __device__ __forceinline__ i32x4_t make_rsrc_uniform(const void* base, uint32_t 
   return r;
 }
 
+// Orders the LDS accesses of the lanes of one wave: the wave's LDS operations
+// issued so far are complete, and the compiler moves no memory access across.
+// Needed where a lane reads what another lane of its wave wrote: without it the
+// compiler may hoist a lane's read above that lane's own, non-overlapping
+// writes, and the read then misses another lane's write.
+__device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // s_waitcnt vmcnt(n), leaving the other counters unconstrained
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

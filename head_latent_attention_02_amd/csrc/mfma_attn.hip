@@ -503,7 +503,8 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
       }
     }
   }
-  // a wave reads back only what it wrote itself
+  // a wave reads back only what its own lanes wrote
+  lds_wave_fence();
   constexpr int CPR = OROW / 16;                               // 16-byte chunks per row
 #pragma unroll
   for (int it = 0; it < QW * CPR / 64; ++it) {

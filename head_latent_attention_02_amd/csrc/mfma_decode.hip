@@ -533,8 +533,9 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
           u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
     }
   }
-  // a wave reads back only its own rows (LDS accesses of one wave complete in
-  // order): 4 heads x 256 bytes per instruction
+  // a wave reads back only the rows its own lanes wrote: 4 heads x 256 bytes
+  // per instruction
+  lds_wave_fence();
   uint16_t* dst = o_part + ((int64_t)b * a.n_splits + k) * a.H * DC + 128 * wave;
 #pragma unroll
   for (int it = 0; it < 4 * NHT; ++it) {

@@ -43,6 +43,7 @@ constexpr int REG_BYTES = TJ * TK * 2;       // one operand region of a stage (1
 constexpr int STAGE_BYTES = 2 * REG_BYTES;   // latent rows then W rows
 constexpr int LOADS = 2 * REG_BYTES / 16 / NTHREADS;   // 16-byte copies per lane per step (4)
 constexpr int COPY_ROWS = NTHREADS / 4;                 // 64-byte rows one copy instruction fills (128)
+constexpr int STG_BYTES = 16 * 256;                     // output staging per wave: 16 rows of 256 bytes
 
 // acc += A B on the 32x32x16 bf16 MFMA with the accumulator held in AGPRs
 // (the 128 accumulator registers stay in AGPRs; operands stay in VGPRs).
@@ -56,8 +57,8 @@ __device__ __forceinline__ void mfma32_agpr_first(f32x16_t& acc, bf16x8_t a, bf1
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::); }
 // Marks acc as produced here: compiler-generated reads of the accumulator
 // (AGPR -> VGPR copies) cannot move above this point, which follows the
-// drain.  Used one block at a time so that only one block is copied out at
-// once.
+// drain.  Used for one column of blocks at a time, so that only those blocks
+// are copied out at once.
 __device__ __forceinline__ void agpr_fence(f32x16_t& acc) { asm volatile("" : "+a"(acc)); }
 
 // tile id -> (batch*head, key tile)
@@ -80,7 +81,9 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
 mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w,
                    uint16_t* __restrict__ kn, uint16_t* __restrict__ vt, int B, int H, int Skv,
                    int s_vis, int s_pad, int n_jt, int n_tiles, int xcd_deal) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ls[NSTAGE * STAGE_BYTES / 2];
+  // the copy ring, then the output staging of the 8 waves
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[(NSTAGE * STAGE_BYTES + NTHREADS / 64 * STG_BYTES) / 2];
+  uint8_t* const stg_all = reinterpret_cast<uint8_t*>(Ls) + NSTAGE * STAGE_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -172,48 +175,64 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
       }
     }
 
-    // epilogue: fp16 stores straight from the accumulators (the next tile's
-    // first steps are already in flight).  In a 32x32 block a lane holds
-    // 4 consecutive outputs for each of 4 groups gq (8 bytes each); one
-    // permlane32 swap per word gives each lane 8 consecutive outputs of group
-    // 2p (lanes 0-31) or 2p+1 (lanes 32-63), stored as one 16-byte chunk.
+    // epilogue (the next tile's first steps are already in flight): the
+    // wave's 64 output rows (keys of K_nope, features of V^T) go out in four
+    // rounds of 16 rows, each staged in the wave's 4 KB of LDS so that every
+    // store writes whole 256-byte row segments.  In a 32x32 block lane
+    // (l32, hb) holds, for each group g, 4 consecutive outputs of row l32 at
+    // column 8g + 4hb of the block; a staged row's 16-byte chunks are
+    // XOR-swizzled by the row, which keeps both the 8-byte writes and the
+    // 16-byte reads free of bank conflicts.
     int bh, jt;
     tile_coords((int)blockIdx.x + t * G, n_jt, xcd_deal != 0, bh, jt);
     const int j0 = jt * TJ;
+    uint8_t* stg = stg_all + wave * STG_BYTES;
     mfma_drain();
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int y = 0; y < 2; ++y) {
+      uint32_t wd[4][4][2];
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {
+      for (int x = 0; x < 4; ++x) {
         agpr_fence(acc[x][y]);
-        uint32_t wd[4][2];
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          wd[gq][0] = pack_f16x2(acc[x][y][4 * gq + 0], acc[x][y][4 * gq + 1]);
-          wd[gq][1] = pack_f16x2(acc[x][y][4 * gq + 2], acc[x][y][4 * gq + 3]);
+        for (int g = 0; g < 4; ++g) {
+          wd[x][g][0] = pack_f16x2(acc[x][y][4 * g + 0], acc[x][y][4 * g + 1]);
+          wd[x][g][1] = pack_f16x2(acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]);
         }
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          u32x4_t chunk;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            auto r = __builtin_amdgcn_permlane32_swap(wd[2 * pp][e], wd[2 * pp + 1][e], false, false);
-            chunk[e] = r[0];
-            chunk[2 + e] = r[1];
-          }
-          const int o = x * 32 + 16 * pp + 8 * hb;    // first of the lane's 8 outputs in the block's rows
-          if (part == 0) {
-            // D[n][j]: n = o .. o+7 (features), j = jq*128 + nh*64 + y*32 + l32
-            uint16_t* dst = kn + ((int64_t)bh * s_pad + j0 + jq * 128 + nh * 64 + y * 32 + l32) * 128 + o;
-            *reinterpret_cast<u32x4_t*>(dst) = chunk;
-          } else {
-            // D[j][n]: j = jq*128 + o .. +7 (keys), n = nh*64 + y*32 + l32
-            uint16_t* dst = vt + ((int64_t)bh * 128 + nh * 64 + y * 32 + l32) * s_pad + j0 + jq * 128 + o;
-            *reinterpret_cast<u32x4_t*>(dst) = chunk;
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);     // one accumulator block at a time
       }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if ((l32 >> 4) == h) {
+          const int rr = l32 & 15;
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<u32x2_t*>(stg + rr * 256 + (((4 * x + g) ^ rr) * 16) + 8 * hb) =
+                  u32x2_t{wd[x][g][0], wd[x][g][1]};
+        }
+        // other lanes' writes are read below: no access moves across, and the
+        // writes are complete
+        lds_wave_fence();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * i + (lane >> 4), c = lane & 15;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + rr * 256 + ((c ^ rr) * 16));
+          const int row = nh * 64 + y * 32 + 16 * h + rr;   // within the tile's 256 rows / 128 features
+          if (part == 0) {
+            // K_nope row of key j0 + jq*128 + row, features 8c .. 8c+7
+            uint16_t* dst = kn + ((int64_t)bh * s_pad + j0 + jq * 128 + row) * 128 + 8 * c;
+            *reinterpret_cast<u32x4_t*>(dst) = v;
+          } else {
+            // V^T row of feature row, keys j0 + jq*128 + 8c .. +7
+            uint16_t* dst = vt + ((int64_t)bh * 128 + row) * s_pad + j0 + jq * 128 + 8 * c;
+            *reinterpret_cast<u32x4_t*>(dst) = v;
+          }
+        }
+        lds_wave_fence();                   // the reads are done before the next round's writes
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
