@@ -64,13 +64,13 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "ad854e6f0b5323e8", "fetch_kib": 424311.2, "write_kib": 264192.0,
+    "mfma_attention": {"digest": "9962d9d9c3132bd9", "fetch_kib": 424811.8, "write_kib": 264192.0,
                      "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "e118fd95b1dc5de0", "fetch_kib": 100791.4, "write_kib": 274583.8,
+    "mfma_up_projection": {"digest": "b831868b16a14817", "fetch_kib": 99232.5, "write_kib": 262144.0,
                          "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "18855f1c1ff75aa5", "fetch_kib": 1216729.7, "write_kib": 131584.0,
+    "mfma_split_kv": {"digest": "32ebbd20f275f37e", "fetch_kib": 1216720.4, "write_kib": 131584.0,
                     "fetch_factor": 0.50002, "write_factor": 1.0},
-    "lse_combine": {"digest": "d6e80c8739aea8ce", "fetch_kib": 75876.5, "write_kib": 4352.0,
+    "lse_combine": {"digest": "19c923fb09f72b2d", "fetch_kib": 75876.5, "write_kib": 4352.0,
                   "fetch_factor": 0.50002, "write_factor": 1.0},
 }
 
