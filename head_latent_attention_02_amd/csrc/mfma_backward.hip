@@ -353,10 +353,10 @@ __device__ __forceinline__ int kv_src_late(int pch, int sq_pad) {
 
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 kv_kernel(BackwardArgs a, const uint16_t* __restrict__ qf, const uint16_t* __restrict__ qft,
-           const uint16_t* __restrict__ dof, const uint16_t* __restrict__ doft, const float* __restrict__ lsdt,
-           const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vrow, const uint16_t* __restrict__ krot,
-           uint16_t* __restrict__ dkv, uint16_t* __restrict__ dkvt, float* __restrict__ dkr, int sq_pad, int n_kb,
-           int xcd_deal) {
+          const uint16_t* __restrict__ dof, const uint16_t* __restrict__ doft, const float* __restrict__ lsdt,
+          const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vrow, const uint16_t* __restrict__ krot,
+          uint16_t* __restrict__ dkv, uint16_t* __restrict__ dkvt, float* __restrict__ dkr, int sq_pad, int n_kb,
+          int xcd_deal) {
   __shared__ __attribute__((aligned(16))) uint8_t sm[KV_LDS];
   const ExplicitArgs& f = a.f;
   // XCD x (= blockIdx.x % 8) takes heads x, x + 8, ...: all key blocks of a
