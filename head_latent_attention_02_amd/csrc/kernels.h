@@ -71,8 +71,10 @@ hipError_t launch_simt_explicit(const ExplicitArgs& a, float* kn, float* v, floa
 // kn fp16 [B,H,s_pad,128], vt fp16 [B,H,128,s_pad], krot fp16 [B,s_pad,64].
 hipError_t launch_mfma_upproj(const ExplicitArgs& a, uint16_t* kn, uint16_t* vt,
                               hipStream_t stream);
-hipError_t launch_krot_f16(const ExplicitArgs& a, const float2* ktab, uint16_t* krot,
-                           hipStream_t stream);
+// The query RoPE table qtab [S_q][d_r/2] and the rotated key band krot in one
+// launch (the key table ktab [s_vis][d_r/2] as well when ktab is not null).
+hipError_t launch_rope_band(const ExplicitArgs& a, float2* qtab, float2* ktab, uint16_t* krot,
+                            hipStream_t stream);
 hipError_t launch_mfma_attention(const ExplicitArgs& a, const uint16_t* kn, const uint16_t* vt,
                                  const uint16_t* krot, const float2* qtab, hipStream_t stream);
 // Attention with the up-projection fused in: reads c_kv and w directly.

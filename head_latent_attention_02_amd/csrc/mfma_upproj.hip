@@ -236,27 +236,6 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
   }
 }
 
-// krot[b, j, :] = R(k_pe[b, j, :], kv_pos0 + j) in fp16 for j < s_pad
-// (zeros for j >= s_vis).  One thread per rotation pair.
-__global__ void krot_f16_kernel(const uint16_t* __restrict__ k_pe, const float2* __restrict__ ktab,
-                                uint16_t* __restrict__ krot, int Skv, int s_vis, int s_pad) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int b = blockIdx.y;
-  if (idx >= (int64_t)s_pad * 32) return;
-  int j = (int)(idx >> 5), m = (int)(idx & 31);
-  float ylo = 0.f, yhi = 0.f;
-  if (j < s_vis) {
-    int64_t src = ((int64_t)b * Skv + j) * 64;
-    float lo = bf16_bits_to_float(k_pe[src + m]), hi = bf16_bits_to_float(k_pe[src + m + 32]);
-    float2 cs = ktab[(int64_t)j * 32 + m];
-    ylo = lo * cs.x - hi * cs.y;
-    yhi = hi * cs.x + lo * cs.y;
-  }
-  int64_t dst = ((int64_t)b * s_pad + j) * 64;
-  krot[dst + m] = float_to_f16_bits(ylo);
-  krot[dst + m + 32] = float_to_f16_bits(yhi);
-}
-
 }  // namespace
 
 hipError_t launch_mfma_upproj(const ExplicitArgs& a, uint16_t* kn, uint16_t* vt, hipStream_t stream) {
@@ -275,15 +254,5 @@ hipError_t launch_mfma_upproj(const ExplicitArgs& a, uint16_t* kn, uint16_t* vt,
   hipLaunchKernelGGL(mfma_upproj_kernel, dim3(grid), dim3(NTHREADS), 0, stream,
                      static_cast<const uint16_t*>(a.c_kv), static_cast<const uint16_t*>(a.w), kn, vt,
                      a.B, a.H, a.Skv, a.s_vis, a.s_pad, n_jt, n_tiles, xcd_deal);
-  return hipGetLastError();
-}
-
-hipError_t launch_krot_f16(const ExplicitArgs& a, const float2* ktab, uint16_t* krot,
-                           hipStream_t stream) {
-  if (a.s_pad == 0) return hipSuccess;
-  int64_t n = (int64_t)a.s_pad * 32;
-  dim3 grid((unsigned)((n + 255) / 256), a.B);
-  hipLaunchKernelGGL(krot_f16_kernel, grid, dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(a.k_pe), ktab, krot, a.Skv, a.s_vis, a.s_pad);
   return hipGetLastError();
 }

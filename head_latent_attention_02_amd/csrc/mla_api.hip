@@ -480,7 +480,11 @@ mla_status mla_fwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
   float2* qtab = reinterpret_cast<float2*>(ws + p.off_qtab);
   float2* ktab = reinterpret_cast<float2*>(ws + p.off_ktab);
   hipError_t e;
-  {
+  if (p.fused || p.mfma) {
+    // the query table and the rotated key band (the key table is not needed)
+    TimedLaunch t("rope_band", s);
+    e = launch_rope_band(a, qtab, nullptr, reinterpret_cast<uint16_t*>(ws + p.off_krot), s);
+  } else {
     TimedLaunch t("rope_tables", s);
     e = launch_rope_table(qtab, a.q_pos0, a.Sq, a.dr, a.rope_base, s);
     if (e == hipSuccess) e = launch_rope_table(ktab, a.kv_pos0, a.s_vis, a.dr, a.rope_base, s);
@@ -488,11 +492,6 @@ mla_status mla_fwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
   if (e != hipSuccess) return hip_fail(e, "rope tables");
   if (p.fused) {
     uint16_t* kr = reinterpret_cast<uint16_t*>(ws + p.off_krot);
-    {
-      TimedLaunch t("key_rope_band", s);
-      e = launch_krot_f16(a, ktab, kr, s);
-    }
-    if (e != hipSuccess) return hip_fail(e, "key rope band");
     {
       TimedLaunch t("fused_attention", s);
       e = launch_fused_attention(a, kr, qtab, s);
@@ -507,11 +506,6 @@ mla_status mla_fwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
       e = launch_mfma_upproj(a, kn, vt, s);
     }
     if (e != hipSuccess) return hip_fail(e, "mfma up-projection");
-    {
-      TimedLaunch t("key_rope_band", s);
-      e = launch_krot_f16(a, ktab, kr, s);
-    }
-    if (e != hipSuccess) return hip_fail(e, "key rope band");
     {
       TimedLaunch t("mfma_attention", s);
       e = launch_mfma_attention(a, kn, vt, kr, qtab, s);
@@ -636,9 +630,9 @@ mla_status mla_bwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
     MfmaBwdWorkspace w;
     mfma_backward_workspace(f, &w, ws);
     {
-      TimedLaunch t("rope_tables", s);
-      e = launch_rope_table(w.qtab, f.q_pos0, f.Sq, f.dr, f.rope_base, s);
-      if (e == hipSuccess) e = launch_rope_table(w.ktab, f.kv_pos0, f.s_vis, f.dr, f.rope_base, s);
+      // both tables (the key table turns the key band's gradient back) and the key band
+      TimedLaunch t("rope_band", s);
+      e = launch_rope_band(f, w.qtab, w.ktab, w.krot, s);
     }
     if (e != hipSuccess) return hip_fail(e, "rope tables");
     {
@@ -646,11 +640,6 @@ mla_status mla_bwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
       e = launch_mfma_upproj(f, w.kn, w.vt, s);
     }
     if (e != hipSuccess) return hip_fail(e, "mfma up-projection");
-    {
-      TimedLaunch t("key_rope_band", s);
-      e = launch_krot_f16(f, w.ktab, w.krot, s);
-    }
-    if (e != hipSuccess) return hip_fail(e, "key rope band");
     {
       TimedLaunch t("bwd_prep", s);
       e = launch_bwd_prep(a, w, s);
