@@ -64,13 +64,13 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "9962d9d9c3132bd9", "fetch_kib": 424811.8, "write_kib": 264192.0,
+    "mfma_attention": {"digest": "25fe80bc34a290ad", "fetch_kib": 427186.2, "write_kib": 264192.0,
                      "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "b831868b16a14817", "fetch_kib": 99232.5, "write_kib": 262144.0,
+    "mfma_up_projection": {"digest": "062fdda03379c521", "fetch_kib": 99798.0, "write_kib": 262144.0,
                          "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "32ebbd20f275f37e", "fetch_kib": 1216720.4, "write_kib": 131584.0,
+    "mfma_split_kv": {"digest": "c02c6aa89b292ddd", "fetch_kib": 1216698.1, "write_kib": 131584.0,
                     "fetch_factor": 0.50002, "write_factor": 1.0},
-    "lse_combine": {"digest": "19c923fb09f72b2d", "fetch_kib": 75876.5, "write_kib": 4352.0,
+    "lse_combine": {"digest": "9a17e4a0062952c0", "fetch_kib": 75876.5, "write_kib": 4352.0,
                   "fetch_factor": 0.50002, "write_factor": 1.0},
 }
 
