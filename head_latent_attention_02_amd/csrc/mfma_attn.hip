@@ -19,7 +19,7 @@
 //   M(t): the MFMA stream of S(t+1) = K(t+1) Q^T (24 MFMAs) and of
 //         O^T += V^T(t) P^T(t) (16 MFMAs);
 //   V(t): the softmax of S(t) into P(t) (exponentials, row sums, running
-//         maxima, fp16 packing) and, in group 0, the tile copies.
+//         maxima, fp16 packing) and half of a tile's copies.
 // Group 1 starts one barrier late, so while one wave of a SIMD issues MFMAs
 // the other does its vector work and memory instructions: the matrix unit is
 // fed by one wave while the other's exponentials and copy issues (which hold
@@ -36,8 +36,10 @@
 //
 // Tiles.  K (64 x 192, as a K_nope part and a rope part) and V^T (128 x 64)
 // tiles are copied from global memory straight into LDS (buffer loads to LDS,
-// 16 bytes per lane) through a ring of 4 stages; the four waves of group 0
-// issue the 40 copies of a tile, 10 each, in their V phase two tiles ahead.
+// 16 bytes per lane) through a ring of 4 stages.  Each wave issues 5 of a
+// tile's 40 copies in its V phase: group 0 two tiles ahead, group 1 (one
+// phase behind) three, so both halves of a tile have two phases to land.
+// Split this way, neither group's V phase outgrows the M phase it faces.
 // In every tile row the 16-byte chunks are XOR-swizzled by row so that the
 // 16-byte operand reads of 16 consecutive lanes fall in distinct banks.
 //
@@ -56,7 +58,7 @@ namespace {
 
 constexpr int QW = 32;            // query rows per wave
 constexpr int NW = 8;             // waves per workgroup (two per SIMD)
-constexpr int NWC = 4;            // waves that issue tile copies (group 0)
+constexpr int NWC = 4;            // waves per group
 constexpr int QT = QW * NW;       // query rows per workgroup
 constexpr int KT = 64;            // keys per tile
 constexpr int DN = 128, DR = 64, DQK = 192, DV = 128;
@@ -71,17 +73,19 @@ constexpr int KS = DQK / 16;      // S k-steps (12)
 // operand reads of every k-step take one of four per-lane offsets plus a
 // constant.
 // Copy instruction g (64 lanes x 16 bytes) fills chunks 64g .. 64g+63, so each
-// instruction reads one source tensor only; copy wave w (0..3) issues
-// g = 4u + w for u = 0 .. 9, so the tensor of copy u is the same for every
-// copy wave (u < 4: K_nope, u < 6: rope, else V^T).
+// instruction reads one source tensor only; copy u = 0 .. 9 of a tile is
+// g = 4u + w for the wave w (0..3) of its group, so the tensor of copy u is the
+// same for all four (u < 4: K_nope, u < 6: rope, else V^T).  Group 0 issues
+// u = 0 .. 4, group 1 u = 5 .. 9.
 constexpr int N_SLOTS = KT * (DN / 8);    // 1024
 constexpr int R_SLOTS = KT * (DR / 8);    // 512
 constexpr int V_SLOTS = DV * (KT / 8);    // 1024
 constexpr int R0 = N_SLOTS * 8, V0 = (N_SLOTS + R_SLOTS) * 8;    // fp16 offsets of the parts
-constexpr int LPW = (N_SLOTS + R_SLOTS + V_SLOTS) / (64 * NWC); // copies per copy wave per tile (10)
+constexpr int LPW = (N_SLOTS + R_SLOTS + V_SLOTS) / (64 * NWC); // copies per wave index per tile (10)
+constexpr int HPW = LPW / 2;      // copies per wave per tile (5), one half per group
 constexpr int STAGE = (N_SLOTS + R_SLOTS + V_SLOTS) * 8;        // fp16 elements per ring stage
 constexpr int NSTAGE = 4;
-constexpr int LOOKAHEAD = 2;      // copies of tile t + 2 go out in V(t)
+constexpr int LOOKAHEAD = 2;      // group 0's copies of tile t + 2 go out in V(t), group 1's of t + 3
 constexpr float TAU = 12.f;       // log2 units: P < 2^12 in fp16
 constexpr int MPF = 4;            // operand fragments read ahead in the M phase
 constexpr int PRIO_M = 2;         // issue priority of a wave in its M phase
@@ -91,8 +95,10 @@ static_assert(LPW * 64 * NWC == N_SLOTS + R_SLOTS + V_SLOTS, "tile chunks must s
 static_assert(N_SLOTS % (64 * NWC) == 0 && R_SLOTS % (64 * NWC) == 0, "a copy round must not straddle two parts");
 static_assert(LPW * 2 < 64, "vmcnt range");
 // stage reuse: V(t) of group 0 writes the stage of tile t+2 = tile t-2, whose
-// last reader (group 1's M(t-2)) ran two barriers earlier
-static_assert(NSTAGE >= LOOKAHEAD + 2, "ring too short for the copy lookahead");
+// last reader (group 1's M(t-2)) ran two barriers earlier; V(t) of group 1
+// writes that of tile t+3 = tile t-1, whose last reader (group 1's own
+// M(t-1)) ran in the previous interval
+static_assert(NSTAGE == LOOKAHEAD + 2, "ring length and copy lookahead go together");
 
 // MFMAs with the register files pinned: S^T = K Q^T with Q^T in AGPRs and the
 // result in VGPRs; O^T += V^T P^T with O^T in AGPRs.  Inline assembly keeps the
@@ -158,8 +164,8 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool copier = wave < NWC;                    // group 0 issues the tile copies
-  const int cw = wave & (NWC - 1);                   // index among the copy waves
+  const bool lead = wave < NWC;                    // group 0 (runs one phase ahead of group 1)
+  const int cw = wave & (NWC - 1);                   // index within the group
   const int l32 = lane & 31, hb = lane >> 5;
   const int iw0 = i0 + wave * QW;
   const float c_log2 = a.scale * MLA_LOG2E;
@@ -221,12 +227,21 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
     asm volatile("" : "+s"(base));
     lds_dma_b128(rs, base + u * NWC * 1024, voff, __builtin_amdgcn_readfirstlane(so));
   };
-  auto issue_all = [&](int t) __attribute__((always_inline)) {
-    if (copier && t < ntile) static_for<LPW>([&](auto uc) __attribute__((always_inline)) { issue_copy(uc, t); });
+  // group 0 issues copies 0 .. HPW-1 of a tile, group 1 copies HPW .. LPW-1
+  auto issue_half = [&](int t) __attribute__((always_inline)) {
+    if (t >= ntile) return;
+    if (lead) static_for<HPW>([&](auto uc) __attribute__((always_inline)) { issue_copy(uc, t); });
+    else static_for<HPW>([&](auto uc) __attribute__((always_inline)) {
+      issue_copy(std::integral_constant<int, decltype(uc)::value + HPW>{}, t);
+    });
+  };
+  // group 0 is LOOKAHEAD tiles ahead, group 1 one more
+  auto issue_prologue = [&]() __attribute__((always_inline)) {
+    for (int t = 0; t < LOOKAHEAD + (lead ? 0 : 1); ++t) issue_half(t);
   };
 
   // the first tiles of the first pass are on their way while Q is loaded
-  for (int t = 0; t < LOOKAHEAD; ++t) issue_all(t);
+  issue_prologue();
 
   // ---- Q^T operand (fp16) ------------------------------------------------------
   // Lane (l32, hb) supplies query row l32 of the wave, k-slots 8hb .. 8hb+7 of
@@ -420,30 +435,49 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
     // ---- phases ---------------------------------------------------------------
     // Interval k (between two consecutive barriers) runs phase k of group 0 and
     // phase k-1 of group 1.  Phase 0 is M(-1) (S of tile 0), then V(t), M(t)
-    // for t = 0 .. ntile-1.  Tile t's copies go out in V(t-2) of group 0 (the
-    // first LOOKAHEAD tiles before the pass) and have landed when group 0
-    // leaves V(t-1): it waits for them there, before the barrier after which
-    // M(t-1) reads K(t).
-    if (pass > 0)
-      for (int t = 0; t < LOOKAHEAD; ++t) issue_all(t);
-    if (ntile > 1) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
+    // for t = 0 .. ntile-1.  Tile t is first read by group 0's M(t-1), in
+    // interval 2t.  Group 0's half goes out in its V(t-2) (interval 2t-3) and
+    // is waited for at the end of its V(t-1); group 1's half goes out in its
+    // V(t-3) (interval 2t-4) and is waited for at the end of its M(t-2)
+    // (interval 2t-1).  The first tiles go out before the pass.
+    if (pass > 0) issue_prologue();
+    // tile 0 has landed: at most the wave's copies of tiles 1 .. are in flight
+    if (lead) {
+      if (ntile > 1) wait_vmcnt<HPW>();
+      else wait_vmcnt<0>();
+    } else {
+      if (ntile > 2) wait_vmcnt<2 * HPW>();
+      else if (ntile > 1) wait_vmcnt<HPW>();
+      else wait_vmcnt<0>();
+    }
     __syncthreads();                       // tile 0 has landed; the ring's old contents are dead
-    if (!copier) barrier();                // group 1 runs one phase behind
+    if (!lead) barrier();                // group 1 runs one phase behind
     m_phase(-1);
+    // group 1: its half of tile 1 (read by group 0's M(0), in the next interval)
+    if (!lead) {
+      if (ntile > 2) wait_vmcnt<HPW>();
+      else wait_vmcnt<0>();
+    }
     for (int T = 0; T < ntile; ++T) {
       barrier();
-      issue_all(T + LOOKAHEAD);
+      issue_half(T + LOOKAHEAD + (lead ? 0 : 1));
       v_phase(T);
-      // tile T+1 has landed once at most the copies of tile T+2 are in flight
-      if (copier) {
-        if (T + LOOKAHEAD < ntile) wait_vmcnt<LPW>();
+      // group 0: its half of tile T+1 has landed once at most its copies of
+      // tile T+2 are in flight
+      if (lead) {
+        if (T + LOOKAHEAD < ntile) wait_vmcnt<HPW>();
         else wait_vmcnt<0>();
       }
       barrier();
       m_phase(T);
+      // group 1: its half of tile T+2 (first read by group 0's M(T+1), in the
+      // next interval) has landed once at most its copies of tile T+3 are in flight
+      if (!lead) {
+        if (T + LOOKAHEAD + 1 < ntile) wait_vmcnt<HPW>();
+        else wait_vmcnt<0>();
+      }
     }
-    if (copier) barrier();                 // group 0 catches up
+    if (lead) barrier();                 // group 0 catches up
     // a second pass (rare): every wave learns whether any row of the
     // workgroup saw a tile exceed its reference by more than tau
     __syncthreads();                       // every wave is done with the ring

@@ -15,7 +15,8 @@
 //
 // Persistent kernel, one workgroup of 8 waves per CU (two waves per SIMD:
 // while one is held issuing its tile copies, the other keeps the SIMD's
-// matrix unit busy).  A tile is 256 latent rows x the 256 output columns of
+// matrix unit busy; waves 0-3 issue theirs at the start of a reduction step,
+// waves 4-7 after their first 8 MFMAs of it).  A tile is 256 latent rows x the 256 output columns of
 // one head; waves 0-3 produce its K_nope half (W rows as the A operand, so
 // each lane ends with 4 consecutive features of one key) and waves 4-7 its V
 // half (latent rows as the A operand, so each lane ends with 4 consecutive
@@ -86,7 +87,7 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
   uint8_t* const stg_all = reinterpret_cast<uint8_t*>(Ls) + NSTAGE * STAGE_BYTES;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hb = lane >> 5;
   const int part = wave >> 2;          // 0: K_nope columns, 1: V columns
   const int jq = (wave >> 1) & 1;      // 128-row half of the A side
@@ -148,7 +149,8 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
       else if (newer == 1) wait_vmcnt<LOADS>();
       else wait_vmcnt<0>();
       __syncthreads();           // ... for every wave; stage g-1 is free again
-      if (g + NSTAGE - 1 < total_steps) issue_step(g + NSTAGE - 1);
+      const bool issue_now = g + NSTAGE - 1 < total_steps;
+      if (wave < 4 && issue_now) issue_step(g + NSTAGE - 1);
 
       const char* st = reinterpret_cast<const char*>(Ls) + (g % NSTAGE) * STAGE_BYTES;
 #pragma unroll
@@ -172,6 +174,8 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
 #pragma unroll
             for (int y = 0; y < 2; ++y) mfma32_agpr(acc[x][y], fa[x], fb[y]);
         }
+        // waves 4-7 issue theirs while waves 0-3 (one per SIMD) run their MFMAs
+        if (kk == 0 && wave >= 4 && issue_now) issue_step(g + NSTAGE - 1);
       }
     }
 
