@@ -64,11 +64,11 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "25fe80bc34a290ad", "fetch_kib": 427186.2, "write_kib": 264192.0,
+    "mfma_attention": {"digest": "59e7221ec81226c1", "fetch_kib": 427717.8, "write_kib": 264192.0,
                      "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "062fdda03379c521", "fetch_kib": 99798.0, "write_kib": 262144.0,
+    "mfma_up_projection": {"digest": "b07cc03d569c190c", "fetch_kib": 99912.7, "write_kib": 262144.0,
                          "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "c02c6aa89b292ddd", "fetch_kib": 1216698.1, "write_kib": 131584.0,
+    "mfma_split_kv": {"digest": "c02c6aa89b292ddd", "fetch_kib": 1216714.7, "write_kib": 131584.0,
                     "fetch_factor": 0.50002, "write_factor": 1.0},
     "lse_combine": {"digest": "9a17e4a0062952c0", "fetch_kib": 75876.5, "write_kib": 4352.0,
                   "fetch_factor": 0.50002, "write_factor": 1.0},
