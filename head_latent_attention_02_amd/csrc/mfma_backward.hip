@@ -1172,118 +1172,148 @@ __global__ void dk_pe_kernel(BackwardArgs a, const float* __restrict__ dkr, cons
 }
 
 // ---------------------------------------------------------------- gemm_nt --
-// C[m][n] = sum_k A[m][k] B[n][k] for m < M_store (rows m in [M_store, M) are
-// computed but not stored), n < N; A [M][K], B [N][K] fp16 row-major (lda = ldb
-// = K), C fp32 with row stride ldc.  M, N multiples of the tile; K a multiple
-// of 32.  Tile BM x 128, 4 waves of (BM/2) x 64, 32x32x16 MFMAs, K step 32,
-// LDS double buffer with rows padded to 40 elements.
-template <int BM>
-__global__ void __launch_bounds__(256)
-gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ C, int M,
-               int M_store, int N, int K, int64_t ldc, int64_t c_row_map_div, int64_t c_row_map_stride) {
-  constexpr int BN = 128, BK = 32, LD = 40;          // LDS row: BK fp16 plus one padding chunk
-  constexpr int WM = BM / 2, WN = 64;               // per-wave tile
-  constexpr int FM = WM / 32, FN = WN / 32;         // 32x32 blocks per wave
-  constexpr int NST = 4;                            // LDS stages
-  // stage: A rows then B rows, 16-byte chunks; whole copy instructions for 4 waves
-  constexpr int A_CH = BM * LD / 8, B_CH = BN * LD / 8;
-  constexpr int ST_CH = (A_CH + B_CH + 255) / 256 * 256;
-  constexpr int IPW = ST_CH / 64 / 4;               // copy instructions per wave per step
-  static_assert(A_CH % 64 == 0 && B_CH % 64 == 0, "parts on instruction boundaries");
-  __shared__ __attribute__((aligned(16))) uint16_t Ls[NST * ST_CH * 8];
-  const int n_tn = N / BN;
-  // XCD x (= blockIdx.x % 8) takes the row tiles x, x + 8, ..., each with all
-  // its column tiles at once: the A rows of a tile reach that XCD's L2 once
-  // for every column tile (when the row tiles split evenly over the XCDs)
-  int tm, tn;
-  if ((M / BM) % 8 == 0) {
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    tm = xcd + 8 * (slot / n_tn);
-    tn = slot % n_tn;
-  } else {
-    tm = blockIdx.x / n_tn;
-    tn = blockIdx.x % n_tn;
+// C[m][n] = sum_k A[m][k] B[n][k]: dc_kv = dKV W and dW = dKV^T c_kv.  A [M][K]
+// and B [N][K] fp16 row-major, M, N multiples of 256, K a multiple of 32.
+// Tile 256 x 256, one workgroup of 8 waves (two per SIMD); wave w computes rows
+// 128 (w & 1) .. +127 and columns 64 (w >> 1) .. +63 of the tile on 32x32x16
+// MFMAs with the accumulators in AGPRs.  The reduction streams in steps of 32
+// through a ring of 4 LDS stages (16 KB of A rows + 16 KB of B rows), filled
+// by buffer->LDS copies: waves 0-3 issue theirs at the start of a step, waves
+// 4-7 after their first 8 MFMAs of it, so one wave of each SIMD keeps the
+// matrix unit busy while the other is held issuing.  Rows of 32 elements
+// (4 chunks of 16 bytes) hold chunk c at c ^ ((r >> 2) & 3).
+// With ksplit > 1 the reduction is cut into ksplit slices of kchunk; slice s
+// writes its fp32 sum to part[s] (row-major M x N) and gemm_reduce_kernel adds
+// the slices.  Otherwise the result goes straight to C, row m at
+// (m / map_div) * map_stride + m % map_div (a batch of row blocks stored with
+// their own stride) and only rows with m % map_div < m_store.
+// Workgroups: the n_tn column tiles of one (row tile, slice) run on one XCD
+// (blockIdx.x % 8, the dispatcher's order), so its A block reaches that XCD's
+// L2 once for all of them.
+constexpr int GT = 256, GKS = 32, GNST = 4;
+constexpr int G_REG = GT * GKS * 2;                 // one operand region of a stage (16 KB)
+constexpr int G_STAGE = 2 * G_REG;
+constexpr int G_THREADS = 512;
+__global__ void __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ C,
+               float* __restrict__ part, int M, int N, int K, int kchunk, int ksplit, int m_store, int64_t ldc,
+               int64_t map_div, int64_t map_stride) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[GNST * G_STAGE / 2];
+  const int n_tm = M / GT, n_tn = N / GT;
+  const int n_groups = n_tm * ksplit;                // (row tile, slice) pairs
+  int tm, tn, sl;
+  {
+    int gi;
+    if (n_groups % 8 == 0) {
+      const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+      gi = xcd + 8 * (slot / n_tn);
+      tn = slot % n_tn;
+    } else {
+      gi = blockIdx.x / n_tn;
+      tn = blockIdx.x % n_tn;
+    }
+    tm = gi % n_tm;
+    sl = gi / n_tm;
   }
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = tm * GT, n0 = tn * GT, k0 = sl * kchunk;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hb = lane >> 5;
-  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
-  // copies: chunk p of a stage is row p / 5 (A rows, then B rows), column
-  // chunk p % 5 (chunk 4 is padding: a second copy of chunk 0)
-  const i32x4_t rs_a = make_rsrc_uniform(A + (int64_t)m0 * K, (uint32_t)BM * K * 2);
-  const i32x4_t rs_b = make_rsrc_uniform(B + (int64_t)n0 * K, (uint32_t)BN * K * 2);
-  int voff[IPW];
-#pragma unroll
-  for (int k = 0; k < IPW; ++k) {
-    int p = 64 * (IPW * wave + k) + lane;
-    if (p >= A_CH) p -= A_CH;                       // B rows (or a dummy copy past them)
-    int r = p / (LD / 8), c = p % (LD / 8);
-    if (c >= BK / 8 || r >= BN) r = c = 0;
-    voff[k] = (r * K + 8 * c) * 2;
-  }
+  const int wr = 128 * (wave & 1), wc = 64 * (wave >> 1);
+
+  // copy instruction i (0, 1) of an operand covers stage slot 512 i + tid:
+  // row 128 i + tid / 4, physical chunk tid & 3, which holds logical chunk
+  // (tid & 3) ^ ((tid >> 4) & 3) of that row
+  const int v_lane = (tid >> 2) * (K * 2) + (((tid & 3) ^ ((tid >> 4) & 3)) * 16);
+  const i32x4_t ra = make_rsrc_uniform(A + (int64_t)m0 * K, (uint32_t)GT * K * 2);
+  const i32x4_t rb = make_rsrc_uniform(B + (int64_t)n0 * K, (uint32_t)GT * K * 2);
   const uint32_t ls_lds = (uint32_t)(uintptr_t)(LDS_AS void*)&Ls[0];
-  auto issue_w = [&](auto wc, int g) __attribute__((always_inline)) {
-    constexpr int W = decltype(wc)::value;
-    const uint32_t st = __builtin_amdgcn_readfirstlane(ls_lds + (uint32_t)((g % NST) * ST_CH * 16));
-    static_for<IPW>([&](auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value, c0 = 64 * (IPW * W + k);
-      const i32x4_t& rs = c0 < A_CH ? rs_a : rs_b;
-      lds_dma_b128(rs, st + (uint32_t)c0 * 16, voff[k], __builtin_amdgcn_readfirstlane(g * BK * 2));
-    });
-  };
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int g) __attribute__((always_inline)) {
-    if (wave_u == 0) issue_w(std::integral_constant<int, 0>{}, g);
-    else if (wave_u == 1) issue_w(std::integral_constant<int, 1>{}, g);
-    else if (wave_u == 2) issue_w(std::integral_constant<int, 2>{}, g);
-    else issue_w(std::integral_constant<int, 3>{}, g);
-  };
-  f32x16_t acc[FM][FN];
+  auto issue_step = [&](int g) __attribute__((always_inline)) {
+    const uint32_t dst = ls_lds + (uint32_t)((g % GNST) * G_STAGE) + (uint32_t)wave * 1024u;
 #pragma unroll
-  for (int x = 0; x < FM; ++x)
-#pragma unroll
-    for (int y = 0; y < FN; ++y) acc[x][y] = f32x16_t{};
-  const int nk = K / BK;
-  for (int g = 0; g < NST - 1 && g < nk; ++g) issue(g);
-  for (int kk = 0; kk < nk; ++kk) {
-    // copies of step kk have landed (up to two later steps may be in flight)
-    const int newer = min(NST - 2, nk - 1 - kk);
-    if (newer == 2) wait_vmcnt<2 * IPW>();
-    else if (newer == 1) wait_vmcnt<IPW>();
+    for (int i = 0; i < 2; ++i) {
+      const int so = __builtin_amdgcn_readfirstlane(i * 128 * (K * 2) + (k0 + g * GKS) * 2);
+      lds_dma_b128(ra, dst + i * (G_THREADS * 16), v_lane, so);
+      lds_dma_b128(rb, dst + G_REG + i * (G_THREADS * 16), v_lane, so);
+    }
+  };
+  constexpr int LOADS = 4;                           // copies per wave per step
+  const int sw = (l32 >> 2) & 3;
+  const int fo0 = l32 * (GKS * 2) + ((0 + hb) ^ sw) * 16;
+  const int fo1 = l32 * (GKS * 2) + ((2 + hb) ^ sw) * 16;
+
+  f32x16_t acc[4][2];
+  const int nk = kchunk / GKS;
+  for (int g = 0; g < GNST - 1 && g < nk; ++g) issue_step(g);
+  for (int g = 0; g < nk; ++g) {
+    // the copies of step g have landed (later steps may still be in flight)
+    const int newer = min(GNST - 2, nk - 1 - g);
+    if (newer >= 2) wait_vmcnt<2 * LOADS>();
+    else if (newer == 1) wait_vmcnt<LOADS>();
     else wait_vmcnt<0>();
-    __syncthreads();                                 // ... for every wave; the stage of step kk - 1 is free
-    if (kk + NST - 1 < nk) issue(kk + NST - 1);
-    const uint16_t* As = Ls + (kk % NST) * ST_CH * 8;
-    const uint16_t* Bs = As + A_CH * 8;
+    __syncthreads();                                 // ... for every wave; the stage of step g-1 is free
+    const bool issue_now = g + GNST - 1 < nk;
+    if (wave < 4 && issue_now) issue_step(g + GNST - 1);
+    const char* st = reinterpret_cast<const char*>(Ls) + (g % GNST) * G_STAGE;
 #pragma unroll
-    for (int u = 0; u < BK / 16; ++u) {
-      f16x8_t af[FM], bf[FN];
+    for (int kk = 0; kk < 2; ++kk) {
+      const int fo = kk ? fo1 : fo0;
+      f16x8_t fa[4], fb[2];
 #pragma unroll
-      for (int x = 0; x < FM; ++x)
-        af[x] = *reinterpret_cast<const f16x8_t*>(&As[(wm + 32 * x + l32) * LD + 16 * u + 8 * hb]);
+      for (int x = 0; x < 4; ++x) fa[x] = *reinterpret_cast<const f16x8_t*>(st + (wr + 32 * x) * (GKS * 2) + fo);
 #pragma unroll
-      for (int y = 0; y < FN; ++y)
-        bf[y] = *reinterpret_cast<const f16x8_t*>(&Bs[(wn + 32 * y + l32) * LD + 16 * u + 8 * hb]);
+      for (int y = 0; y < 2; ++y)
+        fb[y] = *reinterpret_cast<const f16x8_t*>(st + G_REG + (wc + 32 * y) * (GKS * 2) + fo);
+      if (kk == 0 && g == 0) {
 #pragma unroll
-      for (int x = 0; x < FM; ++x)
+        for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int y = 0; y < FN; ++y) acc[x][y] = mfma(af[x], bf[y], acc[x][y]);
+          for (int y = 0; y < 2; ++y)
+            asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=a"(acc[x][y]) : "v"(fa[x]), "v"(fb[y]));
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 2; ++y)
+            asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc[x][y]) : "v"(fa[x]), "v"(fb[y]));
+      }
+      if (kk == 0 && wave >= 4 && issue_now) issue_step(g + GNST - 1);
     }
   }
-  // D element e of block (x, y): row wm + 32x + 8(e/4) + 4hb + e%4, column wn + 32y + l32.
-  // Row m of C sits at (m / div) * stride + m % div (a batch of row blocks
-  // stored with their own stride), so padded rows of each batch are skipped.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::);
+  // D element e of block (x, y): row wr + 32x + 8(e/4) + 4hb + e%4, column wc + 32y + l32
 #pragma unroll
-  for (int x = 0; x < FM; ++x)
+  for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < FN; ++y)
+    for (int y = 0; y < 2; ++y) {
+      asm volatile("" : "+a"(acc[x][y]));
+      const int n = n0 + wc + 32 * y + l32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm + 32 * x + 8 * (e >> 2) + 4 * hb + (e & 3);
-        const int n = n0 + wn + 32 * y + l32;
-        const int64_t mb = m / c_row_map_div, mr = m % c_row_map_div;
-        if (mr < M_store) C[(mb * c_row_map_stride + mr) * ldc + n] = acc[x][y][e];
+        const int m = m0 + wr + 32 * x + 8 * (e >> 2) + 4 * hb + (e & 3);
+        if (ksplit > 1) {
+          part[((int64_t)sl * M + m) * N + n] = acc[x][y][e];
+        } else {
+          const int64_t mb = m / map_div, mr = m % map_div;
+          if (mr < m_store) C[(mb * map_stride + mr) * ldc + n] = acc[x][y][e];
+        }
       }
+    }
+}
+
+// C (row map as in gemm_nt_kernel) = sum over the ksplit slices of part,
+// four columns per thread
+__global__ void __launch_bounds__(256)
+gemm_reduce_kernel(const float* __restrict__ part, float* __restrict__ C, int M, int N, int ksplit, int m_store,
+                   int64_t ldc, int64_t map_div, int64_t map_stride) {
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i4 >= (int64_t)M * N / 4) return;
+  const int64_t m = i4 * 4 / N, n = i4 * 4 % N;
+  const int64_t mb = m / map_div, mr = m % map_div;
+  if (mr >= m_store) return;
+  f32x4_t s = *reinterpret_cast<const f32x4_t*>(part + m * N + n);
+  for (int k = 1; k < ksplit; ++k) s += *reinterpret_cast<const f32x4_t*>(part + ((int64_t)k * M + m) * N + n);
+  *reinterpret_cast<f32x4_t*>(C + (mb * map_stride + mr) * ldc + n) = s;
 }
 
 }  // namespace
@@ -1409,6 +1439,36 @@ hipError_t launch_bwd_dkpe(const BackwardArgs& a, const MfmaBwdWorkspace& w, hip
   return hipGetLastError();
 }
 
+namespace {
+// C = A B^T on gemm_nt_kernel.  When the 256 x 256 tiles alone cannot fill the
+// CUs, the reduction is cut into up to 8 slices whose fp32 sums go to the
+// workspace's fp16 query operands (qf, dead once the two attention-backward
+// kernels have run) and are added by gemm_reduce_kernel.
+hipError_t gemm_nt(const uint16_t* A, const uint16_t* Bm, float* C, int M, int N, int K, int m_store, int64_t ldc,
+                   int64_t map_div, int64_t map_stride, const MfmaBwdWorkspace& w, const ExplicitArgs& f,
+                   hipStream_t s) {
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 256;
+  const int n_tiles = (M / GT) * (N / GT);
+  const size_t part_room = 2 * (size_t)f.B * f.H * w.sq_pad * DQK;   // bytes of qf
+  int ksplit = 1;
+  while (ksplit < 8 && n_tiles * ksplit * 2 <= n_cu && K % (2 * ksplit * GKS) == 0 && K / (2 * ksplit) >= 256 &&
+         (size_t)2 * ksplit * M * N * 4 <= part_room)
+    ksplit *= 2;
+  float* part = ksplit > 1 ? reinterpret_cast<float*>(w.qf) : nullptr;
+  hipLaunchKernelGGL(gemm_nt_kernel, dim3((unsigned)(n_tiles * ksplit)), dim3(G_THREADS), 0, s, A, Bm, C, part, M, N,
+                     K, K / ksplit, ksplit, m_store, ldc, map_div, map_stride);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ksplit == 1) return e;
+  const int64_t n4 = (int64_t)M * N / 4;
+  hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, part, C, M, N, ksplit,
+                     m_store, ldc, map_div, map_stride);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_bwd_gemms(const BackwardArgs& a, const MfmaBwdWorkspace& w, hipStream_t s) {
   const ExplicitArgs& f = a.f;
   const int B = f.B, H = f.H, sp = f.s_pad;
@@ -1422,15 +1482,12 @@ hipError_t launch_bwd_gemms(const BackwardArgs& a, const MfmaBwdWorkspace& w, hi
   }
   if (sp > 0) {
     // dc_kv[b][j][c] = sum_k dKV[b sp + j][k] W^T[c][k]   (rows j < min(sp, Skv) of each entry)
-    const int M = B * sp;
-    hipLaunchKernelGGL(gemm_nt_kernel<64>, dim3((M / 64) * (DKV / 128)), dim3(256), 0, s, w.dkv, w.wt, a.dc_kv, M,
-                       min(sp, f.Skv), DKV, H * HD, (int64_t)DKV, (int64_t)sp, (int64_t)f.Skv);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = gemm_nt(w.dkv, w.wt, a.dc_kv, B * sp, DKV, H * HD, min(sp, f.Skv), (int64_t)DKV, (int64_t)sp,
+                     (int64_t)f.Skv, w, f, s)) != hipSuccess)
+      return e;
     // dW[r][c] = sum_{b, j} dKV^T[r][b sp + j] c^T[c][b sp + j]
     const int Mw = H * HD;
-    hipLaunchKernelGGL(gemm_nt_kernel<128>, dim3((Mw / 128) * (DKV / 128)), dim3(256), 0, s, w.dkvt, w.ct, a.dw, Mw, Mw,
-                       DKV, B * sp, (int64_t)DKV, (int64_t)Mw, (int64_t)Mw);
-    return hipGetLastError();
+    return gemm_nt(w.dkvt, w.ct, a.dw, Mw, DKV, B * sp, Mw, (int64_t)DKV, (int64_t)Mw, (int64_t)Mw, w, f, s);
   }
   // no visible key: every weight gradient is zero
   const int64_t n = (int64_t)H * HD * DKV;
