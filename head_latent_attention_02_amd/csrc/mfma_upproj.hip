@@ -115,28 +115,43 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
   const int a_rows = (part == 0) ? (REG_BYTES + 0) : (jq * 128 * TK * 2);
   const int b_rows = (part == 0) ? ((jq * 128 + nh * 64) * TK * 2) : (REG_BYTES + (128 + nh * 64) * TK * 2);
 
-  // issue the copies of global reduction step g (tile g / NKS, step g % NKS)
-  auto issue_step = [&](int g) {
-    const int t = g / NKS, ks = g - t * NKS;
+  // Copy-issue state: the step issued next is step is_ks of the block's
+  // tile is_t, into ring stage is_stage; ra / rb address that tile's latent
+  // rows and W rows and change only when the issue moves on to a new tile, so
+  // the per-step issue is the copies alone.
+  int is_t = 0, is_ks = 0, is_stage = 0;
+  i32x4_t ra, rb;
+  auto set_issue_tile = [&](int t) {
     int bh, jt;
     tile_coords((int)blockIdx.x + t * G, n_jt, xcd_deal != 0, bh, jt);
     const int h = bh % H, b = bh / H;
     const int j0 = jt * TJ;
     const int rows = max(0, min(TJ, s_vis - j0));
-    const i32x4_t ra = make_rsrc_uniform(c_kv + ((int64_t)b * Skv + j0) * DKV, (uint32_t)rows * (DKV * 2));
-    const i32x4_t rb = make_rsrc_uniform(w + (int64_t)h * TN * DKV, (uint32_t)TN * (DKV * 2));
-    const uint32_t dst = ls_lds + (uint32_t)((g % NSTAGE) * STAGE_BYTES) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+    ra = make_rsrc_uniform(c_kv + ((int64_t)b * Skv + j0) * DKV, (uint32_t)rows * (DKV * 2));
+    rb = make_rsrc_uniform(w + (int64_t)h * TN * DKV, (uint32_t)TN * (DKV * 2));
+  };
+  auto issue_next = [&]() {
+    const uint32_t dst = ls_lds + (uint32_t)(is_stage * STAGE_BYTES) + (uint32_t)wave * 1024u;
 #pragma unroll
     for (int i = 0; i < LOADS / 2; ++i) {
-      const int so = __builtin_amdgcn_readfirstlane(i * COPY_ROWS * (DKV * 2) + ks * (TK * 2));
+      const int so = i * COPY_ROWS * (DKV * 2) + is_ks * (TK * 2);
       lds_dma_b128(ra, dst + i * (NTHREADS * 16), v_lane, so);
       lds_dma_b128(rb, dst + REG_BYTES + i * (NTHREADS * 16), v_lane, so);
     }
   };
+  auto advance_issue = [&]() {
+    is_stage = (is_stage + 1) & (NSTAGE - 1);
+    if (++is_ks == NKS) {
+      is_ks = 0;
+      if (++is_t < my_tiles) set_issue_tile(is_t);
+    }
+  };
+  static_assert((NSTAGE & (NSTAGE - 1)) == 0, "ring depth is a power of two");
 
   f32x16_t acc[4][2];
   const int ahead = min(NSTAGE - 1, total_steps);
-  for (int g = 0; g < ahead; ++g) issue_step(g);
+  if (my_tiles > 0) set_issue_tile(0);
+  for (int g = 0; g < ahead; ++g) { issue_next(); advance_issue(); }
 
   for (int t = 0; t < my_tiles; ++t) {
     for (int ks = 0; ks < NKS; ++ks) {
@@ -150,7 +165,7 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
       else wait_vmcnt<0>();
       __syncthreads();           // ... for every wave; stage g-1 is free again
       const bool issue_now = g + NSTAGE - 1 < total_steps;
-      if (wave < 4 && issue_now) issue_step(g + NSTAGE - 1);
+      if (wave < 4 && issue_now) issue_next();
 
       const char* st = reinterpret_cast<const char*>(Ls) + (g % NSTAGE) * STAGE_BYTES;
 #pragma unroll
@@ -175,8 +190,9 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
             for (int y = 0; y < 2; ++y) mfma32_agpr(acc[x][y], fa[x], fb[y]);
         }
         // waves 4-7 issue theirs while waves 0-3 (one per SIMD) run their MFMAs
-        if (kk == 0 && wave >= 4 && issue_now) issue_step(g + NSTAGE - 1);
+        if (kk == 0 && wave >= 4 && issue_now) issue_next();
       }
+      if (issue_now) advance_issue();
     }
 
     // epilogue (the next tile's first steps are already in flight): the
