@@ -349,6 +349,12 @@ DEC_EDGE = [
     (I.small_decode("heads48", batch=2, cache_len=300, n_heads=48, n_splits=4, seed=205), [300, 45], None),
     (I.small_decode("heads64", batch=2, cache_len=257, n_heads=64, n_splits=2, seed=206), [257, 33], None),
     (I.small_decode("heads112", batch=2, cache_len=200, n_heads=112, n_splits=5, seed=207), [200, 199], None),
+    # the full head count and split count of the decode workload with ragged
+    # lengths: whole chunks of 4 tiles plus a 4-token tail (2100), a single
+    # row (1, fifteen empty chunks), chunks of 2 or 3 rows (31, 33), and an
+    # odd length whose chunks end mid-tile (1057)
+    (I.small_decode("heads128_ragged", batch=6, cache_len=2100, n_heads=128, n_splits=16, seed=208),
+     [2100, 0, 1, 31, 33, 1057], None),
 ]
 
 
