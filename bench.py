@@ -20,6 +20,10 @@ Two timed regions of K steps each follow the warm-up:
      bit-identical to the eager result) and replayed K times: the step time,
      `value`, tokens/s and GB/s, without per-launch host overhead between the
      kernels.  `--no-graph` reports the eager region's step time instead.
+After the graph region each captured step replays back to back for about a
+second while a side thread reads the graphics clock through amdsmi; the
+matrix-unit fractions are also given against the peak scaled to that clock
+(`clock`, `roofline.frac_at_clock`), since the quoted peak assumes 2.4 GHz.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--copy-calibration]
@@ -38,6 +42,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -47,6 +52,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 / fp16
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_CLOCK_MHZ = 2400.0        # the shader clock the matrix peak is quoted at
 METRIC = "MLA attn fwd TFLOP/s (+% MFMA peak) at V3 dims; absorbed decode tok/s (+% HBM)"
 COPY_CALIBRATION_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 
@@ -445,6 +451,53 @@ def absorbed_forward(mla, torch, ecfg, t, fl, args):
             "workspace": mem, "gap_bytes_per_token": slope}
 
 
+def clock_under_load(torch, replay, seconds=1.0):
+    """Median graphics (shader) clock in MHz while `replay` runs back to back
+    for about `seconds`: amdsmi's current SYS clock polled every 10 ms from a
+    side thread.  Returns None (with the reason) when amdsmi is unavailable."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:  # no amdsmi module or no access to the driver
+        return {"error": f"amdsmi unavailable: {e}"}
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        dev = torch.cuda.current_device()
+        if not handles:
+            return {"error": "amdsmi lists no GPU"}
+        h = handles[dev] if dev < len(handles) else handles[0]
+        samples, stop = [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                try:
+                    clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)["clk"]
+                    if isinstance(clk, (int, float)) and clk > 0:
+                        samples.append(float(clk))
+                except Exception:
+                    pass
+                time.sleep(0.01)
+
+        th = threading.Thread(target=poll, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                replay()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        if not samples:
+            return {"error": "no clock samples"}
+        return {"sclk_mhz_median": float(np.median(samples)), "sclk_mhz_min": min(samples),
+                "sclk_mhz_max": max(samples), "samples": len(samples)}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -637,6 +690,7 @@ def main():
     d_ms = float(np.mean(dec_ms))
     eager = {"ms_per_step": ms_step, "explicit_ms": e_ms, "decode_ms": d_ms}
     graph = None
+    clocks = None
     if not args.no_graph:
         # the reference outputs of one eager step
         step(False)
@@ -690,6 +744,11 @@ def main():
         d_ms = float(np.mean(g_dec_ms))
         graph = {"ms_per_step": ms_step, "explicit_ms": e_ms, "decode_ms": d_ms,
                  "check": "replay bit-identical to the eager step"}
+        log("graphics clock under each step's load (amdsmi, after the timed region)")
+        clocks = {"explicit": clock_under_load(torch, g_exp.replay), "decode": clock_under_load(torch, g_dec.replay),
+                  "source": "amdsmi_get_clock_info(SYS) polled every 10 ms while the captured step replays "
+                            "back to back for about 1 s, after the timed region",
+                  "peak_clock_mhz": PEAK_CLOCK_MHZ}
     fl = ecfg.flops()
     dflops = dcfg.flops()
     dbytes = dcfg.algorithmic_bytes()
@@ -730,6 +789,13 @@ def main():
                 "source_digest": source_digest(name)}
 
     roofline = roof("mfma_attention", "mfma", "TFLOP/s", fl["attention"], PEAK_MFMA_TFLOPS)
+    # the matrix peak scales with the shader clock: the same rate against the
+    # peak at the clock measured under this step's load
+    clk = (clocks or {}).get("explicit") or {}
+    if roofline is not None and "sclk_mhz_median" in clk:
+        pk = PEAK_MFMA_TFLOPS * clk["sclk_mhz_median"] / PEAK_CLOCK_MHZ
+        roofline["peak_at_clock"] = pk
+        roofline["frac_at_clock"] = roofline["achieved"] / pk
     roofline_decode = roof("mfma_split_kv", "hbm", "GB/s", dbytes["cache"], PEAK_HBM_GBS)
 
     res = {
@@ -758,7 +824,10 @@ def main():
             "arithmetic": "bf16 inputs; up-projection bf16 MFMA; attention QK^T/PV fp16 MFMA; decode bf16 MFMA; "
                           "fp32 accumulate and fp32 outputs",
         },
-        "explicit": {"ms": e_ms, "tflops": explicit_tflops, "frac_mfma_peak": explicit_tflops / PEAK_MFMA_TFLOPS},
+        "explicit": {"ms": e_ms, "tflops": explicit_tflops, "frac_mfma_peak": explicit_tflops / PEAK_MFMA_TFLOPS,
+                     "frac_mfma_peak_at_clock": (explicit_tflops / (PEAK_MFMA_TFLOPS * clk["sclk_mhz_median"]
+                                                                    / PEAK_CLOCK_MHZ)
+                                                 if "sclk_mhz_median" in clk else None)},
         "decode": {"ms": d_ms, "tok_per_s": decode_tok_s, "algorithmic_gbs": decode_gbs,
                    "frac_hbm_peak": decode_gbs / PEAK_HBM_GBS},
         "roofline": roofline,
@@ -766,6 +835,7 @@ def main():
         "kernels": kernels,
         "timing": {"step": "hip_graph_replay" if graph is not None else "eager", "eager": eager,
                    "graph": graph},
+        "clock": clocks,
     }
 
     res["context"] = CONTEXT
