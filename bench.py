@@ -20,8 +20,9 @@ Two timed regions of K steps each follow the warm-up:
      bit-identical to the eager result) and replayed K times: the step time,
      `value`, tokens/s and GB/s, without per-launch host overhead between the
      kernels.  `--no-graph` reports the eager region's step time instead.
-After the graph region each captured step replays back to back for about a
-second while a side thread reads the graphics clock through amdsmi; the
+After the graph region each captured step replays back to back for about two
+seconds while a side thread reads the graphics clock and the socket power
+through amdsmi; the
 matrix-unit fractions are also given against the peak scaled to that clock
 (`clock`, `roofline.frac_at_clock`), since the quoted peak assumes 2.4 GHz.
 
@@ -451,10 +452,12 @@ def absorbed_forward(mla, torch, ecfg, t, fl, args):
             "workspace": mem, "gap_bytes_per_token": slope}
 
 
-def clock_under_load(torch, replay, seconds=1.0):
+def clock_under_load(torch, replay, seconds=2.0):
     """Median graphics (shader) clock in MHz while `replay` runs back to back
     for about `seconds`: amdsmi's current SYS clock polled every 10 ms from a
-    side thread.  Returns None (with the reason) when amdsmi is unavailable."""
+    side thread, with the socket power and its cap from the same polls (the
+    medians of the second half of the samples).
+    Returns the reason instead when amdsmi is unavailable."""
     try:
         import amdsmi
         amdsmi.amdsmi_init()
@@ -466,7 +469,7 @@ def clock_under_load(torch, replay, seconds=1.0):
         if not handles:
             return {"error": "amdsmi lists no GPU"}
         h = handles[dev] if dev < len(handles) else handles[0]
-        samples, stop = [], threading.Event()
+        samples, power, limit, stop = [], [], [], threading.Event()
 
         def poll():
             while not stop.is_set():
@@ -474,6 +477,14 @@ def clock_under_load(torch, replay, seconds=1.0):
                     clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)["clk"]
                     if isinstance(clk, (int, float)) and clk > 0:
                         samples.append(float(clk))
+                    pw = amdsmi.amdsmi_get_power_info(h)
+                    cur = pw.get("current_socket_power", "N/A")
+                    if cur in ("N/A", 0):
+                        cur = pw.get("socket_power", "N/A")
+                    if isinstance(cur, (int, float)) and cur > 0:
+                        power.append(float(cur))
+                    if isinstance(pw.get("power_limit"), (int, float)) and pw["power_limit"] > 0:
+                        limit.append(float(pw["power_limit"]))
                 except Exception:
                     pass
                 time.sleep(0.01)
@@ -489,8 +500,18 @@ def clock_under_load(torch, replay, seconds=1.0):
         th.join()
         if not samples:
             return {"error": "no clock samples"}
-        return {"sclk_mhz_median": float(np.median(samples)), "sclk_mhz_min": min(samples),
-                "sclk_mhz_max": max(samples), "samples": len(samples)}
+        # the second half only: the power reading is a trailing average, and
+        # the clock settles once the load has run for a while
+        samples, power, limit = samples[len(samples) // 2:], power[len(power) // 2:], limit[len(limit) // 2:]
+        r = {"sclk_mhz_median": float(np.median(samples)), "sclk_mhz_min": min(samples),
+             "sclk_mhz_max": max(samples), "samples": len(samples)}
+        if power:
+            r["socket_power_w_median"] = float(np.median(power))
+        if limit:
+            # amdsmi reports the cap in microwatts on some releases and in watts on others
+            lim = float(np.median(limit))
+            r["power_limit_w"] = lim / 1e6 if lim > 1e5 else lim
+        return r
     finally:
         try:
             amdsmi.amdsmi_shut_down()
@@ -746,8 +767,9 @@ def main():
                  "check": "replay bit-identical to the eager step"}
         log("graphics clock under each step's load (amdsmi, after the timed region)")
         clocks = {"explicit": clock_under_load(torch, g_exp.replay), "decode": clock_under_load(torch, g_dec.replay),
-                  "source": "amdsmi_get_clock_info(SYS) polled every 10 ms while the captured step replays "
-                            "back to back for about 1 s, after the timed region",
+                  "source": "amdsmi_get_clock_info(SYS) and amdsmi_get_power_info polled every 10 ms while the "
+                            "captured step replays back to back for about 2 s after the timed region; "
+                            "medians of the second second",
                   "peak_clock_mhz": PEAK_CLOCK_MHZ}
     fl = ecfg.flops()
     dflops = dcfg.flops()
