@@ -198,7 +198,9 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
     // epilogue (the next tile's first steps are already in flight): the
     // wave's 64 output rows (keys of K_nope, features of V^T) go out in four
     // rounds of 16 rows, each staged in the wave's 4 KB of LDS so that every
-    // store writes whole 256-byte row segments.  In a 32x32 block lane
+    // store writes whole 256-byte row segments.  The stores are non-temporal,
+    // so that the 4 MB an XCD writes per round of tiles does not push the
+    // latent rows, which the XCD's next tiles read again, out of its L2.  In a 32x32 block lane
     // (l32, hb) holds, for each group g, 4 consecutive outputs of row l32 at
     // column 8g + 4hb of the block; a staged row's 16-byte chunks are
     // XOR-swizzled by the row, which keeps both the 8-byte writes and the
@@ -242,11 +244,11 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
           if (part == 0) {
             // K_nope row of key j0 + jq*128 + row, features 8c .. 8c+7
             uint16_t* dst = kn + ((int64_t)bh * s_pad + j0 + jq * 128 + row) * 128 + 8 * c;
-            *reinterpret_cast<u32x4_t*>(dst) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
           } else {
             // V^T row of feature row, keys j0 + jq*128 + 8c .. +7
             uint16_t* dst = vt + ((int64_t)bh * 128 + row) * s_pad + j0 + jq * 128 + 8 * c;
-            *reinterpret_cast<u32x4_t*>(dst) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
           }
         }
         lds_wave_fence();                   // the reads are done before the next round's writes
