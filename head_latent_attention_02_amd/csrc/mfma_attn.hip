@@ -503,7 +503,9 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
   // ---- epilogue ---------------------------------------------------------------
   // O = O^T / l goes row-major through this wave's part of the idle ring (rows
   // padded by 16 bytes against bank conflicts), so that every store to global
-  // memory covers whole output rows.
+  // memory covers whole output rows.  The stores are non-temporal: the output
+  // is not read again here, and the K/V tiles the XCD's other query tiles
+  // still read keep their place in its L2.
   constexpr int OB = (OT == MLA_FP32) ? 4 : 2;                 // bytes per output element
   constexpr int OROW = DV * OB, OSTR = OROW + 16;              // row bytes, LDS row stride
   static_assert(NW * QW * OSTR <= NSTAGE * STAGE * 2, "output staging must fit in the ring");
@@ -546,8 +548,8 @@ mfma_attention_kernel(ExplicitArgs a, const uint16_t* __restrict__ kn, const uin
     const int i = iw0 + row;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ob + row * OSTR + 16 * c);
     if (i < a.Sq)
-      *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(a.out) +
-                                  (((int64_t)b * a.Sq + i) * a.H + h) * OROW + 16 * c) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(a.out) +
+                                                                (((int64_t)b * a.Sq + i) * a.H + h) * OROW + 16 * c));
   }
   {
     const int i = iw0 + l32e;
