@@ -146,6 +146,21 @@ __device__ __forceinline__ void lds_dma_b128(i32x4_t rsrc, uint32_t lds_addr, in
       : "memory");
 }
 
+// The same copy with the non-temporal hint (data read once: it should not
+// displace what the CU's neighbours read again from L2).
+__device__ __forceinline__ void lds_dma_b128_nt(i32x4_t rsrc, uint32_t lds_addr, int voffset, int soffset = 0) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
+
 // Buffer resource for `bytes` bytes at `base` (gfx9 data-format word).
 __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
   uint64_t p = reinterpret_cast<uint64_t>(base);

@@ -141,7 +141,9 @@ absorb_mfma_kernel(DecodeArgs a, uint16_t* __restrict__ qt) {
 // (chunk, sequence).  The chunk's cache rows stream through a ring of 4 LDS
 // tile buffers of 32 tokens x 576 latent columns, filled by direct
 // buffer->LDS loads (every lane issues 9 loads of 16 bytes per tile; 2 to 3
-// tiles are in flight while one is computed).  Each tile goes through two
+// tiles are in flight while one is computed).  The loads carry the
+// non-temporal hint: each cache row is read once, and the step's small
+// operands (q~, W_kv_b, the partials) then stay in the caches.  Each tile goes through two
 // products:
 //
 //   scores: wave w owns head groups 2w and 2w+1 (32 heads, q~ in VGPRs) and
@@ -268,7 +270,7 @@ mfma_splitkv_kernel(DecodeArgs a, const uint16_t* __restrict__ qt, float* __rest
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int voff_i = (int)((i & 1) ? (slot_off[i >> 1] >> 16) : (slot_off[i >> 1] & 0xffffu));
-      lds_dma_b128(rsrc, dst + i * 1024, voff_i, tbyte);
+      lds_dma_b128_nt(rsrc, dst + i * 1024, voff_i, tbyte);
     }
   };
   // wait until the loads of tile `tile` (issued in order) have landed, given
