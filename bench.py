@@ -71,14 +71,14 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "59e7221ec81226c1", "fetch_kib": 427717.8, "write_kib": 264192.0,
+    "mfma_attention": {"digest": "f89189f8df4a43fe", "fetch_kib": 399489.1, "write_kib": 264194.2,
+                      "fetch_factor": 0.50002, "write_factor": 1.0},
+    "mfma_up_projection": {"digest": "f2073c3b471b65cf", "fetch_kib": 43342.3, "write_kib": 262511.2,
+                          "fetch_factor": 0.50002, "write_factor": 1.0},
+    "mfma_split_kv": {"digest": "14ab2cf9c5b52bf5", "fetch_kib": 1216709.1, "write_kib": 131584.0,
                      "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "b07cc03d569c190c", "fetch_kib": 99912.7, "write_kib": 262144.0,
-                         "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "c02c6aa89b292ddd", "fetch_kib": 1216714.7, "write_kib": 131584.0,
-                    "fetch_factor": 0.50002, "write_factor": 1.0},
-    "lse_combine": {"digest": "9a17e4a0062952c0", "fetch_kib": 75876.5, "write_kib": 4352.0,
-                  "fetch_factor": 0.50002, "write_factor": 1.0},
+    "lse_combine": {"digest": "48c52d59877d4e83", "fetch_kib": 75877.4, "write_kib": 4352.0,
+                   "fetch_factor": 0.50002, "write_factor": 1.0},
 }
 
 
@@ -535,6 +535,8 @@ def parse():
                    help="approximate CPU seconds for the oracle baseline sample")
     p.add_argument("--no-absorbed", action="store_true",
                    help="skip the absorbed-form forward of the explicit workload")
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the graphics-clock probe after the timed region (it replays each step for ~2 s)")
     p.add_argument("--no-graph", action="store_true",
                    help="time the step as eager calls (no HIP graph replay)")
     p.add_argument("--no-configs", action="store_true",
@@ -765,6 +767,7 @@ def main():
         d_ms = float(np.mean(g_dec_ms))
         graph = {"ms_per_step": ms_step, "explicit_ms": e_ms, "decode_ms": d_ms,
                  "check": "replay bit-identical to the eager step"}
+    if graph is not None and not args.no_clock:
         log("graphics clock under each step's load (amdsmi, after the timed region)")
         clocks = {"explicit": clock_under_load(torch, g_exp.replay), "decode": clock_under_load(torch, g_dec.replay),
                   "source": "amdsmi_get_clock_info(SYS) and amdsmi_get_power_info polled every 10 ms while the "
