@@ -526,8 +526,8 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--explicit-config", default="v3_bf16")
     p.add_argument("--decode-config", default="v3_decode_b64_32k")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -711,6 +711,7 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     e_ms = float(np.mean(exp_ms))
     d_ms = float(np.mean(dec_ms))
+    e_med, d_med = float(np.median(exp_ms)), float(np.median(dec_ms))
     eager = {"ms_per_step": ms_step, "explicit_ms": e_ms, "decode_ms": d_ms}
     graph = None
     clocks = None
@@ -765,6 +766,7 @@ def main():
         ms_step = (t1 - t0) * 1e3 / args.steps
         e_ms = float(np.mean(g_exp_ms))
         d_ms = float(np.mean(g_dec_ms))
+        e_med, d_med = float(np.median(g_exp_ms)), float(np.median(g_dec_ms))
         graph = {"ms_per_step": ms_step, "explicit_ms": e_ms, "decode_ms": d_ms,
                  "check": "replay bit-identical to the eager step"}
     if graph is not None and not args.no_clock:
@@ -849,11 +851,12 @@ def main():
             "arithmetic": "bf16 inputs; up-projection bf16 MFMA; attention QK^T/PV fp16 MFMA; decode bf16 MFMA; "
                           "fp32 accumulate and fp32 outputs",
         },
-        "explicit": {"ms": e_ms, "tflops": explicit_tflops, "frac_mfma_peak": explicit_tflops / PEAK_MFMA_TFLOPS,
+        "explicit": {"ms": e_ms, "ms_median": e_med, "tflops": explicit_tflops,
+                     "frac_mfma_peak": explicit_tflops / PEAK_MFMA_TFLOPS,
                      "frac_mfma_peak_at_clock": (explicit_tflops / (PEAK_MFMA_TFLOPS * clk["sclk_mhz_median"]
                                                                     / PEAK_CLOCK_MHZ)
                                                  if "sclk_mhz_median" in clk else None)},
-        "decode": {"ms": d_ms, "tok_per_s": decode_tok_s, "algorithmic_gbs": decode_gbs,
+        "decode": {"ms": d_ms, "ms_median": d_med, "tok_per_s": decode_tok_s, "algorithmic_gbs": decode_gbs,
                    "frac_hbm_peak": decode_gbs / PEAK_HBM_GBS},
         "roofline": roofline,
         "roofline_decode": roofline_decode,
