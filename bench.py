@@ -452,6 +452,24 @@ def absorbed_forward(mla, torch, ecfg, t, fl, args):
             "workspace": mem, "gap_bytes_per_token": slope}
 
 
+def summarise_clock(samples, power, limit):
+    """Medians of the second half of the polled clock (MHz), socket power (W)
+    and power cap: the power reading is a trailing average, and the clock
+    settles once the load has run for a while.  amdsmi reports the cap in
+    microwatts on some releases and in watts on others."""
+    if not samples:
+        return {"error": "no clock samples"}
+    samples, power, limit = samples[len(samples) // 2:], power[len(power) // 2:], limit[len(limit) // 2:]
+    r = {"sclk_mhz_median": float(np.median(samples)), "sclk_mhz_min": min(samples),
+         "sclk_mhz_max": max(samples), "samples": len(samples)}
+    if power:
+        r["socket_power_w_median"] = float(np.median(power))
+    if limit:
+        lim = float(np.median(limit))
+        r["power_limit_w"] = lim / 1e6 if lim > 1e5 else lim
+    return r
+
+
 def clock_under_load(torch, replay, seconds=2.0):
     """Median graphics (shader) clock in MHz while `replay` runs back to back
     for about `seconds`: amdsmi's current SYS clock polled every 10 ms from a
@@ -498,20 +516,7 @@ def clock_under_load(torch, replay, seconds=2.0):
             torch.cuda.synchronize()
         stop.set()
         th.join()
-        if not samples:
-            return {"error": "no clock samples"}
-        # the second half only: the power reading is a trailing average, and
-        # the clock settles once the load has run for a while
-        samples, power, limit = samples[len(samples) // 2:], power[len(power) // 2:], limit[len(limit) // 2:]
-        r = {"sclk_mhz_median": float(np.median(samples)), "sclk_mhz_min": min(samples),
-             "sclk_mhz_max": max(samples), "samples": len(samples)}
-        if power:
-            r["socket_power_w_median"] = float(np.median(power))
-        if limit:
-            # amdsmi reports the cap in microwatts on some releases and in watts on others
-            lim = float(np.median(limit))
-            r["power_limit_w"] = lim / 1e6 if lim > 1e5 else lim
-        return r
+        return summarise_clock(samples, power, limit)
     finally:
         try:
             amdsmi.amdsmi_shut_down()

@@ -55,3 +55,16 @@ def test_host_info_and_pool_size(monkeypatch):
     assert bench.pool_size() == min(3, info["cpus_visible"])
     monkeypatch.delenv("OMP_NUM_THREADS")
     assert 1 <= bench.pool_size() <= 16
+
+
+def test_clock_summary_uses_the_settled_half():
+    """The clock probe keeps the second half of its samples (the first half is
+    the ramp and the power sensor's trailing average) and reads the power cap
+    in watts whether amdsmi reports watts or microwatts."""
+    b = bench
+    clk = [2400.0] * 50 + [1800.0] * 49 + [1900.0]
+    r = b.summarise_clock(clk, [300.0] * 50 + [1390.0] * 50, [1.4e9] * 100)
+    assert r["sclk_mhz_median"] == 1800.0 and r["sclk_mhz_max"] == 1900.0 and r["samples"] == 50
+    assert r["socket_power_w_median"] == 1390.0 and r["power_limit_w"] == 1400.0
+    assert b.summarise_clock([2000.0, 2000.0], [], [1400.0])["power_limit_w"] == 1400.0
+    assert "error" in b.summarise_clock([], [], [])
