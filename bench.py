@@ -71,13 +71,13 @@ KERNEL_SOURCES = {
 # source_digest() of the kernel's sources when the counters were taken.
 HBM_COUNTERS: dict = {
     # taken with the sources of digest below; see profiles/hbm_traffic_counters.md
-    "mfma_attention": {"digest": "f89189f8df4a43fe", "fetch_kib": 399489.1, "write_kib": 264194.2,
+    "mfma_attention": {"digest": "3d5f6139de14b62c", "fetch_kib": 400906.3, "write_kib": 264192.7,
                       "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_up_projection": {"digest": "f2073c3b471b65cf", "fetch_kib": 43342.3, "write_kib": 262511.2,
+    "mfma_up_projection": {"digest": "e5764d858299461f", "fetch_kib": 43514.0, "write_kib": 262475.5,
                           "fetch_factor": 0.50002, "write_factor": 1.0},
-    "mfma_split_kv": {"digest": "14ab2cf9c5b52bf5", "fetch_kib": 1216709.1, "write_kib": 131584.0,
+    "mfma_split_kv": {"digest": "07a5151308c08d0f", "fetch_kib": 1216703.3, "write_kib": 131584.0,
                      "fetch_factor": 0.50002, "write_factor": 1.0},
-    "lse_combine": {"digest": "48c52d59877d4e83", "fetch_kib": 75877.4, "write_kib": 4352.0,
+    "lse_combine": {"digest": "505b7a7a5042aa17", "fetch_kib": 75877.3, "write_kib": 4352.0,
                    "fetch_factor": 0.50002, "write_factor": 1.0},
 }
 

@@ -68,9 +68,10 @@ hipError_t launch_simt_explicit(const ExplicitArgs& a, float* kn, float* v, floa
                                 const float2* qtab, const float2* ktab, hipStream_t stream);
 
 // ---- MFMA explicit path ---------------------------------------------------
-// kn fp16 [B,H,s_pad,128], vt fp16 [B,H,128,s_pad], krot fp16 [B,s_pad,64].
+// kn fp16 [B,H,s_pad,128], vt fp16 [B,H,128,s_pad] (or, with v_rows, V in
+// rows [B,H,s_pad,128]), krot fp16 [B,s_pad,64].
 hipError_t launch_mfma_upproj(const ExplicitArgs& a, uint16_t* kn, uint16_t* vt,
-                              hipStream_t stream);
+                              hipStream_t stream, bool v_rows = false);
 // The query RoPE table qtab [S_q][d_r/2] and the rotated key band krot in one
 // launch (the key table ktab [s_vis][d_r/2] as well when ktab is not null).
 hipError_t launch_rope_band(const ExplicitArgs& a, float2* qtab, float2* ktab, uint16_t* krot,
@@ -92,16 +93,16 @@ struct SimtBwdWorkspace {
 hipError_t launch_simt_backward(const BackwardArgs& a, const SimtBwdWorkspace& w, hipStream_t stream);
 
 // MFMA path (bf16 inputs, d_kv 512, d_nope 128, d_rope 64, d_v 128).  fp16
-// workspace tensors: the forward's kn [bh][s_pad][128], vt [bh][128][s_pad],
-// krot [b][s_pad][64]; Q = [q_nope ; R(q_pe)] as qf [bh][sq_pad][192] and
+// workspace tensors: the up-projection's kn [bh][s_pad][128] and vrow
+// [bh][s_pad][128] (V in rows), krot [b][s_pad][64]; Q = [q_nope ; R(q_pe)] as qf [bh][sq_pad][192] and
 // qft [bh][192][sq_pad]; dO as dof [bh][sq_pad][128] and doft
-// [bh][128][sq_pad]; vrow [bh][s_pad][128]; knt [bh][128][s_pad]; krt
+// [bh][128][sq_pad]; knt [bh][128][s_pad]; krt
 // [b][64][s_pad]; dkv [b][s_pad][H*256] and dkvt [H*256][b*s_pad] ([dK_nope |
 // dV] per head, scaled); wt [512][H*256]; ct [512][b*s_pad].  fp32: dvec
 // [bh][sq_pad] (dO . out), dkr [bh][s_pad][64].  sq_pad = s_q rounded up to 128.
 struct MfmaBwdWorkspace {
   float2 *qtab, *ktab;
-  uint16_t *kn, *vt, *krot, *qf, *qft, *dof, *doft, *vrow, *knt, *krt, *dkv, *dkvt, *wt, *ct;
+  uint16_t *kn, *krot, *qf, *qft, *dof, *doft, *vrow, *knt, *krt, *dkv, *dkvt, *wt, *ct;
   float *dvec, *dkr;
   float* lsdt;        // per 32-query tile: LSE then D, 32 each, in the permuted row order
   int sq_pad;

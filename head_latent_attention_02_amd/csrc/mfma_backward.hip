@@ -16,8 +16,8 @@
 //   prep_q      fp16 Q = [q_nope ; R(q_pe)] and dO in row layout [bh][i][d] and
 //               transposed layout [bh][d][i] (query rows padded to 128 with
 //               zeros), and D = dO . out in fp32.
-//   transpose   V [bh][key][128] from the up-projection's V^T, K_nope^T, the
-//               rotated key band transposed, W^T and c_kv^T (fp16).
+//   transpose   K_nope^T, the rotated key band transposed, W^T and c_kv^T
+//               (fp16); V comes from the up-projection in rows [bh][key][128].
 //   kv          per (b, h, 128 keys): 8 waves, two per 32-key block sharing a
 //               SIMD: one holds K and computes S = Q K^T, P and dV^T += dO^T P,
 //               the other holds V and computes dP = dO V^T, dS and
@@ -1330,7 +1330,6 @@ size_t mfma_backward_workspace(const ExplicitArgs& f, MfmaBwdWorkspace* w, char*
   p = take(8 * (size_t)f.Sq * 32);             if (w) w->qtab = reinterpret_cast<float2*>(p);
   p = take(8 * sp * 32);                       if (w) w->ktab = reinterpret_cast<float2*>(p);
   p = take(2 * B * H * sp * DN);               if (w) w->kn = reinterpret_cast<uint16_t*>(p);
-  p = take(2 * B * H * DV * sp);               if (w) w->vt = reinterpret_cast<uint16_t*>(p);
   p = take(2 * B * sp * DR);                   if (w) w->krot = reinterpret_cast<uint16_t*>(p);
   p = take(2 * B * H * sq_pad * DQK);          if (w) w->qf = reinterpret_cast<uint16_t*>(p);
   p = take(2 * B * H * DQK * sq_pad);          if (w) w->qft = reinterpret_cast<uint16_t*>(p);
@@ -1393,9 +1392,7 @@ hipError_t launch_bwd_prep(const BackwardArgs& a, const MfmaBwdWorkspace& w, hip
                          w.dof, w.doft, w.dvec, w.lsdt, w.sq_pad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // V rows: vt[bh][d][key] -> vrow[bh][key][d]
-  if ((e = transpose<false>(w.vt, w.vrow, DV, DV, sp, sp, (int64_t)DV * sp, DV, (int64_t)sp * DV, B * H, s)) != hipSuccess)
-    return e;
+  // (V comes from the up-projection in the row layout vrow[bh][key][d].)
   // K_nope columns: kn[bh][key][d] -> knt[bh][d][key]
   if ((e = transpose<false>(w.kn, w.knt, sp, sp, DN, DN, (int64_t)sp * DN, sp, (int64_t)DN * sp, B * H, s)) != hipSuccess)
     return e;

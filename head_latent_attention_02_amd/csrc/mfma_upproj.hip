@@ -11,7 +11,8 @@
 // the way in.
 //
 // Outputs (fp16): Kn [B, H, s_pad, 128] and V^T [B, H, 128, s_pad] (key index
-// fastest, the layout the attention kernel's P.V product reads).
+// fastest, the layout the attention kernel's P.V product reads), or, for the
+// backward, V in rows [B, H, s_pad, 128] like Kn.
 //
 // Persistent kernel, one workgroup of 8 waves per CU (two waves per SIMD:
 // while one is held issuing its tile copies, the other keeps the SIMD's
@@ -81,7 +82,7 @@ __device__ __forceinline__ void tile_coords(int tile, int n_jt, bool xcd_deal, i
 __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w,
                    uint16_t* __restrict__ kn, uint16_t* __restrict__ vt, int B, int H, int Skv,
-                   int s_vis, int s_pad, int n_jt, int n_tiles, int xcd_deal) {
+                   int s_vis, int s_pad, int n_jt, int n_tiles, int xcd_deal, int v_rows) {
   // the copy ring, then the output staging of the 8 waves
   __shared__ __attribute__((aligned(16))) uint16_t Ls[(NSTAGE * STAGE_BYTES + NTHREADS / 64 * STG_BYTES) / 2];
   uint8_t* const stg_all = reinterpret_cast<uint8_t*>(Ls) + NSTAGE * STAGE_BYTES;
@@ -112,8 +113,11 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
   const int frag_off0 = l32 * (TK * 2) + ((0 + hb) ^ sw) * 16;   // kk = 0
   const int frag_off1 = l32 * (TK * 2) + ((2 + hb) ^ sw) * 16;   // kk = 1
   // first (A) and second (B) operand regions of this wave, byte offsets in a stage
-  const int a_rows = (part == 0) ? (REG_BYTES + 0) : (jq * 128 * TK * 2);
-  const int b_rows = (part == 0) ? ((jq * 128 + nh * 64) * TK * 2) : (REG_BYTES + (128 + nh * 64) * TK * 2);
+  // With v_rows the V half is formed like the K_nope half (W rows 128..255 as
+  // the A operand) and stored as rows [B, H, s_pad, 128] into vt.
+  const bool row_form = part == 0 || v_rows != 0;
+  const int a_rows = row_form ? (REG_BYTES + part * 128 * TK * 2) : (jq * 128 * TK * 2);
+  const int b_rows = row_form ? ((jq * 128 + nh * 64) * TK * 2) : (REG_BYTES + (128 + nh * 64) * TK * 2);
 
   // Copy-issue state: the step issued next is step is_ks of the block's
   // tile is_t, into ring stage is_stage; ra / rb address that tile's latent
@@ -241,9 +245,9 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
           const int rr = 4 * i + (lane >> 4), c = lane & 15;
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + rr * 256 + ((c ^ rr) * 16));
           const int row = nh * 64 + y * 32 + 16 * h + rr;   // within the tile's 256 rows / 128 features
-          if (part == 0) {
-            // K_nope row of key j0 + jq*128 + row, features 8c .. 8c+7
-            uint16_t* dst = kn + ((int64_t)bh * s_pad + j0 + jq * 128 + row) * 128 + 8 * c;
+          if (row_form) {
+            // K_nope (or V) row of key j0 + jq*128 + row, features 8c .. 8c+7
+            uint16_t* dst = (part == 0 ? kn : vt) + ((int64_t)bh * s_pad + j0 + jq * 128 + row) * 128 + 8 * c;
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
           } else {
             // V^T row of feature row, keys j0 + jq*128 + 8c .. +7
@@ -260,7 +264,7 @@ mfma_upproj_kernel(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict
 
 }  // namespace
 
-hipError_t launch_mfma_upproj(const ExplicitArgs& a, uint16_t* kn, uint16_t* vt, hipStream_t stream) {
+hipError_t launch_mfma_upproj(const ExplicitArgs& a, uint16_t* kn, uint16_t* vt, hipStream_t stream, bool v_rows) {
   if (a.s_vis == 0) return hipSuccess;
   const int n_jt = a.s_pad / TJ;
   const int n_tiles = a.B * a.H * n_jt;
@@ -275,6 +279,6 @@ hipError_t launch_mfma_upproj(const ExplicitArgs& a, uint16_t* kn, uint16_t* vt,
   const int xcd_deal = (grid == 256 && n_tiles % 256 == 0 && n_jt == 16 && (a.B * a.H) % 4 == 0) ? 1 : 0;
   hipLaunchKernelGGL(mfma_upproj_kernel, dim3(grid), dim3(NTHREADS), 0, stream,
                      static_cast<const uint16_t*>(a.c_kv), static_cast<const uint16_t*>(a.w), kn, vt,
-                     a.B, a.H, a.Skv, a.s_vis, a.s_pad, n_jt, n_tiles, xcd_deal);
+                     a.B, a.H, a.Skv, a.s_vis, a.s_pad, n_jt, n_tiles, xcd_deal, v_rows ? 1 : 0);
   return hipGetLastError();
 }

@@ -637,7 +637,7 @@ mla_status mla_bwd_explicit(const mla_explicit_desc* desc, const void* q_nope, c
     if (e != hipSuccess) return hip_fail(e, "rope tables");
     {
       TimedLaunch t("mfma_up_projection", s);
-      e = launch_mfma_upproj(f, w.kn, w.vt, s);
+      e = launch_mfma_upproj(f, w.kn, w.vrow, s, /*v_rows=*/true);   // V straight in the row layout
     }
     if (e != hipSuccess) return hip_fail(e, "mfma up-projection");
     {
